@@ -1,0 +1,562 @@
+// C ABI of the ring-attention rank-share library: validation, the per-shape
+// plan cache (schedule + tile lists in device memory) and the per-step kernel
+// launches.  See include/ring_attn.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <numeric>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "kernel_args.h"
+#include "planner.h"
+#include "ring_attn.h"
+
+namespace ra {
+namespace {
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// ---------------------------------------------------------------------------
+// Plans: the active steps of a rank in ring order, with the per-row visible
+// key intervals and the forward / backward tile lists, uploaded once.
+// ---------------------------------------------------------------------------
+
+struct DevStep {
+    int32_t s = 0, j = 0;
+    int64_t pairs = 0;
+    const int32_t* rng = nullptr;
+    const int32_t* f_off = nullptr;
+    const int32_t* f_ent = nullptr;
+    const int32_t* f_order = nullptr;
+    const int32_t* b_off = nullptr;
+    const int32_t* b_ent = nullptr;
+    const int32_t* b_order = nullptr;
+};
+
+struct Plan {
+    int device = 0;
+    int64_t S_pad = 0;
+    int32_t nqt = 0;    // forward query tiles
+    int32_t nkt_b = 0;  // backward key tiles
+    void* dbuf = nullptr;
+    std::vector<DevStep> steps;
+    ~Plan() {
+        if (dbuf) {
+            int cur = 0;
+            if (hipGetDevice(&cur) == hipSuccess && cur != device) hipSetDevice(device);
+            (void)hipFree(dbuf);
+            if (cur != device) hipSetDevice(cur);
+        }
+    }
+};
+
+std::mutex g_plan_mu;
+std::map<std::string, std::unique_ptr<Plan>> g_plans;
+
+// Host image of a plan before upload: a list of int32 arrays.
+struct HostArrays {
+    std::vector<std::vector<int32_t>> arrays;
+    size_t add(std::vector<int32_t>&& a) {
+        arrays.push_back(std::move(a));
+        return arrays.size() - 1;
+    }
+};
+
+void build_lists(const std::vector<int8_t>& kinds, int64_t nrows, int64_t ncols, bool by_row,
+                 std::vector<int32_t>& off, std::vector<int32_t>& ent,
+                 std::vector<int32_t>& order) {
+    // by_row: lists per row tile (forward, per query tile over key tiles);
+    // else lists per column tile (backward, per key tile over query tiles).
+    const int64_t nlists = by_row ? nrows : ncols, nitems = by_row ? ncols : nrows;
+    off.assign(nlists + 1, 0);
+    ent.clear();
+    for (int64_t l = 0; l < nlists; ++l) {
+        for (int64_t it = 0; it < nitems; ++it) {
+            const int8_t k = by_row ? kinds[l * ncols + it] : kinds[it * ncols + l];
+            if (k == TILE_EMPTY) continue;
+            ent.push_back((int32_t)it | (k == TILE_PARTIAL ? (int32_t)0x80000000u : 0));
+        }
+        off[l + 1] = (int32_t)ent.size();
+    }
+    order.resize(nlists);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+        return off[x + 1] - off[x] > off[y + 1] - off[y];
+    });
+}
+
+int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
+    auto plan = std::make_unique<Plan>();
+    plan->device = device;
+    plan->S_pad = round_up(g.S, FWD_BQ);
+    plan->nqt = (int32_t)((g.S + FWD_BQ - 1) / FWD_BQ);
+    plan->nkt_b = (int32_t)((g.Skv + BWD_BK - 1) / BWD_BK);
+    const int64_t nkt_f = (g.Skv + FWD_BK - 1) / FWD_BK;
+    const int64_t nqt_b = (g.S + BWD_BQ - 1) / BWD_BQ;
+
+    HostArrays H;
+    struct Idx { size_t rng, foff, fent, ford, boff, bent, bord; };
+    std::vector<Idx> idx;
+    std::vector<StepRanges> all(g.nb);
+    int64_t total_pairs = 0;
+    for (int32_t s = 0; s < g.nb; ++s) {
+        step_ranges(g, s, all[s]);
+        total_pairs += all[s].pairs;
+    }
+    std::vector<int8_t> kinds;
+    for (int32_t s = 0; s < g.nb; ++s) {
+        const StepRanges& sr = all[s];
+        // A step with no visible pair is skipped; under a causal basic layout
+        // these are exactly the steps with s > rank.  Step 0 is kept when
+        // nothing is visible at all so that the output is still written.
+        if (sr.pairs == 0 && !(s == 0 && total_pairs == 0)) continue;
+        DevStep ds;
+        ds.s = s;
+        ds.j = sr.j;
+        ds.pairs = sr.pairs;
+        std::vector<int32_t> rng(2 * plan->S_pad, 0);
+        for (int64_t i = 0; i < g.S; ++i) {
+            rng[2 * i] = sr.a[i];
+            rng[2 * i + 1] = sr.b[i];
+        }
+        Idx ix;
+        ix.rng = H.add(std::move(rng));
+        std::vector<int32_t> off, ent, order;
+        classify(sr, g.S, g.Skv, FWD_BQ, FWD_BK, kinds);
+        build_lists(kinds, plan->nqt, nkt_f, true, off, ent, order);
+        ix.foff = H.add(std::move(off));
+        ix.fent = H.add(std::move(ent));
+        ix.ford = H.add(std::move(order));
+        classify(sr, g.S, g.Skv, BWD_BQ, BWD_BK, kinds);
+        build_lists(kinds, nqt_b, plan->nkt_b, false, off, ent, order);
+        ix.boff = H.add(std::move(off));
+        ix.bent = H.add(std::move(ent));
+        ix.bord = H.add(std::move(order));
+        plan->steps.push_back(ds);
+        idx.push_back(ix);
+    }
+    // One device allocation holding every array, each 256-byte aligned.
+    std::vector<size_t> offs(H.arrays.size());
+    size_t total = 0;
+    for (size_t i = 0; i < H.arrays.size(); ++i) {
+        offs[i] = total;
+        total += round_up((int64_t)std::max<size_t>(1, H.arrays[i].size()) * 4, 256);
+    }
+    std::vector<unsigned char> img(total, 0);
+    for (size_t i = 0; i < H.arrays.size(); ++i)
+        if (!H.arrays[i].empty())
+            std::memcpy(img.data() + offs[i], H.arrays[i].data(), H.arrays[i].size() * 4);
+    if (hipMalloc(&plan->dbuf, total) != hipSuccess) {
+        plan->dbuf = nullptr;
+        return RA_E_HIP;
+    }
+    if (hipMemcpy(plan->dbuf, img.data(), total, hipMemcpyHostToDevice) != hipSuccess)
+        return RA_E_HIP;
+    auto P = [&](size_t i) { return (const int32_t*)((unsigned char*)plan->dbuf + offs[i]); };
+    for (size_t k = 0; k < plan->steps.size(); ++k) {
+        DevStep& d = plan->steps[k];
+        d.rng = P(idx[k].rng);
+        d.f_off = P(idx[k].foff);
+        d.f_ent = P(idx[k].fent);
+        d.f_order = P(idx[k].ford);
+        d.b_off = P(idx[k].boff);
+        d.b_ent = P(idx[k].bent);
+        d.b_order = P(idx[k].bord);
+    }
+    out = std::move(plan);
+    return RA_OK;
+}
+
+int get_plan(const Geometry& g, const Plan** out) {
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return RA_E_HIP;
+    const std::string key = std::to_string(device) + "#" + plan_key(g);
+    std::lock_guard<std::mutex> lock(g_plan_mu);
+    auto it = g_plans.find(key);
+    if (it == g_plans.end()) {
+        std::unique_ptr<Plan> p;
+        const int rc = build_plan(g, device, p);
+        if (rc != RA_OK) return rc;
+        it = g_plans.emplace(key, std::move(p)).first;
+    }
+    *out = it->second.get();
+    return RA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Optional per-kernel event timing
+// ---------------------------------------------------------------------------
+
+enum KernelClass { KC_FWD = 0, KC_MERGE, KC_FINALIZE, KC_BWD_PRE, KC_BWD, KC_COUNT };
+const char* kClassNames[KC_COUNT] = {"fwd_step", "lse_merge", "finalize", "bwd_pre", "bwd_step"};
+
+struct Timing {
+    std::mutex mu;
+    bool on = false;
+    std::vector<std::tuple<int, hipEvent_t, hipEvent_t>> pending;
+    std::vector<hipEvent_t> pool;
+    int64_t launches[KC_COUNT] = {};
+    double ms[KC_COUNT] = {};
+} g_timing;
+
+hipEvent_t take_event() {
+    if (!g_timing.pool.empty()) {
+        hipEvent_t e = g_timing.pool.back();
+        g_timing.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+template <class F>
+hipError_t timed(int cls, hipStream_t s, F&& launch) {
+    bool on;
+    {
+        std::lock_guard<std::mutex> lock(g_timing.mu);
+        on = g_timing.on;
+    }
+    if (!on) return launch();
+    hipEvent_t a, b;
+    {
+        std::lock_guard<std::mutex> lock(g_timing.mu);
+        a = take_event();
+        b = take_event();
+    }
+    if (!a || !b) return launch();
+    hipEventRecord(a, s);
+    const hipError_t err = launch();
+    hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lock(g_timing.mu);
+    g_timing.pending.emplace_back(cls, a, b);
+    return err;
+}
+
+int collect_timing() {
+    std::lock_guard<std::mutex> lock(g_timing.mu);
+    for (auto& [cls, a, b] : g_timing.pending) {
+        if (hipEventSynchronize(b) != hipSuccess) return RA_E_HIP;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, a, b) != hipSuccess) return RA_E_HIP;
+        g_timing.launches[cls] += 1;
+        g_timing.ms[cls] += ms;
+        g_timing.pool.push_back(a);
+        g_timing.pool.push_back(b);
+    }
+    g_timing.pending.clear();
+    return RA_OK;
+}
+
+// ---------------------------------------------------------------------------
+
+int64_t elem_bytes(const Geometry& g) { return g.dtype == RA_BF16 ? 2 : 4; }
+
+int64_t fwd_workspace(const Geometry& g) {
+    const int64_t S_pad = round_up(g.S, FWD_BQ);
+    if (g.merge_mode == RA_MERGE_FUSED) return round_up((int64_t)g.B * g.Hq * S_pad * g.d * 4, 256);
+    const int64_t o = round_up((int64_t)g.B * g.S * g.Hq * g.d * 4, 256);
+    return 2 * o + round_up((int64_t)g.B * g.Hq * g.S * 4, 256);
+}
+
+int64_t bwd_workspace(const Geometry& g) {
+    const int64_t S_pad = round_up(g.S, FWD_BQ);
+    return round_up((int64_t)g.B * g.Hq * S_pad * 4, 256);
+}
+
+int check_support(const Geometry& g, bool bwd) {
+    if (g.d != 64 && g.d != 128) return RA_E_UNSUPPORTED;
+    if (bwd && g.dtype != RA_BF16) return RA_E_UNSUPPORTED;
+    return RA_OK;
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? RA_OK : RA_E_HIP; }
+
+}  // namespace
+}  // namespace ra
+
+using namespace ra;
+
+extern "C" {
+
+int ring_attn_version(void) { return 1; }
+
+const char* ring_attn_strerror(int code) {
+    switch (code) {
+        case RA_OK: return "success";
+        case RA_E_NULL: return "a required pointer is NULL";
+        case RA_E_SHAPE: return "batch, heads, head_dim or seqlen out of range";
+        case RA_E_WORLD: return "world < 1 or rank outside [0, world)";
+        case RA_E_DIVISIBILITY: return "seqlen not divisible by world (2*world for zigzag)";
+        case RA_E_CU_SEQLENS:
+            return "cu_seqlens must start at 0, be non-decreasing and end at seqlen; "
+                   "varlen-ring document lengths must be multiples of world";
+        case RA_E_HEADS: return "heads_q is not a multiple of heads_kv";
+        case RA_E_UNSUPPORTED: return "no kernel for this head_dim / dtype combination";
+        case RA_E_WORKSPACE: return "workspace is NULL or smaller than required";
+        case RA_E_LAYOUT: return "unknown layout, or batch != 1 with a varlen layout";
+        case RA_E_HIP: return "the HIP runtime reported an error";
+        case RA_E_ARG: return "an argument is out of range";
+        default: return "unknown error code";
+    }
+}
+
+int64_t ring_attn_workspace_bytes(const ring_attn_desc* desc, int is_bwd) {
+    Geometry g;
+    const int rc = validate(desc, nullptr, &g, false);
+    if (rc != RA_OK) return rc;
+    return is_bwd ? bwd_workspace(g) : fwd_workspace(g);
+}
+
+int ring_attn_positions(const ring_attn_desc* desc, const int32_t* cu, int32_t rank,
+                        int64_t* pos_out) {
+    try {
+        Geometry g;
+        int rc = validate(desc, cu, &g, true);
+        if (rc != RA_OK) return rc;
+        if (!pos_out) return RA_E_NULL;
+        if (rank < 0 || rank >= g.D) return RA_E_WORLD;
+        std::vector<int64_t> p;
+        rank_positions(g, rank, p);
+        std::memcpy(pos_out, p.data(), p.size() * sizeof(int64_t));
+        return RA_OK;
+    } catch (...) {
+        return RA_E_ARG;
+    }
+}
+
+int ring_attn_kv_positions(const ring_attn_desc* desc, const int32_t* cu, int32_t block,
+                           int64_t* pos_out) {
+    try {
+        Geometry g;
+        int rc = validate(desc, cu, &g, true);
+        if (rc != RA_OK) return rc;
+        if (!pos_out) return RA_E_NULL;
+        if (block < 0 || block >= g.nb) return RA_E_ARG;
+        std::vector<int64_t> p;
+        block_positions(g, block, p);
+        std::memcpy(pos_out, p.data(), p.size() * sizeof(int64_t));
+        return RA_OK;
+    } catch (...) {
+        return RA_E_ARG;
+    }
+}
+
+int ring_attn_schedule(const ring_attn_desc* desc, const int32_t* cu, int32_t* block_out,
+                       int64_t* pairs_out, int32_t* n_steps) {
+    try {
+        Geometry g;
+        int rc = validate(desc, cu, &g, true);
+        if (rc != RA_OK) return rc;
+        if (!block_out || !pairs_out || !n_steps) return RA_E_NULL;
+        StepRanges sr;
+        for (int32_t s = 0; s < g.nb; ++s) {
+            step_ranges(g, s, sr);
+            block_out[s] = sr.j;
+            pairs_out[s] = sr.pairs;
+        }
+        *n_steps = g.nb;
+        return RA_OK;
+    } catch (...) {
+        return RA_E_ARG;
+    }
+}
+
+int ring_attn_tile_kinds(const ring_attn_desc* desc, const int32_t* cu, int32_t step,
+                         int32_t tile_q, int32_t tile_k, int8_t* kinds_out) {
+    try {
+        Geometry g;
+        int rc = validate(desc, cu, &g, true);
+        if (rc != RA_OK) return rc;
+        if (!kinds_out) return RA_E_NULL;
+        if (step < 0 || step >= g.nb || tile_q < 1 || tile_k < 1) return RA_E_ARG;
+        StepRanges sr;
+        step_ranges(g, step, sr);
+        std::vector<int8_t> k;
+        classify(sr, g.S, g.Skv, tile_q, tile_k, k);
+        std::memcpy(kinds_out, k.data(), k.size());
+        return RA_OK;
+    } catch (...) {
+        return RA_E_ARG;
+    }
+}
+
+int ring_attn_lse_merge(float* out, float* lse, const float* out_j, const float* lse_j,
+                        int32_t batch, int64_t seqlen, int32_t heads, int32_t head_dim,
+                        void* stream) {
+    if (!out || !lse || !out_j || !lse_j) return RA_E_NULL;
+    if (batch < 0 || seqlen < 0 || heads < 0 || head_dim < 4 || head_dim % 4) return RA_E_SHAPE;
+    hipStream_t s = (hipStream_t)stream;
+    return hip_rc(timed(KC_MERGE, s, [&] {
+        return launch_lse_merge(out, lse, out_j, lse_j, batch, seqlen, heads, head_dim, s);
+    }));
+}
+
+int ring_attn_fwd(const ring_attn_desc* desc, const void* q, const void* k, const void* v,
+                  const int32_t* cu, void* out, float* lse, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    try {
+        Geometry g;
+        int rc = validate(desc, cu, &g, true);
+        if (rc != RA_OK) return rc;
+        if ((rc = check_support(g, false)) != RA_OK) return rc;
+        if (!q || !k || !v || !out || !lse) return RA_E_NULL;
+        const int64_t need = fwd_workspace(g);
+        if (!workspace || (int64_t)workspace_bytes < need) return RA_E_WORKSPACE;
+        const Plan* plan = nullptr;
+        if ((rc = get_plan(g, &plan)) != RA_OK) return rc;
+        hipStream_t s = (hipStream_t)stream;
+
+        const int64_t eb = elem_bytes(g);
+        const int64_t block_elems = (int64_t)g.B * g.Skv * g.Hkv * g.d;
+        FwdArgs a{};
+        a.q = q;
+        a.lse = lse;
+        a.out = out;
+        a.B = g.B; a.S = (int32_t)g.S; a.Skv = (int32_t)g.Skv; a.Hq = g.Hq; a.Hkv = g.Hkv;
+        a.nqt = plan->nqt;
+        a.S_pad = (int32_t)plan->S_pad;
+        a.total_work = g.B * g.Hq * plan->nqt;
+        a.scale_log2 = g.scale * 1.4426950408889634f;
+        auto launch_step = [&](const FwdArgs& args) {
+            return timed(KC_FWD, s, [&] {
+                return g.dtype == RA_BF16 ? launch_fwd_bf16(args, g.d, s)
+                                          : launch_fwd_f32(args, g.d, s);
+            });
+        };
+        const size_t n = plan->steps.size();
+        if (g.merge_mode == RA_MERGE_FUSED) {
+            a.o_run = (float*)workspace;
+            for (size_t i = 0; i < n; ++i) {
+                const DevStep& st = plan->steps[i];
+                a.k = (const unsigned char*)k + st.j * block_elems * eb;
+                a.v = (const unsigned char*)v + st.j * block_elems * eb;
+                a.rng = st.rng; a.t_off = st.f_off; a.t_ent = st.f_ent; a.t_order = st.f_order;
+                a.mode = n == 1 ? FWD_SOLO : (i == 0 ? FWD_FIRST : (i + 1 == n ? FWD_LAST : FWD_MERGE));
+                if ((rc = hip_rc(launch_step(a))) != RA_OK) return rc;
+            }
+        } else {
+            const int64_t o_bytes = round_up((int64_t)g.B * g.S * g.Hq * g.d * 4, 256);
+            float* o_run = (float*)workspace;
+            float* o_j = (float*)((unsigned char*)workspace + o_bytes);
+            float* l_j = (float*)((unsigned char*)workspace + 2 * o_bytes);
+            for (size_t i = 0; i < n; ++i) {
+                const DevStep& st = plan->steps[i];
+                a.k = (const unsigned char*)k + st.j * block_elems * eb;
+                a.v = (const unsigned char*)v + st.j * block_elems * eb;
+                a.rng = st.rng; a.t_off = st.f_off; a.t_ent = st.f_ent; a.t_order = st.f_order;
+                a.mode = FWD_PARTIAL;
+                a.o_part = i == 0 ? o_run : o_j;
+                a.lse_part = i == 0 ? lse : l_j;
+                if ((rc = hip_rc(launch_step(a))) != RA_OK) return rc;
+                if (i > 0) {
+                    rc = hip_rc(timed(KC_MERGE, s, [&] {
+                        return launch_lse_merge(o_run, lse, o_j, l_j, g.B, g.S, g.Hq, g.d, s);
+                    }));
+                    if (rc != RA_OK) return rc;
+                }
+            }
+            const int64_t nel = (int64_t)g.B * g.S * g.Hq * g.d;
+            rc = hip_rc(timed(KC_FINALIZE, s, [&] {
+                return launch_finalize(o_run, out, g.dtype == RA_BF16, nel, s);
+            }));
+            if (rc != RA_OK) return rc;
+        }
+        return RA_OK;
+    } catch (...) {
+        return RA_E_HIP;
+    }
+}
+
+int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, const void* k,
+                  const void* v, const void* out, const float* lse, const int32_t* cu,
+                  float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    try {
+        Geometry g;
+        int rc = validate(desc, cu, &g, true);
+        if (rc != RA_OK) return rc;
+        if ((rc = check_support(g, true)) != RA_OK) return rc;
+        if (!dout || !q || !k || !v || !out || !lse || !dq || !dk || !dv) return RA_E_NULL;
+        const int64_t need = bwd_workspace(g);
+        if (!workspace || (int64_t)workspace_bytes < need) return RA_E_WORKSPACE;
+        const Plan* plan = nullptr;
+        if ((rc = get_plan(g, &plan)) != RA_OK) return rc;
+        hipStream_t s = (hipStream_t)stream;
+        float* delta = (float*)workspace;
+
+        BwdPreArgs pa{};
+        pa.dout = dout; pa.out = out; pa.delta = delta; pa.dq = dq;
+        pa.B = g.B; pa.S = (int32_t)g.S; pa.Hq = g.Hq; pa.S_pad = (int32_t)plan->S_pad; pa.d = g.d;
+        rc = hip_rc(timed(KC_BWD_PRE, s, [&] { return launch_bwd_pre(pa, 1, s); }));
+        if (rc != RA_OK) return rc;
+
+        const int64_t block_elems = (int64_t)g.B * g.Skv * g.Hkv * g.d;
+        BwdArgs a{};
+        a.q = (const uint16_t*)q; a.dout = (const uint16_t*)dout; a.lse = lse; a.delta = delta;
+        a.dq = dq;
+        a.B = g.B; a.S = (int32_t)g.S; a.Skv = (int32_t)g.Skv; a.Hq = g.Hq; a.Hkv = g.Hkv;
+        a.nkt = plan->nkt_b;
+        a.S_pad = (int32_t)plan->S_pad;
+        a.total_work = g.B * g.Hkv * plan->nkt_b;
+        a.scale = g.scale;
+        a.scale_log2 = g.scale * 1.4426950408889634f;
+        for (const DevStep& st : plan->steps) {
+            if (st.pairs == 0) continue;
+            a.k = (const uint16_t*)k + st.j * block_elems;
+            a.v = (const uint16_t*)v + st.j * block_elems;
+            a.dk = dk + st.j * block_elems;
+            a.dv = dv + st.j * block_elems;
+            a.rng = st.rng; a.t_off = st.b_off; a.t_ent = st.b_ent; a.t_order = st.b_order;
+            rc = hip_rc(timed(KC_BWD, s, [&] { return launch_bwd_bf16(a, g.d, s); }));
+            if (rc != RA_OK) return rc;
+        }
+        return RA_OK;
+    } catch (...) {
+        return RA_E_HIP;
+    }
+}
+
+int ring_attn_timing_enable(int enable) {
+    if (!enable) {
+        const int rc = collect_timing();
+        std::lock_guard<std::mutex> lock(g_timing.mu);
+        g_timing.on = false;
+        for (int i = 0; i < KC_COUNT; ++i) {
+            g_timing.launches[i] = 0;
+            g_timing.ms[i] = 0.0;
+        }
+        return rc;
+    }
+    std::lock_guard<std::mutex> lock(g_timing.mu);
+    g_timing.on = true;
+    return RA_OK;
+}
+
+int ring_attn_timing_read(const char* name, int64_t* launches, double* total_ms) {
+    if (!name || !launches || !total_ms) return RA_E_NULL;
+    const int rc = collect_timing();
+    if (rc != RA_OK) return rc;
+    std::lock_guard<std::mutex> lock(g_timing.mu);
+    for (int i = 0; i < KC_COUNT; ++i)
+        if (std::strcmp(name, kClassNames[i]) == 0) {
+            *launches = g_timing.launches[i];
+            *total_ms = g_timing.ms[i];
+            return RA_OK;
+        }
+    return RA_E_ARG;
+}
+
+int ring_attn_clear_cache(void) {
+    std::lock_guard<std::mutex> lock(g_plan_mu);
+    g_plans.clear();
+    return RA_OK;
+}
+
+}  // extern "C"

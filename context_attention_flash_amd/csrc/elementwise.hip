@@ -1,0 +1,141 @@
+// Memory-bound kernels of the ring step:
+//   K2 lse_merge   -- the log-sum-exp merge of a partial into the running
+//                     result (instagit/nanotron page, "Numerically-Stable
+//                     Output Fusion"), one pass over fp32 rows;
+//   K5 finalize    -- running fp32 output -> output dtype;
+//   K3 bwd_pre     -- Delta = rowsum(dout * out) for the backward, and dq = 0.
+#include "kernel_args.h"
+#include "kernel_common.h"
+
+namespace ra {
+
+// One thread per 4 consecutive floats of a row; ITEMS independent items per
+// thread are loaded before any is used to keep enough bytes in flight.
+constexpr int MERGE_ITEMS = 4;
+
+__global__ __launch_bounds__(256) void lse_merge_kernel(float* __restrict__ out,
+                                                        float* __restrict__ lse,
+                                                        const float* __restrict__ oj,
+                                                        const float* __restrict__ lj,
+                                                        int64_t n_items, int64_t S, int32_t H,
+                                                        int32_t c4_per_row) {
+    const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+    const int64_t base = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    f32x4_t o[MERGE_ITEMS], x[MERGE_ITEMS];
+    float L[MERGE_ITEMS], Lj[MERGE_ITEMS];
+    int64_t li[MERGE_ITEMS];
+#pragma unroll
+    for (int it = 0; it < MERGE_ITEMS; ++it) {
+        const int64_t item = base + it * nthreads;
+        if (item < n_items) {
+            const int64_t row = item / c4_per_row;        // (b, s, h)
+            const int64_t h = row % H, bs = row / H;
+            const int64_t b = bs / S, s = bs % S;
+            li[it] = (b * H + h) * S + s;
+            o[it] = __builtin_nontemporal_load((const f32x4_t*)out + item);
+            x[it] = __builtin_nontemporal_load((const f32x4_t*)oj + item);
+            L[it] = lse[li[it]];
+            Lj[it] = lj[li[it]];
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < MERGE_ITEMS; ++it) {
+        const int64_t item = base + it * nthreads;
+        if (item >= n_items) continue;
+        const float M = fmaxf(L[it], Lj[it]);
+        f32x4_t r;
+        float Ln;
+        if (M == -INFINITY) {
+            r = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+            Ln = -INFINITY;
+        } else {
+            const float a = expf(L[it] - M), c = expf(Lj[it] - M), den = a + c;
+            Ln = M + logf(den);
+            const float wa = a / den, wc = c / den;
+            r = wa * o[it] + wc * x[it];
+        }
+        __builtin_nontemporal_store(r, (f32x4_t*)out + item);
+        if ((item % c4_per_row) == 0) lse[li[it]] = Ln;
+    }
+}
+
+hipError_t launch_lse_merge(float* out, float* lse, const float* out_j, const float* lse_j,
+                            int32_t B, int64_t S, int32_t H, int32_t d, hipStream_t s) {
+    const int64_t n_items = (int64_t)B * S * H * (d / 4);
+    if (n_items == 0) return hipSuccess;
+    const int64_t per_block = 256LL * MERGE_ITEMS;
+    int64_t grid = (n_items + per_block - 1) / per_block;
+    hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)grid), dim3(256), 0, s, out, lse, out_j,
+                       lse_j, n_items, S, H, d / 4);
+    return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ o, void* out,
+                                                       int is_bf16, int64_t n4) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    const f32x4_t x = ((const f32x4_t*)o)[i];
+    if (is_bf16) {
+        ((u32x2_t*)out)[i] = (u32x2_t){pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    } else {
+        ((f32x4_t*)out)[i] = x;
+    }
+}
+
+hipError_t launch_finalize(const float* o, void* out, int is_bf16, int64_t n, hipStream_t s) {
+    const int64_t n4 = n / 4;
+    if (n4 == 0) return hipSuccess;
+    hipLaunchKernelGGL(finalize_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, o,
+                       out, is_bf16, n4);
+    return hipGetLastError();
+}
+
+// K3: one group of d/8 lanes per (b, s, h) row; each lane reads 8 elements.
+template <bool BF16>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs a) {
+    const int lanes_per_row = a.d / 8;
+    const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = gt / lanes_per_row;
+    const int c = (int)(gt % lanes_per_row);
+    const int64_t rows = (int64_t)a.B * a.S * a.Hq;
+    float sum = 0.f;
+    if (row < rows) {
+        if (BF16) {
+            const u32x4_t x = *((const u32x4_t*)a.dout + gt);
+            const u32x4_t y = *((const u32x4_t*)a.out + gt);
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                sum += bf16_lo(x[w]) * bf16_lo(y[w]) + bf16_hi(x[w]) * bf16_hi(y[w]);
+        } else {
+            const f32x4_t* xp = (const f32x4_t*)a.dout + 2 * gt;
+            const f32x4_t* yp = (const f32x4_t*)a.out + 2 * gt;
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                const f32x4_t x = xp[w], y = yp[w];
+                sum += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+            }
+        }
+        f32x4_t* dq = (f32x4_t*)a.dq + 2 * gt;
+        dq[0] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        dq[1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    }
+    for (int off = lanes_per_row / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    if (row < rows && c == 0) {
+        const int64_t h = row % a.Hq, bs = row / a.Hq;
+        const int64_t b = bs / a.S, s = bs % a.S;
+        a.delta[(b * a.Hq + h) * a.S_pad + s] = sum;
+    }
+}
+
+hipError_t launch_bwd_pre(const BwdPreArgs& a, int is_bf16, hipStream_t s) {
+    const int64_t threads = (int64_t)a.B * a.S * a.Hq * (a.d / 8);
+    if (threads == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((threads + 255) / 256);
+    if (is_bf16)
+        hipLaunchKernelGGL(bwd_pre_kernel<true>, dim3(grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(bwd_pre_kernel<false>, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace ra

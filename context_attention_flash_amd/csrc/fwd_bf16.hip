@@ -1,0 +1,332 @@
+// K1: one ring step of the flash forward, bf16 inputs, fp32 accumulation.
+//
+// One work-group = one (batch, q head, 128-row query tile); it walks the
+// step's list of 64-key tiles of block j (instagit/nanotron page, "Forward
+// Pass Implementation": one flash call per ring step) with an online softmax
+// (ai360xpert "Ring Attention", "Online softmax across ring steps") and ends
+// with the step's epilogue: write, merge ("Numerically-Stable Output Fusion")
+// or finalise the running result.
+//
+// Per wave (32 query rows) and key tile:
+//   S^T[64 x 32] = K[64 x d] * Q^T[d x 32]   (v_mfma_f32_32x32x16_bf16)
+//   so each lane owns one query column: its 32 scores are in-lane and the
+//   other 32 sit in lane ^ 32 (one permlane32 swap for the row max);
+//   P = exp2(S * scale*log2e - m) in fp32, rounded to bf16;
+//   O^T[d x 32] += V^T[d x 64] * P^T[64 x 32]; the P^T operand is read
+//   straight from the S^T accumulator registers, which hold keys
+//   {0-3, 8-11} (lanes 0-31) and {4-7, 12-15} (lanes 32-63) of every 16-key
+//   step, so V^T is stored in LDS with that key order inside each 16-key group.
+// K and V^T tiles are double-buffered in LDS (global -> registers -> LDS),
+// XOR-swizzled so the 16-byte MFMA operand reads are free of bank conflicts.
+#include "kernel_args.h"
+#include "kernel_common.h"
+
+namespace ra {
+
+template <int DH>
+struct FwdCfg {
+    static constexpr int NT = 256;
+    static constexpr int BQ = FWD_BQ, BK = FWD_BK;
+    static constexpr int NKS = DH / 16;        // MFMA steps over the head dim
+    static constexpr int NDT = DH / 32;        // 32-row tiles of O^T
+    static constexpr int ROWB = DH * 2;        // bytes of one K row
+    static constexpr int KCH = DH / 8;         // 16-byte chunks per K row
+    static constexpr int K_BYTES = BK * ROWB;
+    static constexpr int V_BYTES = DH * BK * 2;
+    static constexpr int STAGE = K_BYTES + V_BYTES;
+    static constexpr int KLD = BK * KCH / NT;  // 16-byte K loads per thread per tile
+    static constexpr int VLD = (BK / 4) * (DH / 4) / NT;  // 4x4 V blocks per thread
+    static constexpr int OUT_STRIDE = ROWB + 16;          // epilogue staging row
+    static constexpr int LDS = 2 * STAGE > 4 * 32 * OUT_STRIDE ? 2 * STAGE : 4 * 32 * OUT_STRIDE;
+    static_assert(KLD >= 1 && VLD >= 1, "tile shape");
+};
+
+// K rows hold KCH 16-byte chunks; chunk c of row r is stored at c ^ swz(r).
+template <int KCH>
+__device__ __forceinline__ int k_swz(int row) {
+    return KCH == 16 ? (row & 15) : ((row >> 1) & 7);
+}
+// V^T rows hold 64 keys = 8 chunks; chunk c of row d is stored at c ^ ((d>>1)&7).
+__device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
+
+// Position of key group m (keys 4m..4m+3 of a 16-key group) inside that group
+// of a V^T row: order {0-3, 8-11, 4-7, 12-15}.
+__device__ __forceinline__ int v_group_slot(int m) { return m == 1 ? 2 : (m == 2 ? 1 : m); }
+
+template <int DH>
+struct FwdTileRegs {
+    u32x4_t k[FwdCfg<DH>::KLD];
+    u32x2_t v[FwdCfg<DH>::VLD][4];
+};
+
+template <int DH>
+__device__ __forceinline__ void fwd_load_tile(FwdTileRegs<DH>& R, const uint16_t* kb,
+                                              const uint16_t* vb, int64_t row_stride,
+                                              int kt, int Skv, int tid) {
+    using C = FwdCfg<DH>;
+#pragma unroll
+    for (int c = 0; c < C::KLD; ++c) {
+        const int idx = tid + C::NT * c;
+        const int row = idx / C::KCH, ch = idx % C::KCH;
+        const int key = min(kt * C::BK + row, Skv - 1);
+        R.k[c] = *(const u32x4_t*)(kb + key * row_stride + ch * 8);
+    }
+#pragma unroll
+    for (int c = 0; c < C::VLD; ++c) {
+        const int idx = tid + C::NT * c;
+        const int dg = idx % (DH / 4), kg = idx / (DH / 4);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int key = min(kt * C::BK + kg * 4 + rr, Skv - 1);
+            R.v[c][rr] = *(const u32x2_t*)(vb + key * row_stride + dg * 4);
+        }
+    }
+}
+
+template <int DH>
+__device__ __forceinline__ void fwd_store_tile(const FwdTileRegs<DH>& R, unsigned char* stage,
+                                               int tid) {
+    using C = FwdCfg<DH>;
+    unsigned char* Ks = stage;
+    unsigned char* Vt = stage + C::K_BYTES;
+#pragma unroll
+    for (int c = 0; c < C::KLD; ++c) {
+        const int idx = tid + C::NT * c;
+        const int row = idx / C::KCH, ch = idx % C::KCH;
+        *(u32x4_t*)(Ks + row * C::ROWB + ((ch ^ k_swz<C::KCH>(row)) << 4)) = R.k[c];
+    }
+#pragma unroll
+    for (int c = 0; c < C::VLD; ++c) {
+        const int idx = tid + C::NT * c;
+        const int dg = idx % (DH / 4), kg = idx / (DH / 4);
+        const int sp = 16 * (kg >> 2) + 4 * v_group_slot(kg & 3);  // stored key position
+        const int chunk = sp >> 3, inner = (sp & 7) * 2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int d = dg * 4 + e;
+            const int w = e >> 1;
+            uint32_t a0 = R.v[c][0][w], a1 = R.v[c][1][w], a2 = R.v[c][2][w], a3 = R.v[c][3][w];
+            u32x2_t o;
+            if (e & 1) {
+                o[0] = (a0 >> 16) | (a1 & 0xffff0000u);
+                o[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+            } else {
+                o[0] = (a0 & 0xffffu) | (a1 << 16);
+                o[1] = (a2 & 0xffffu) | (a3 << 16);
+            }
+            *(u32x2_t*)(Vt + d * (C::BK * 2) + ((chunk ^ v_swz(d)) << 4) + inner) = o;
+        }
+    }
+}
+
+template <int DH>
+__global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
+    using C = FwdCfg<DH>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+    const int work = xcd_work_index(blockIdx.x, gridDim.x);
+    if (work >= p.total_work) return;
+    const int t = work % p.nqt, bh = work / p.nqt;
+    const int h = bh % p.Hq, b = bh / p.Hq;
+    const int qt = p.t_order[t];
+    const int hk = (h * p.Hkv) / p.Hq;
+    const int e0 = p.t_off[qt], e1 = p.t_off[qt + 1];
+
+    const int iq = qt * C::BQ + wave * 32 + l32;  // this lane's query row
+    const int iqc = min(iq, p.S - 1);
+    const uint16_t* qrow = (const uint16_t*)p.q + ((int64_t)(b * p.S + iqc) * p.Hq + h) * DH;
+    u32x4_t qreg[C::NKS];
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) qreg[ks] = *(const u32x4_t*)(qrow + 16 * ks + 8 * g);
+    const int ra = p.rng[2 * iq], rb = p.rng[2 * iq + 1];
+
+    const int64_t row_stride = (int64_t)p.Hkv * DH;
+    const uint16_t* kb = (const uint16_t*)p.k + (int64_t)b * p.Skv * row_stride + hk * DH;
+    const uint16_t* vb = (const uint16_t*)p.v + (int64_t)b * p.Skv * row_stride + hk * DH;
+
+    f32x16_t oacc[C::NDT];
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] = (f32x16_t){};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float c2 = p.scale_log2;
+
+    if (e0 < e1) {
+        FwdTileRegs<DH> R;
+        fwd_load_tile<DH>(R, kb, vb, row_stride, p.t_ent[e0] & 0x7fffffff, p.Skv, tid);
+        fwd_store_tile<DH>(R, smem, tid);
+        for (int e = e0; e < e1; ++e) {
+            unsigned char* stage = smem + ((e - e0) & 1) * C::STAGE;
+            __syncthreads();
+            const bool has_next = e + 1 < e1;
+            if (has_next)
+                fwd_load_tile<DH>(R, kb, vb, row_stride, p.t_ent[e + 1] & 0x7fffffff, p.Skv, tid);
+            const int ent = p.t_ent[e];
+            const int kt = ent & 0x7fffffff;
+            const unsigned char* Ks = stage;
+            const unsigned char* Vt = stage + C::K_BYTES;
+
+            // S^T = K Q^T for the 64 keys of the tile (two 32-key halves)
+            f32x16_t sacc[2];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                sacc[mt] = (f32x16_t){};
+                const int row = 32 * mt + l32;
+                const unsigned char* kr = Ks + row * C::ROWB;
+                const int sw = k_swz<C::KCH>(row);
+#pragma unroll
+                for (int ks = 0; ks < C::NKS; ++ks) {
+                    const u32x4_t a = *(const u32x4_t*)(kr + (((2 * ks + g) ^ sw) << 4));
+                    sacc[mt] = mfma_32x32x16(a, qreg[ks], sacc[mt]);
+                }
+            }
+            if (ent < 0) {  // partial tile: keys outside [ra, rb) are invisible
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kt * C::BK + 32 * mt + (r >> 2) * 8 + g * 4 + (r & 3);
+                        if (key < ra || key >= rb) sacc[mt][r] = -INFINITY;
+                    }
+            }
+            float mx = sacc[0][0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
+            mx = pair_max(mx);
+            const float m_new = fmaxf(m_run, mx * c2);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = fast_exp2(m_run - m_use);
+            m_run = m_new;
+
+            u32x4_t pb[4];
+            float rs = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const float p0 = fast_exp2(fmaf(sacc[mt][r], c2, -m_use));
+                    const float p1 = fast_exp2(fmaf(sacc[mt][r + 1], c2, -m_use));
+                    rs += p0 + p1;
+                    pb[2 * mt + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+                }
+            l_run = l_run * alpha + rs;
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] *= alpha;
+
+            // O^T += V^T P^T
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) {
+                const int row = 32 * dt + l32;
+                const unsigned char* vr = Vt + row * (C::BK * 2);
+                const int sw = v_swz(row);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const u32x4_t a = *(const u32x4_t*)(vr + (((2 * kk + g) ^ sw) << 4));
+                    oacc[dt] = mfma_32x32x16(a, pb[kk], oacc[dt]);
+                }
+            }
+            if (has_next) fwd_store_tile<DH>(R, smem + (((e - e0) & 1) ^ 1) * C::STAGE, tid);
+        }
+    }
+
+    // ---- epilogue: normalise the step's partial and apply the step mode ----
+    const float l_tot = pair_sum(l_run);
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : 1.f / l_tot;
+    const float Lj = empty ? -INFINITY : (m_run + log2f(l_tot)) * kLn2;
+    const bool valid = iq < p.S;
+    const int64_t lse_idx = ((int64_t)b * p.Hq + h) * p.S + iq;
+
+    // O_j (normalised) in registers; element (dt, r) is head-dim index
+    // 32*dt + 8*(r/4) + 4*g + r%4 of query row iq.
+    float w_old = 0.f, w_new = inv, L_out = Lj;
+    f32x4_t* orun = (f32x4_t*)p.o_run +
+                    (((int64_t)b * p.Hq + h) * (p.S_pad / 32) + (qt * 4 + wave)) * (8 * DH) + lane;
+    const int mode = p.mode;
+    if (mode == FWD_MERGE || mode == FWD_LAST) {
+        const float Lr = valid ? p.lse[lse_idx] : -INFINITY;
+        const float M = fmaxf(Lr, Lj);
+        if (M == -INFINITY) {
+            w_old = 0.f; w_new = 0.f; L_out = -INFINITY;
+        } else {
+            const float er = expf(Lr - M), ej = expf(Lj - M);
+            const float den = er + ej;
+            L_out = M + logf(den);
+            w_old = er / den;
+            w_new = ej * inv / den;
+        }
+    }
+
+    if (mode == FWD_FIRST || mode == FWD_MERGE) {
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                f32x4_t* ptr = orun + (dt * 4 + rg) * 64;
+                f32x4_t o = {oacc[dt][4 * rg] * w_new, oacc[dt][4 * rg + 1] * w_new,
+                             oacc[dt][4 * rg + 2] * w_new, oacc[dt][4 * rg + 3] * w_new};
+                if (mode == FWD_MERGE) o += w_old * (*ptr);
+                *ptr = o;
+            }
+        if (valid && g == 0) p.lse[lse_idx] = L_out;
+        return;
+    }
+    if (mode == FWD_PARTIAL) {
+        if (valid) {
+            float* orow = p.o_part + ((int64_t)(b * p.S + iq) * p.Hq + h) * DH;
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    f32x4_t o = {oacc[dt][4 * rg] * inv, oacc[dt][4 * rg + 1] * inv,
+                                 oacc[dt][4 * rg + 2] * inv, oacc[dt][4 * rg + 3] * inv};
+                    *(f32x4_t*)(orow + 32 * dt + 8 * rg + 4 * g) = o;
+                }
+            if (g == 0) p.lse_part[lse_idx] = Lj;
+        }
+        return;
+    }
+
+    // FWD_LAST / FWD_SOLO: final bf16 output through LDS for coalesced rows.
+    __syncthreads();  // every wave is done with the K/V stages
+    unsigned char* st = smem + wave * 32 * C::OUT_STRIDE;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            f32x4_t o = {oacc[dt][4 * rg] * w_new, oacc[dt][4 * rg + 1] * w_new,
+                         oacc[dt][4 * rg + 2] * w_new, oacc[dt][4 * rg + 3] * w_new};
+            if (mode == FWD_LAST) o += w_old * orun[(dt * 4 + rg) * 64];
+            u32x2_t w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+            *(u32x2_t*)(st + l32 * C::OUT_STRIDE + (32 * dt + 8 * rg + 4 * g) * 2) = w;
+        }
+    if (valid && g == 0) p.lse[lse_idx] = L_out;
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    constexpr int CPR = DH / 8;            // 16-byte chunks per output row
+    constexpr int RPI = 64 / CPR;          // rows per wave instruction
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+        const int row = it * RPI + lane / CPR, ch = lane % CPR;
+        const int iqr = qt * C::BQ + wave * 32 + row;
+        const u32x4_t val = *(const u32x4_t*)(st + row * C::OUT_STRIDE + ch * 16);
+        if (iqr < p.S)
+            *(u32x4_t*)((uint16_t*)p.out + ((int64_t)(b * p.S + iqr) * p.Hq + h) * DH + ch * 8) = val;
+    }
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, hipStream_t s) {
+    const int grid = (a.total_work + 7) / 8 * 8;
+    if (head_dim == 128)
+        hipLaunchKernelGGL(fwd_step_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a);
+    else if (head_dim == 64)
+        hipLaunchKernelGGL(fwd_step_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace ra

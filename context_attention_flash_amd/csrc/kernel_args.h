@@ -1,0 +1,81 @@
+// Kernel argument blocks and launchers shared between the host ABI and the
+// HIP translation units.  Host-visible, no device code.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace ra {
+
+// Per-step epilogue of the forward kernel.
+enum FwdMode : int32_t {
+    FWD_FIRST = 0,    // write the step's partial as the running result
+    FWD_MERGE = 1,    // merge the partial into the running result
+    FWD_LAST = 2,     // merge, then write out (input dtype) and lse
+    FWD_SOLO = 3,     // single active step: write out and lse directly
+    FWD_PARTIAL = 4,  // write the normalised partial, fp32 [B,S,Hq,d], and its lse
+};
+
+constexpr int FWD_BQ = 128;   // query rows per forward work-group (4 waves x 32)
+constexpr int FWD_BK = 64;    // keys per forward tile
+constexpr int BWD_BQ = 64;    // query rows per backward tile
+constexpr int BWD_BK = 128;   // keys per backward work-group (4 waves x 32)
+
+struct FwdArgs {
+    const void* q;          // [B, S, Hq, d]
+    const void* k;          // block j: [B, Skv, Hkv, d]
+    const void* v;
+    const int32_t* rng;     // [S_pad][2] visible local key interval [a, b) per query row
+    const int32_t* t_off;   // [nqt + 1] tile-list offsets per query tile
+    const int32_t* t_ent;   // key tile index | (partial << 31)
+    const int32_t* t_order; // [nqt] query tiles, heaviest first
+    float* o_run;           // running fp32 output (layout private to the kernel family)
+    float* lse;             // [B, Hq, S] running / final lse
+    void* out;              // [B, S, Hq, d] final output (input dtype)
+    float* o_part;          // FWD_PARTIAL: [B, S, Hq, d] fp32
+    float* lse_part;        // FWD_PARTIAL: [B, Hq, S]
+    int32_t B, S, Skv, Hq, Hkv, nqt, S_pad;
+    int32_t mode;
+    int32_t total_work;     // B * Hq * nqt
+    float scale_log2;       // softmax scale * log2(e)
+};
+
+struct BwdArgs {
+    const uint16_t* q;      // [B, S, Hq, d] bf16
+    const uint16_t* k;      // block j: [B, Skv, Hkv, d]
+    const uint16_t* v;
+    const uint16_t* dout;   // [B, S, Hq, d]
+    const float* lse;       // [B, Hq, S]
+    const float* delta;     // [B, Hq, S_pad] rowsum(dout * out)
+    const int32_t* rng;     // [S_pad][2]
+    const int32_t* t_off;   // [nkt + 1] query-tile lists per key tile
+    const int32_t* t_ent;   // query tile index | (partial << 31)
+    const int32_t* t_order; // [nkt] key tiles, heaviest first
+    float* dq;              // [B, S, Hq, d] fp32, accumulated with atomics
+    float* dk;              // block j: [B, Skv, Hkv, d] fp32, +=
+    float* dv;
+    int32_t B, S, Skv, Hq, Hkv, nkt, S_pad;
+    int32_t total_work;     // B * Hkv * nkt
+    float scale;            // softmax scale
+    float scale_log2;       // softmax scale * log2(e)
+};
+
+struct BwdPreArgs {
+    const void* dout;       // [B, S, Hq, d] input dtype
+    const void* out;
+    float* delta;           // [B, Hq, S_pad]
+    float* dq;              // [B, S, Hq, d] zeroed here
+    int32_t B, S, Hq, S_pad, d;
+};
+
+// Launchers (defined in the .hip files).  Return hipSuccess or the launch error.
+hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_lse_merge(float* out, float* lse, const float* out_j, const float* lse_j,
+                            int32_t B, int64_t S, int32_t H, int32_t d, hipStream_t s);
+hipError_t launch_finalize(const float* o, void* out, int is_bf16, int64_t n, hipStream_t s);
+hipError_t launch_bwd_pre(const BwdPreArgs& a, int is_bf16, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, hipStream_t s);
+
+}  // namespace ra

@@ -1,0 +1,64 @@
+// Host planner: layout -> position maps -> ring schedule -> tile classification.
+//
+// Pure host C++ (no HIP); compiled into the library and also on its own by the
+// host sanitizer test.  Every quantity here is integer and deterministic.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "ring_attn.h"
+
+namespace ra {
+
+struct Geometry {
+    int32_t B = 0, Hq = 0, Hkv = 0, d = 0;
+    int64_t N = 0;
+    int32_t D = 1, r = 0;
+    bool causal = false;
+    int32_t layout = RA_BASIC;
+    int32_t dtype = RA_BF16;
+    float scale = 0.f;          // resolved softmax scale (> 0)
+    int32_t merge_mode = RA_MERGE_FUSED;
+    int64_t S = 0;              // local query rows
+    int64_t Skv = 0;            // rows per KV block
+    int32_t nb = 1;             // number of KV blocks (ring steps)
+    bool varlen = false;
+    std::vector<int64_t> cu;    // cu_seqlens (varlen layouts only)
+};
+
+// Validates the descriptor (and cu_seqlens when the layout is varlen).
+// Returns RA_OK and fills *g, or a negative RA_E_* code.
+int validate(const ring_attn_desc* desc, const int32_t* cu_seqlens, Geometry* g,
+             bool check_cu);
+
+// Global positions of the local rows of `rank` (size S), increasing.
+void rank_positions(const Geometry& g, int32_t rank, std::vector<int64_t>& out);
+// Global positions of the rows of KV block `block` (size Skv), increasing.
+void block_positions(const Geometry& g, int32_t block, std::vector<int64_t>& out);
+
+// One ring step of rank g.r: the block it holds and, for every local query
+// row i, the half-open interval [a[i], b[i]) of local key indices of that
+// block that row i may see.  Because positions inside a block increase, the
+// visible keys of a row (same document, not in its future) are contiguous.
+struct StepRanges {
+    int32_t s = 0, j = 0;
+    int64_t pairs = 0;          // sum over rows of (b - a)
+    std::vector<int32_t> a, b;
+};
+
+void step_ranges(const Geometry& g, int32_t s, StepRanges& out);
+
+enum TileKind : int8_t { TILE_EMPTY = 0, TILE_PARTIAL = 1, TILE_FULL = 2 };
+
+// kinds[qt * nkt + kt] for query tiles of bq rows and key tiles of bk keys.
+// FULL: every (row < S, key) pair of the tile visible; EMPTY: none; else PARTIAL.
+// A key tile that runs past Skv is never FULL.
+void classify(const StepRanges& sr, int64_t S, int64_t Skv, int32_t bq, int32_t bk,
+              std::vector<int8_t>& kinds);
+
+// Canonical text key of a geometry (for the plan cache).
+std::string plan_key(const Geometry& g);
+
+}  // namespace ra

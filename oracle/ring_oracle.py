@@ -178,14 +178,15 @@ def _row_chunks(n_rows: int, n_keys: int, budget: int = 1 << 24):
 
 def rank_share_forward(q_glob, k_glob, v_glob, layout: int, world: int, rank: int,
                        causal: bool, cu_seqlens=None, scale: Optional[float] = None,
-                       rows: Optional[np.ndarray] = None):
+                       rows: Optional[np.ndarray] = None, heads: Optional[Sequence[int]] = None):
     """Expected (out, lse) of rank ``rank``: plain attention of the rank's query
     rows over every key of the global sequence, with the global-position mask.
 
     q_glob [B, N, Hq, d], k_glob/v_glob [B, N, Hkv, d] in global order.
     Returns out [B, S, Hq, d] (local row order) and lse [B, Hq, S], float64.
     ``rows`` optionally restricts the computation to some local rows (then the
-    returned arrays hold only those rows, in the given order).
+    returned arrays hold only those rows, in the given order); ``heads``
+    restricts it to some q heads (the others are left at zero).
     """
     B, N, Hq, d = q_glob.shape
     Hkv = k_glob.shape[2]
@@ -202,7 +203,7 @@ def rank_share_forward(q_glob, k_glob, v_glob, layout: int, world: int, rank: in
     for a, b in _row_chunks(S, N):
         mask = allowed(pos_q[a:b], pos_k, causal, cu)
         for bi in range(B):
-            for h in range(Hq):
+            for h in (range(Hq) if heads is None else heads):
                 hk = kv_head_of(h, Hq, Hkv)
                 o, l = attention_rows(q_glob[bi, pos_q[a:b], h], k_glob[bi, :, hk],
                                       v_glob[bi, :, hk], mask, scale)

@@ -1,0 +1,229 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle,
+element by element, on seeded inputs that span several tiles and a ragged tail.
+
+Tolerances: fp32 out/lse <= 1e-4; bf16 out <= 2e-2, lse <= 1e-3; gradients
+max-abs-err <= 5e-2 * max |oracle grad| per tensor.
+"""
+import numpy as np
+import pytest
+
+import context_attention_flash_amd as ca
+import oracle
+from context_attention_flash_amd import synth
+
+from _helpers import max_err_lse, say, shard, to_dev, tol
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+LAYOUTS = [ca.BASIC, ca.ZIGZAG, ca.STRIPE, ca.VARLEN_RING, ca.LLAMA3]
+
+
+def _small_workload(layout, causal, head_dim, dtype="bf16", D=4, S=200, B=2, Hq=4, Hkv=2,
+                    seed=0, with_grad=False):
+    N = D * S
+    cu = None
+    if layout == ca.VARLEN_RING:
+        cu = tuple(synth.random_cu_seqlens(N, 3, np.random.default_rng(seed + 7), multiple=D))
+        B = 1
+    elif layout == ca.LLAMA3:
+        cu = tuple(synth.random_cu_seqlens(N, 4, np.random.default_rng(seed + 7)))
+        B = 1
+    return synth.Workload(f"small-{layout}", B, Hq, Hkv, head_dim, N, D, 0, causal, layout, dtype,
+                          seed=seed, cu_seqlens=cu, with_grad=with_grad)
+
+
+def _run_fwd(w, glob, rank, merge_mode=ca.RA_MERGE_FUSED):
+    sh = shard(glob, w, rank)
+    desc = ca.desc_from_workload(w, rank=rank, merge_mode=merge_mode)
+    q, k, v = (to_dev(sh[n], w.dtype) for n in ("q", "k", "v"))
+    out, lse = ca.ring_attn_fwd(desc, q, k, v, w.cu_seqlens)
+    torch.cuda.synchronize()
+    return sh, desc, (q, k, v), out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def _check_fwd(w, glob, rank, out, lse):
+    ref_out, ref_lse = oracle.rank_share_forward(glob["q"], glob["k"], glob["v"], w.layout, w.world,
+                                                 rank, w.causal, w.cu_seqlens)
+    t = tol(w.dtype)
+    e_out = float(np.abs(out - ref_out).max())
+    e_lse = max_err_lse(lse, ref_lse)
+    assert e_out <= t["out"], e_out
+    assert e_lse <= t["lse"], e_lse
+    return e_out, e_lse
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("head_dim", [128, 64])
+@pytest.mark.parametrize("merge_mode", [ca.RA_MERGE_FUSED, ca.RA_MERGE_SEPARATE])
+def test_fwd_bf16_small(layout, causal, head_dim, merge_mode):
+    w = _small_workload(layout, causal, head_dim, seed=layout * 4 + causal)
+    glob = synth.draw_global(w)
+    for rank in (0, 2, w.world - 1):
+        say(f"fwd bf16 layout={layout} causal={causal} d={head_dim} merge={merge_mode} rank={rank}")
+        _, _, _, out, lse = _run_fwd(w, glob, rank, merge_mode)
+        _check_fwd(w, glob, rank, out, lse)
+
+
+@pytest.mark.parametrize("layout", [ca.BASIC, ca.STRIPE, ca.LLAMA3])
+def test_fwd_f32_small(layout):
+    w = _small_workload(layout, True, 64, dtype="f32", seed=11)
+    glob = synth.draw_global(w)
+    for rank in (0, w.world - 1):
+        for mm in (ca.RA_MERGE_FUSED, ca.RA_MERGE_SEPARATE):
+            say(f"fwd f32 layout={layout} rank={rank} merge={mm}")
+            _, _, _, out, lse = _run_fwd(w, glob, rank, mm)
+            _check_fwd(w, glob, rank, out, lse)
+
+
+def test_tiny_fp32_all_ranks():
+    """batch 1, 2 heads, d 64, N 512 over D = 4 simulated ranks, fp32
+    N(0,1)*0.1, non-causal basic ring: every rank's out + lse against full
+    softmax attention."""
+    w = synth.WORKLOADS["tiny_fp32"]
+    glob = synth.draw_global(w)
+    outs = []
+    for rank in range(w.world):
+        say(f"tiny fp32 rank={rank}")
+        _, _, _, out, lse = _run_fwd(w, glob, rank)
+        _check_fwd(w, glob, rank, out, lse)
+        outs.append(out)
+    full, _ = oracle.rank_share_forward(glob["q"], glob["k"], glob["v"], ca.BASIC, 1, 0, False)
+    assert np.abs(np.concatenate(outs, axis=1) - full).max() <= 1e-4
+
+
+@pytest.mark.parametrize("S", [1, 63, 64, 65, 129])
+def test_fwd_edge_shapes(S):
+    """One-row shards, exact and ragged tile boundaries."""
+    for layout in (ca.BASIC, ca.ZIGZAG, ca.STRIPE):
+        if layout == ca.ZIGZAG and S % 2:
+            continue
+        w = _small_workload(layout, True, 128, D=3, S=S, B=1, Hq=2, Hkv=1, seed=S)
+        glob = synth.draw_global(w)
+        for rank in range(w.world):
+            say(f"edge S={S} layout={layout} rank={rank}")
+            _, _, _, out, lse = _run_fwd(w, glob, rank)
+            _check_fwd(w, glob, rank, out, lse)
+
+
+def test_fwd_world_one_is_plain_attention():
+    w = _small_workload(ca.BASIC, True, 128, D=1, S=300, seed=5)
+    glob = synth.draw_global(w)
+    say("world=1")
+    _, _, _, out, lse = _run_fwd(w, glob, 0)
+    _check_fwd(w, glob, 0, out, lse)
+
+
+def test_fwd_is_deterministic():
+    w = _small_workload(ca.ZIGZAG, True, 128, seed=9)
+    glob = synth.draw_global(w)
+    say("determinism")
+    _, _, _, o1, l1 = _run_fwd(w, glob, 1)
+    _, _, _, o2, l2 = _run_fwd(w, glob, 1)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_identity_v_gives_exact_zeros_where_masked():
+    """V = identity over the keys (head_dim >= keys): out is the probability
+    matrix, exactly zero on masked keys."""
+    N, D, d = 128, 2, 128
+    w = synth.Workload("eye", 1, 1, 1, d, N, D, 0, True, ca.STRIPE, "bf16", seed=3)
+    glob = synth.draw_global(w)
+    glob["v"] = np.zeros_like(glob["v"])
+    glob["v"][0, :, 0, :N] = np.eye(N, dtype=np.float32)
+    for rank in range(D):
+        say(f"identity V rank={rank}")
+        sh, desc, _, out, lse = _run_fwd(w, glob, rank)
+        m = oracle.allowed(sh["pos_q"], np.arange(N), True)
+        P = out[0, :, 0, :N]
+        assert np.all(P[~m] == 0.0)
+        assert np.all(P[m] > 0.0)
+
+
+def test_lse_merge_kernel():
+    rng = np.random.default_rng(17)
+    B, S, H, d = 2, 777, 3, 128
+    o = rng.standard_normal((B, S, H, d)).astype(np.float32)
+    oj = rng.standard_normal((B, S, H, d)).astype(np.float32)
+    l = (rng.standard_normal((B, H, S)) * 5).astype(np.float32)
+    lj = (rng.standard_normal((B, H, S)) * 5).astype(np.float32)
+    l[0, 0, :10] = -np.inf            # empty running rows
+    lj[0, 1, 5:20] = -np.inf          # empty partial rows
+    l[1, 2, 30:40] = -np.inf
+    lj[1, 2, 30:40] = -np.inf         # both empty
+    o[0, :10, 0] = 0.0
+    oj[0, 5:20, 1] = 0.0
+    o[1, 30:40, 2] = 0.0
+    oj[1, 30:40, 2] = 0.0
+    say("lse merge")
+    to = torch.from_numpy(o).cuda()
+    tl = torch.from_numpy(l).cuda()
+    ca.ring_attn_lse_merge(to, tl, torch.from_numpy(oj).cuda(), torch.from_numpy(lj).cuda())
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.lse_merge(o.transpose(0, 2, 1, 3), l, oj.transpose(0, 2, 1, 3), lj)
+    got_o = to.cpu().numpy().transpose(0, 2, 1, 3)
+    assert np.abs(got_o - ref_o).max() < 1e-5
+    assert max_err_lse(tl.cpu().numpy(), ref_l) < 1e-5
+    assert not np.isnan(got_o).any()
+
+
+# ---------------------------------------------------------------------------
+# Backward
+# ---------------------------------------------------------------------------
+
+def _check_bwd(w, glob, rank, dq, dk, dv):
+    sh = shard(glob, w, rank)
+    rdq, rdk, rdv = oracle.rank_share_backward(glob["q"], glob["k"], glob["v"], sh["dout"], w.layout,
+                                               w.world, rank, w.causal, w.cu_seqlens)
+    errs = {}
+    for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        e = float(np.abs(got - ref).max())
+        bound = 5e-2 * float(np.abs(ref).max())
+        errs[name] = (e, bound)
+        assert e <= bound, (name, e, bound)
+    return errs
+
+
+def _run_bwd(w, glob, rank, dk=None, dv=None):
+    sh = shard(glob, w, rank)
+    desc = ca.desc_from_workload(w, rank=rank)
+    q, k, v = (to_dev(sh[n], w.dtype) for n in ("q", "k", "v"))
+    out, lse = ca.ring_attn_fwd(desc, q, k, v, w.cu_seqlens)
+    dout = to_dev(sh["dout"], w.dtype)
+    dq, dk, dv = ca.ring_attn_bwd(desc, dout, q, k, v, out, lse, w.cu_seqlens, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("head_dim", [128, 64])
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_small(layout, head_dim, causal):
+    w = _small_workload(layout, causal, head_dim, seed=20 + layout, with_grad=True)
+    glob = synth.draw_global(w)
+    for rank in (0, w.world - 1):
+        say(f"bwd layout={layout} d={head_dim} causal={causal} rank={rank}")
+        dq, dk, dv = _run_bwd(w, glob, rank)
+        _check_bwd(w, glob, rank, dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
+
+
+def test_bwd_ranks_sum_to_full_gradient():
+    """dk/dv accumulated over every rank's backward on the same buffers equal
+    the full-sequence gradient; the ranks' dq tile the full dq."""
+    w = _small_workload(ca.ZIGZAG, True, 128, D=4, S=160, B=1, seed=31, with_grad=True)
+    glob = synth.draw_global(w)
+    dk = dv = None
+    dq_full = np.zeros_like(glob["q"])
+    for rank in range(w.world):
+        say(f"bwd sum over ranks rank={rank}")
+        dq, dk, dv = _run_bwd(w, glob, rank, dk=dk, dv=dv)
+        dq_full[:, oracle.positions(w.layout, w.seqlen, w.world, rank)] = dq.cpu().numpy()
+    rdq, rdk, rdv = oracle.rank_share_backward(glob["q"], glob["k"], glob["v"], glob["dout"],
+                                               ca.BASIC, 1, 0, True)
+    blocks = [oracle.kv_positions(w.layout, w.seqlen, w.world, j) for j in range(w.world)]
+    order = np.concatenate(blocks)
+    got_dk = np.concatenate(list(dk.cpu().numpy()), axis=1)
+    got_dv = np.concatenate(list(dv.cpu().numpy()), axis=1)
+    for got, ref in ((got_dk, rdk[0][:, order]), (got_dv, rdv[0][:, order]), (dq_full, rdq)):
+        assert np.abs(got - ref).max() <= 5e-2 * np.abs(ref).max()
