@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the ring-attention rank share on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+the forward (every active ring step of the flash forward with its fused LSE
+merge and finalisation) followed by the backward (Delta preprocess, every
+active ring step of the backward with fp32 dQ/dK/dV accumulation), through the
+C ABI.  Default workload: basic causal ring, rank 7 of D = 8, global sequence
+65536 (8192 rows per block), 32 heads, head_dim 128, bf16, batch 1.
+
+Prints ONE JSON line.  Throughput counts algorithmic work only (visible
+(query, key) pairs): forward 4*d*Hq*B*pairs flops, backward 10*d*Hq*B*pairs.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+METRIC = "causal attn fwd/bwd TFLOP/s per rank share (bf16) + % of MFMA peak"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def build_inputs(ca, w, torch):
+    from context_attention_flash_amd import synth
+    t0 = time.time()
+    g = synth.draw_global(w)
+    desc = ca.desc_from_workload(w)
+    pos_q = ca.ring_attn_positions(desc, w.cu_seqlens)
+    _, _, nb = ca.shard_sizes(desc)
+    blocks = [ca.ring_attn_kv_positions(desc, w.cu_seqlens, j) for j in range(nb)]
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dt).cuda()
+
+    t = {"q": dev(g["q"][:, pos_q]),
+         "k": dev(np.stack([g["k"][:, p] for p in blocks])),
+         "v": dev(np.stack([g["v"][:, p] for p in blocks]))}
+    if w.with_grad:
+        t["dout"] = dev(g["dout"][:, pos_q])
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+    return g, desc, t
+
+
+def cpu_baseline(w, g, budget_s: float):
+    """The fp64 oracle on a bounded sample of the same workload: the forward
+    (and backward, when the workload has one) of consecutive query rows of head
+    0, chunk after chunk until ~budget_s of CPU time has been spent."""
+    import oracle
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    S = w.seqlen // w.world
+    cu = list(w.cu_seqlens) if w.cu_seqlens else None
+    pos_q = oracle.positions(w.layout, w.seqlen, w.world, w.rank, cu)
+    dout_local = g["dout"][:, pos_q] if w.with_grad else None
+    chunk = 128
+    done_rows = 0
+    flops = 0.0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and done_rows < S:
+        hi = S - done_rows  # the heaviest rows of a causal shard first
+        rows = np.arange(max(0, hi - chunk), hi)
+        oracle.rank_share_forward(g["q"], g["k"], g["v"], w.layout, w.world, w.rank, w.causal, cu,
+                                  rows=rows, heads=[0])
+        m = oracle.allowed(pos_q[rows], np.arange(w.seqlen), w.causal,
+                           cu if w.layout in (3, 4) else None)
+        pairs = float(m.sum())
+        flops += 4.0 * w.head_dim * pairs
+        if w.with_grad:
+            oracle.rank_share_backward(g["q"], g["k"], g["v"], dout_local, w.layout, w.world,
+                                       w.rank, w.causal, cu, rows=rows, heads=[0])
+            flops += 10.0 * w.head_dim * pairs
+        done_rows += len(rows)
+    el = time.perf_counter() - t0
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 numpy oracle, {'fwd+bwd' if w.with_grad else 'fwd'} of {done_rows} "
+                      f"query rows x 1 head of the same rank share ({flops / 1e9:.1f} GFLOP "
+                      f"algorithmic) in {el:.1f} s"}
+
+
+def merge_bandwidth(ca, torch, rows=524288, d=128, reps=20):
+    """Standalone LSE merge at 524288 rows x 128 (the zigzag rank share's
+    per-step partial, 774 MiB per call, larger than the 256 MB MALL)."""
+    B, H = 1, 32
+    S = rows // H
+    o = torch.randn(B, S, H, d, device="cuda")
+    oj = torch.randn(B, S, H, d, device="cuda")
+    l = torch.randn(B, H, S, device="cuda")
+    lj = torch.randn(B, H, S, device="cuda")
+    for _ in range(3):
+        ca.ring_attn_lse_merge(o, l, oj, lj)
+    torch.cuda.synchronize()
+    ca.ring_attn_timing_enable(False)
+    ca.ring_attn_timing_enable(True)
+    for _ in range(reps):
+        ca.ring_attn_lse_merge(o, l, oj, lj)
+    n, ms = ca.ring_attn_timing_read("lse_merge")
+    ca.ring_attn_timing_enable(False)
+    nbytes = (12 * d + 12) * rows
+    gbs = nbytes / (ms / n * 1e-3) / 1e9
+    return {"kernel": "lse_merge", "rows": rows, "head_dim": d, "bytes_per_launch": nbytes,
+            "avg_ms": ms / n, "GB/s": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="basic_s8192")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-merge", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one rank's share on ONE GPU; multi-GPU runs are not part of "
+              "this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import context_attention_flash_amd as ca
+    from context_attention_flash_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    g, desc, t = build_inputs(ca, w, torch)
+    sched = ca.ring_attn_schedule(desc, w.cu_seqlens)
+    pairs = sum(p for _, _, p in sched)
+    heads_b = w.heads_q * w.batch
+    fwd_flops = 4.0 * w.head_dim * heads_b * pairs
+    bwd_flops = 10.0 * w.head_dim * heads_b * pairs if w.with_grad else 0.0
+
+    ws_f = ca.alloc_workspace(desc, False)
+    out = torch.empty_like(t["q"])
+    lse = torch.empty(w.batch, w.heads_q, w.seqlen // w.world, device="cuda")
+    if w.with_grad:
+        ws_b = ca.alloc_workspace(desc, True)
+        dq = torch.empty(t["q"].shape, dtype=torch.float32, device="cuda")
+        dk = torch.zeros(t["k"].shape, dtype=torch.float32, device="cuda")
+        dv = torch.zeros(t["v"].shape, dtype=torch.float32, device="cuda")
+
+    def step():
+        ca.ring_attn_fwd(desc, t["q"], t["k"], t["v"], w.cu_seqlens, out, lse, ws_f)
+        if w.with_grad:
+            ca.ring_attn_bwd(desc, t["dout"], t["q"], t["k"], t["v"], out, lse, w.cu_seqlens,
+                             dq, dk, dv, ws_b)
+
+    for i in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    # timed region: K steps; per-kernel HIP events on the launching stream
+    ca.ring_attn_timing_enable(False)
+    ca.ring_attn_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern = {}
+    for name in ("fwd_step", "bwd_pre", "bwd_step", "lse_merge", "finalize"):
+        n, ms = ca.ring_attn_timing_read(name)
+        if n:
+            kern[name] = {"launches": n // args.steps, "ms_per_step": ms / args.steps,
+                          "avg_launch_ms": ms / n}
+    ca.ring_attn_timing_enable(False)
+    log(f"timed {args.steps} steps in {elapsed:.3f}s")
+    assert torch.isfinite(out.float()).all().item(), "non-finite output"
+
+    ms_step = elapsed / args.steps * 1e3
+    total_flops = fwd_flops + bwd_flops
+    value = total_flops / (ms_step * 1e-3) / 1e12
+    if "fwd_step" in kern:
+        kern["fwd_step"]["TFLOP/s"] = fwd_flops / (kern["fwd_step"]["ms_per_step"] * 1e-3) / 1e12
+    if "bwd_step" in kern:
+        kern["bwd_step"]["TFLOP/s"] = bwd_flops / (kern["bwd_step"]["ms_per_step"] * 1e-3) / 1e12
+
+    dom = "bwd_step" if w.with_grad else "fwd_step"
+    dom_flops = bwd_flops if w.with_grad else fwd_flops
+    n_launch = kern[dom]["launches"]
+    achieved = (dom_flops / n_launch) / (kern[dom]["avg_launch_ms"] * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "flops_per_launch": dom_flops / n_launch,
+                "avg_launch_ms": kern[dom]["avg_launch_ms"]}
+
+    res = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded N(0,1), bf16-rounded)",
+        "config": {"workload": f"{w.name}: {'basic' if w.layout == 0 else w.layout} "
+                               f"{'causal' if w.causal else 'non-causal'} "
+                               f"{'fwd+bwd' if w.with_grad else 'fwd'} rank share",
+                   "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+                   "head_dim": w.head_dim, "global_seqlen": w.seqlen, "world": w.world,
+                   "rank": w.rank, "shard_rows": w.seqlen // w.world,
+                   "visible_pairs_per_head": pairs, "fwd_tflop": fwd_flops / 1e12,
+                   "bwd_tflop": bwd_flops / 1e12},
+        "roofline": roofline,
+        "kernels": kern,
+        "mfma_frac_whole_step": value / PEAK_BF16_TFLOPS,
+    }
+    if not args.no_merge:
+        res["merge"] = merge_bandwidth(ca, torch)
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host ...")
+        res["cpu_baseline"] = cpu_baseline(w, g, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

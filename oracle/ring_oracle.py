@@ -304,7 +304,8 @@ def ring_forward(q_glob, k_glob, v_glob, layout: int, world: int, rank: int,
 
 def rank_share_backward(q_glob, k_glob, v_glob, dout_local, layout: int, world: int,
                         rank: int, causal: bool, cu_seqlens=None,
-                        scale: Optional[float] = None):
+                        scale: Optional[float] = None, rows: Optional[np.ndarray] = None,
+                        heads: Optional[Sequence[int]] = None):
     """Gradients of  sum(dout * out)  over the rank's rows.
 
     With P_tu = exp(scale <q_t,k_u> - lse_t) on visible pairs (0 elsewhere) and
@@ -320,6 +321,9 @@ def rank_share_backward(q_glob, k_glob, v_glob, dout_local, layout: int, world: 
     dout_local [B, S, Hq, d] in the rank's local order.
     Returns dq [B, S, Hq, d] and dk, dv per KV block in block-major order,
     [nblocks, B, Skv, Hkv, d] (LLAMA3: one gathered block of N rows).
+    ``rows`` (local row indices) and ``heads`` optionally restrict the sum to
+    those query rows and heads: dq then holds those rows in the given order
+    and dk, dv hold only their contribution (used to time a bounded sample).
     """
     B, N, Hq, d = q_glob.shape
     Hkv = k_glob.shape[2]
@@ -327,33 +331,42 @@ def rank_share_backward(q_glob, k_glob, v_glob, dout_local, layout: int, world: 
         scale = default_scale(d)
     cu = cu_seqlens if layout in (VARLEN_RING, LLAMA3) else None
     pos_q = positions(layout, N, world, rank, cu)
+    local = np.arange(len(pos_q)) if rows is None else np.asarray(rows)
+    pos_q = pos_q[local]
     S = len(pos_q)
     pos_k = np.arange(N, dtype=np.int64)
     mask = allowed(pos_q, pos_k, causal, cu)
-    dq = np.zeros((B, S, Hq, d))
-    dk_g = np.zeros((B, N, Hkv, d))
-    dv_g = np.zeros((B, N, Hkv, d))
-    for bi in range(B):
-        for h in range(Hq):
-            hk = kv_head_of(h, Hq, Hkv)
-            q = q_glob[bi, pos_q, h].astype(np.float64)
-            k = k_glob[bi, :, hk].astype(np.float64)
-            v = v_glob[bi, :, hk].astype(np.float64)
-            do = dout_local[bi, :, h].astype(np.float64)
-            out, lse = attention_rows(q, k, v, mask, scale)
-            s = scale * (q @ k.T)
-            finite = np.isfinite(lse)
-            p = np.where(mask & finite[:, None],
-                         np.exp(np.where(mask, s, 0.0) - np.where(finite, lse, 0.0)[:, None]), 0.0)
-            delta = (do * out).sum(axis=1)
-            dv_g[bi, :, hk] += p.T @ do
-            ds = p * (do @ v.T - delta[:, None])
-            dq[bi, :, h] = scale * (ds @ k)
-            dk_g[bi, :, hk] += scale * (ds.T @ q)
     nb = num_blocks(layout, world)
     blocks = [kv_positions(layout, N, world, j, cu) for j in range(nb)]
-    dk = np.stack([dk_g[:, pk] for pk in blocks])
-    dv = np.stack([dv_g[:, pk] for pk in blocks])
+    dq = np.zeros((B, S, Hq, d))
+    dk = np.zeros((nb, B, len(blocks[0]), Hkv, d))
+    dv = np.zeros((nb, B, len(blocks[0]), Hkv, d))
+    q_heads = list(range(Hq)) if heads is None else list(heads)
+    for bi in range(B):
+        for hk in sorted({kv_head_of(h, Hq, Hkv) for h in q_heads}):
+            # gradients of every global key of KV head hk, summed over its q heads
+            dk_h = np.zeros((N, d))
+            dv_h = np.zeros((N, d))
+            k = k_glob[bi, :, hk].astype(np.float64)
+            v = v_glob[bi, :, hk].astype(np.float64)
+            for h in q_heads:
+                if kv_head_of(h, Hq, Hkv) != hk:
+                    continue
+                q = q_glob[bi, pos_q, h].astype(np.float64)
+                do = dout_local[bi, local, h].astype(np.float64)
+                out, lse = attention_rows(q, k, v, mask, scale)
+                s = scale * (q @ k.T)
+                finite = np.isfinite(lse)
+                p = np.where(mask & finite[:, None],
+                             np.exp(np.where(mask, s, 0.0) - np.where(finite, lse, 0.0)[:, None]), 0.0)
+                delta = (do * out).sum(axis=1)
+                dv_h += p.T @ do
+                ds = p * (do @ v.T - delta[:, None])
+                dq[bi, :, h] = scale * (ds @ k)
+                dk_h += scale * (ds.T @ q)
+            for j, pk in enumerate(blocks):
+                dk[j, bi, :, hk] = dk_h[pk]
+                dv[j, bi, :, hk] = dv_h[pk]
     return dq, dk, dv
 
 
