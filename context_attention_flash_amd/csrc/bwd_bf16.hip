@@ -9,12 +9,18 @@
 //   S = Q K^T and dP = dO V^T        (C layout: lane = key, 16 query rows)
 //   P = exp(scale*S - lse), dS = P (dP - Delta)
 //   dV^T += dO^T P,  dK^T += Q^T dS  (fp32 accumulators in registers)
-//   dQ += scale * dS K               (dS staged in LDS, fp32 atomics to HBM)
-// P and dS feed the next MFMAs straight from the accumulator registers, so
-// Q^T and dO^T are stored in LDS with the matching query order inside every
-// 16-row group ({0-3, 8-11, 4-7, 12-15}).  dK/dV are added to the caller's
-// fp32 buffers once at the end: every key tile of a block has one owner per
-// launch, so no atomics are needed there.
+//   dQ += scale * dS K               (fp32 atomics to HBM)
+// Q, dO and K live in LDS in their natural row layout only.  The transposed
+// operands (dO^T, Q^T, and K as the B operand of dQ) come from the gfx950 LDS
+// transpose read ds_read_b64_tr_b16: within each 16-lane group, result lane i,
+// element k is the 16-bit value at (address of lane 4k + i/4) + 2*(i%4), so a
+// group turns a 4-row x 16-column K-major block into MFMA operand layout.  P
+// and dS feed the MFMAs straight from the accumulator registers, whose query
+// order inside each 16-row group is {0-3, 8-11 | 4-7, 12-15} (lanes 0-31 |
+// 32-63); the transpose reads pick their rows in that same order.  dS goes to
+// LDS as dS^T [key][query] with 8-byte writes for the dQ product.  dK/dV are
+// added to the caller's buffers once at the end: every key tile of a block has
+// one owner per launch.
 #include "kernel_args.h"
 #include "kernel_common.h"
 
@@ -26,79 +32,99 @@ struct BwdCfg {
     static constexpr int BQ = BWD_BQ, BK = BWD_BK;
     static constexpr int NKS = DH / 16;
     static constexpr int NDT = DH / 32;
-    static constexpr int ROWB = DH * 2;             // natural Q/dO row (bytes)
+    static constexpr int ROWB = DH * 2;             // natural row (bytes)
     static constexpr int KCH = DH / 8;              // 16-byte chunks per natural row
-    static constexpr int NAT_BYTES = BQ * ROWB;     // Q or dO tile, natural
-    static constexpr int TR_BYTES = DH * BQ * 2;    // Q^T or dO^T tile (64 queries per row)
-    static constexpr int KT_BYTES = DH * BK * 2;    // K^T of the work-group's keys
-    static constexpr int DS_BYTES = BQ * BK * 2;    // dS [64 q][128 keys]
+    static constexpr int Q_BYTES = BQ * ROWB;
+    static constexpr int K_BYTES = BK * ROWB;
+    static constexpr int DST_ROWB = BQ * 2;         // dS^T row: 64 queries
+    static constexpr int DST_BYTES = BK * DST_ROWB;
     static constexpr int OFF_Q = 0;
-    static constexpr int OFF_DO = OFF_Q + NAT_BYTES;
-    static constexpr int OFF_QT = OFF_DO + NAT_BYTES;
-    static constexpr int OFF_DOT = OFF_QT + TR_BYTES;
-    static constexpr int OFF_KT = OFF_DOT + TR_BYTES;
-    static constexpr int OFF_DS = OFF_KT + KT_BYTES;
-    static constexpr int OFF_ROW = OFF_DS + DS_BYTES;  // lse2, delta, a, b per query row
+    static constexpr int OFF_DO = OFF_Q + Q_BYTES;
+    static constexpr int OFF_K = OFF_DO + Q_BYTES;
+    static constexpr int OFF_V = OFF_K + K_BYTES;
+    static constexpr int OFF_DST = OFF_V + K_BYTES;
+    static constexpr int OFF_ROW = OFF_DST + DST_BYTES;  // lse2, delta, a, b per query row
     static constexpr int LDS = OFF_ROW + 4 * BQ * 4;
-    static constexpr int LD = BQ * KCH / 4 / NT;       // 4-row x 16-byte loads per thread
-    static_assert(BQ * KCH / 4 == NT || BQ * KCH / 4 == NT / 2, "tile shape");
-    static constexpr int LDT = BQ * KCH / 4;           // threads that take part in a load
+    static constexpr int LDT = BQ * KCH / 4;        // threads taking part in a Q/dO load
+    static_assert(LDT == NT || LDT == NT / 2, "tile shape");
 };
 
-template <int KCH>
-__device__ __forceinline__ int nat_swz(int row) {
-    return KCH == 16 ? (row & 15) : ((row >> 1) & 7);
+// 16-byte slot of logical chunk c in row r.  Rows of 16 chunks (256 B) and of
+// 8 chunks (128 B, two rows per bank cycle) have their own XOR patterns; both
+// keep 16 consecutive rows at one chunk, and 4 consecutive rows x 2 chunks,
+// free of bank conflicts.
+template <int NCH>
+__device__ __forceinline__ int slot(int r, int c) {
+    if (NCH == 16) return c ^ (((r & 7) << 1) | ((r >> 3) & 1));
+    return c ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
 }
-__device__ __forceinline__ int tr_swz(int d) { return (d >> 1) & 7; }
-__device__ __forceinline__ int grp_slot(int m) { return m == 1 ? 2 : (m == 2 ? 1 : m); }
 
-// Global -> registers: 4 consecutive query rows x one 16-byte chunk of Q and dO.
+template <int NCH>
+__device__ __forceinline__ int row_off(int r, int c) {
+    return r * (NCH * 16) + (slot<NCH>(r, c) << 4);
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2_t lds_tr16(const unsigned char* p) {
+    const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(p));
+    return __builtin_bit_cast(u32x2_t, r);
+}
+
+// MFMA operand (8 bf16 per lane) from a K-major LDS block: rows r1 + j/4 and
+// r2 + j/4 (j = lane % 16) give elements 0-3 and 4-7; columns start at c0
+// (element index, multiple of 16) + 16 * ((lane / 16) % 2).
+template <int NCH>
+__device__ __forceinline__ u32x4_t tr_operand(const unsigned char* base, int r1, int r2, int c0,
+                                              int lane) {
+    const int j = lane & 15;
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);   // element index
+    const int c = col >> 3, byte = (col & 7) * 2;
+    const u32x2_t a = lds_tr16(base + row_off<NCH>(r1 + (j >> 2), c) + byte);
+    const u32x2_t b = lds_tr16(base + row_off<NCH>(r2 + (j >> 2), c) + byte);
+    return (u32x4_t){a[0], a[1], b[0], b[1]};
+}
+
+// Global -> registers: 4 consecutive query rows x one 16-byte chunk of Q and
+// dO, plus the per-row values of row tid.
 template <int DH>
 struct BwdTileRegs {
     u32x4_t q[4], o[4];
+    float l2, dl;   // lse * log2(e) (+inf: row sees no key) and Delta
+    int a, b;       // visible key interval
 };
 
 template <int DH>
-__device__ __forceinline__ void bwd_load_tile(BwdTileRegs<DH>& R, const uint16_t* qh,
-                                              const uint16_t* oh, int64_t row_stride, int qt,
-                                              int S, int tid) {
+__device__ __forceinline__ void bwd_load_tile(BwdTileRegs<DH>& R, const BwdArgs& p, int b, int h,
+                                              int qt, int tid) {
     using C = BwdCfg<DH>;
-    if (tid >= C::LDT) return;
-    const int m = tid / C::KCH, ch = tid % C::KCH;
+    const int q_stride = p.Hq * DH;
+    if (tid < C::LDT) {
+        const uint16_t* qh = p.q + ((int64_t)b * p.S) * q_stride + h * DH;
+        const uint16_t* oh = p.dout + ((int64_t)b * p.S) * q_stride + h * DH;
+        const int m = tid / C::KCH, ch = tid % C::KCH;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        const int row = min(qt * C::BQ + 4 * m + rr, S - 1);
-        R.q[rr] = *(const u32x4_t*)(qh + row * row_stride + ch * 8);
-        R.o[rr] = *(const u32x4_t*)(oh + row * row_stride + ch * 8);
-    }
-}
-
-// Registers -> LDS, natural rows and transposed (head dim major) copies.
-template <int DH>
-__device__ __forceinline__ void bwd_store_one(const u32x4_t (&x)[4], unsigned char* nat,
-                                              unsigned char* tr, int tid) {
-    using C = BwdCfg<DH>;
-    const int m = tid / C::KCH, ch = tid % C::KCH;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        const int row = 4 * m + rr;
-        *(u32x4_t*)(nat + row * C::ROWB + ((ch ^ nat_swz<C::KCH>(row)) << 4)) = x[rr];
-    }
-    const int sp = 16 * (m >> 2) + 4 * grp_slot(m & 3);  // stored position of rows 4m..4m+3
-    const int chunk = sp >> 3, inner = (sp & 7) * 2;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int d = ch * 8 + e, w = e >> 1;
-        const uint32_t a0 = x[0][w], a1 = x[1][w], a2 = x[2][w], a3 = x[3][w];
-        u32x2_t o;
-        if (e & 1) {
-            o[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-            o[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-        } else {
-            o[0] = (a0 & 0xffffu) | (a1 << 16);
-            o[1] = (a2 & 0xffffu) | (a3 << 16);
+        for (int rr = 0; rr < 4; ++rr) {
+            const int row = min(qt * C::BQ + 4 * m + rr, p.S - 1);
+            R.q[rr] = *(const u32x4_t*)(qh + (int64_t)row * q_stride + ch * 8);
+            R.o[rr] = *(const u32x4_t*)(oh + (int64_t)row * q_stride + ch * 8);
         }
-        *(u32x2_t*)(tr + d * (C::BQ * 2) + ((chunk ^ tr_swz(d)) << 4) + inner) = o;
+    }
+    if (tid < C::BQ) {
+        const int iq = qt * C::BQ + tid;
+        const int iqc = min(iq, p.S - 1);
+        const float L = p.lse[((int64_t)b * p.Hq + h) * p.S + iqc];
+        R.dl = p.delta[((int64_t)b * p.Hq + h) * p.S_pad + iqc];
+        R.a = p.rng[2 * iqc];
+        R.b = p.rng[2 * iqc + 1];
+        R.l2 = L == -INFINITY ? INFINITY : L * kLog2e;
+        if (iq >= p.S) {  // rows past the shard contribute nothing
+            R.l2 = INFINITY;
+            R.dl = 0.f;
+            R.a = 0;
+            R.b = 0;
+        }
     }
 }
 
@@ -108,13 +134,12 @@ __global__ __launch_bounds__(256, 1) void bwd_step_bf16_kernel(BwdArgs p) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
     unsigned char* sQ = smem + C::OFF_Q;
     unsigned char* sDO = smem + C::OFF_DO;
-    unsigned char* sQT = smem + C::OFF_QT;
-    unsigned char* sDOT = smem + C::OFF_DOT;
-    unsigned char* sKT = smem + C::OFF_KT;
-    unsigned char* sDS = smem + C::OFF_DS;
-    float* sL = (float*)(smem + C::OFF_ROW);        // lse * log2(e) (+inf: no key visible)
-    float* sD = sL + C::BQ;                         // Delta
-    int32_t* sA = (int32_t*)(sD + C::BQ);           // visible key interval [a, b)
+    unsigned char* sK = smem + C::OFF_K;
+    unsigned char* sV = smem + C::OFF_V;
+    unsigned char* sDST = smem + C::OFF_DST;
+    float* sL = (float*)(smem + C::OFF_ROW);
+    float* sD = sL + C::BQ;
+    int32_t* sA = (int32_t*)(sD + C::BQ);
     int32_t* sB = sA + C::BQ;
 
     const int tid = threadIdx.x;
@@ -127,42 +152,18 @@ __global__ __launch_bounds__(256, 1) void bwd_step_bf16_kernel(BwdArgs p) {
     const int e0 = p.t_off[kt], e1 = p.t_off[kt + 1];
     const int group = p.Hq / p.Hkv;
 
-    const int64_t kv_stride = (int64_t)p.Hkv * DH;
+    const int kv_stride = p.Hkv * DH;
     const uint16_t* kb = p.k + (int64_t)b * p.Skv * kv_stride + hk * DH;
     const uint16_t* vb = p.v + (int64_t)b * p.Skv * kv_stride + hk * DH;
     const int key = kt * C::BK + wave * 32 + l32;   // this lane's key (C-layout column)
     const int keyc = min(key, p.Skv - 1);
 
-    // Stationary operands: K and V rows of this lane's key (B operands of S, dP).
-    u32x4_t kreg[C::NKS], vreg[C::NKS];
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-        kreg[ks] = *(const u32x4_t*)(kb + keyc * kv_stride + 16 * ks + 8 * g);
-        vreg[ks] = *(const u32x4_t*)(vb + keyc * kv_stride + 16 * ks + 8 * g);
-    }
-    // K^T of the 128 keys in LDS (B operand of dQ = dS K): row d, keys contiguous.
-    for (int idx = tid; idx < (C::BK / 4) * C::KCH; idx += C::NT) {
-        const int m = idx / C::KCH, ch = idx % C::KCH;
-        u32x4_t x[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int kr = min(kt * C::BK + 4 * m + rr, p.Skv - 1);
-            x[rr] = *(const u32x4_t*)(kb + kr * kv_stride + ch * 8);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int d = ch * 8 + e, w = e >> 1;
-            u32x2_t o;
-            if (e & 1) {
-                o[0] = (x[0][w] >> 16) | (x[1][w] & 0xffff0000u);
-                o[1] = (x[2][w] >> 16) | (x[3][w] & 0xffff0000u);
-            } else {
-                o[0] = (x[0][w] & 0xffffu) | (x[1][w] << 16);
-                o[1] = (x[2][w] & 0xffffu) | (x[3][w] << 16);
-            }
-            const int kp = 4 * m;  // key position in the row
-            *(u32x2_t*)(sKT + d * (C::BK * 2) + (((kp >> 3) ^ (d & 15)) << 4) + (kp & 7) * 2) = o;
-        }
+    // K and V tiles of the work-group in LDS (natural rows).
+    for (int idx = tid; idx < C::BK * C::KCH; idx += C::NT) {
+        const int r = idx / C::KCH, ch = idx % C::KCH;
+        const int64_t kr = min(kt * C::BK + r, p.Skv - 1);
+        *(u32x4_t*)(sK + row_off<C::KCH>(r, ch)) = *(const u32x4_t*)(kb + kr * kv_stride + ch * 8);
+        *(u32x4_t*)(sV + row_off<C::KCH>(r, ch)) = *(const u32x4_t*)(vb + kr * kv_stride + ch * 8);
     }
 
     f32x16_t dk_acc[C::NDT], dv_acc[C::NDT];
@@ -172,141 +173,193 @@ __global__ __launch_bounds__(256, 1) void bwd_step_bf16_kernel(BwdArgs p) {
         dv_acc[dt] = (f32x16_t){};
     }
     const float c2 = p.scale_log2;
-    const int64_t q_stride = (int64_t)p.Hq * DH;
     const int n_ent = e1 - e0;
     const int n_iter = n_ent * group;
 
-    BwdTileRegs<DH> R;
-    if (n_iter > 0) {
-        const int h0 = hk * group;
-        const int qt0 = p.t_ent[e0] & 0x7fffffff;
-        bwd_load_tile<DH>(R, p.q + ((int64_t)b * p.S) * q_stride + h0 * DH,
-                          p.dout + ((int64_t)b * p.S) * q_stride + h0 * DH, q_stride, qt0, p.S, tid);
+    // Per-lane LDS offsets.  Every swizzle below depends only on the low four
+    // bits of the row, so moving by 16 or 32 rows is a constant offset.
+    //   nat[ks]    : natural read of row l32, chunk 2ks+g (S and dP A operands)
+    //   trq[r][dt] : transpose read of rows {4g, 8+4g} + j/4, head-dim block dt
+    //   trd[r]     : transpose read of dS^T rows {8g, 8g+4} + j/4, query block mt_q
+    //   trk[r][tw] : transpose read of K rows {8g, 8g+4} + j/4, head-dim block nt
+    constexpr int TILES = 2 * C::NDT;
+    constexpr int PER_WAVE = TILES / 4;
+    const int mt_q = (wave * PER_WAVE) / C::NDT;
+    const int j = lane & 15, gsel = (lane >> 4) & 1;
+    int nat[C::NKS];
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) nat[ks] = row_off<C::KCH>(l32, 2 * ks + g);
+    int trq[2][C::NDT];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) {
+            const int col = 32 * dt + 16 * gsel + 4 * (j & 3);
+            trq[r][dt] = row_off<C::KCH>(8 * r + 4 * g + (j >> 2), col >> 3) + (col & 7) * 2;
+        }
+    int trd[2], trk[2][PER_WAVE];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int colq = 32 * mt_q + 16 * gsel + 4 * (j & 3);
+        trd[r] = row_off<8>(8 * g + 4 * r + (j >> 2), colq >> 3) + (colq & 7) * 2;
+#pragma unroll
+        for (int tw = 0; tw < PER_WAVE; ++tw) {
+            const int nt = (wave * PER_WAVE + tw) % C::NDT;
+            const int cold = 32 * nt + 16 * gsel + 4 * (j & 3);
+            trk[r][tw] = row_off<C::KCH>(8 * g + 4 * r + (j >> 2), cold >> 3) + (cold & 7) * 2;
+        }
     }
+    const int dst_w = row_off<8>(wave * 32 + l32, 0);  // dS^T row of this lane's key
+    const int dst_x = slot<8>(wave * 32 + l32, 0);     // its chunk swizzle
+
+    BwdTileRegs<DH> R;
+    if (n_iter > 0) bwd_load_tile<DH>(R, p, b, hk * group, p.t_ent[e0] & 0x7fffffff, tid);
     for (int it = 0; it < n_iter; ++it) {
-        const int hh = it / n_ent, ei = e0 + it % n_ent;
-        const int h = hk * group + hh;
-        const int ent = p.t_ent[ei];
+        const int h = hk * group + it / n_ent;
+        const int ent = p.t_ent[e0 + it % n_ent];
         const int qt = ent & 0x7fffffff;
         const bool partial = ent < 0;
+        // Keep the dK/dV accumulators in AGPRs across iterations (the MFMAs
+        // accumulate there directly; no VALU touches them inside the loop).
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) asm volatile("" : "+a"(dk_acc[dt]), "+a"(dv_acc[dt]));
 
-        __syncthreads();  // previous iteration's readers of the Q/dO/dS stages are done
+        __syncthreads();  // previous iteration's readers of the Q/dO/dS^T stages are done
         if (tid < C::LDT) {
-            bwd_store_one<DH>(R.q, sQ, sQT, tid);
-            bwd_store_one<DH>(R.o, sDO, sDOT, tid);
+            const int m = tid / C::KCH, ch = tid % C::KCH;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                *(u32x4_t*)(sQ + row_off<C::KCH>(4 * m + rr, ch)) = R.q[rr];
+                *(u32x4_t*)(sDO + row_off<C::KCH>(4 * m + rr, ch)) = R.o[rr];
+            }
         }
         if (tid < C::BQ) {
-            const int iq = qt * C::BQ + tid;
-            float l2 = INFINITY, dl = 0.f;
-            int a = 0, bb = 0;
-            if (iq < p.S) {
-                const float L = p.lse[((int64_t)b * p.Hq + h) * p.S + iq];
-                l2 = L == -INFINITY ? INFINITY : L * kLog2e;
-                dl = p.delta[((int64_t)b * p.Hq + h) * p.S_pad + iq];
-                a = p.rng[2 * iq];
-                bb = p.rng[2 * iq + 1];
-            }
-            sL[tid] = l2;
-            sD[tid] = dl;
-            sA[tid] = a;
-            sB[tid] = bb;
+            sL[tid] = R.l2;
+            sD[tid] = R.dl;
+            sA[tid] = R.a;
+            sB[tid] = R.b;
         }
         __syncthreads();
-        if (it + 1 < n_iter) {
-            const int hn = hk * group + (it + 1) / n_ent;
-            const int qn = p.t_ent[e0 + (it + 1) % n_ent] & 0x7fffffff;
-            bwd_load_tile<DH>(R, p.q + ((int64_t)b * p.S) * q_stride + hn * DH,
-                              p.dout + ((int64_t)b * p.S) * q_stride + hn * DH, q_stride, qn, p.S,
-                              tid);
-        }
+        if (it + 1 < n_iter)
+            bwd_load_tile<DH>(R, p, b, hk * group + (it + 1) / n_ent,
+                              p.t_ent[e0 + (it + 1) % n_ent] & 0x7fffffff, tid);
 
-        // S = Q K^T and dP = dO V^T: two 32-row halves of the 64-row tile.
+        // S = Q K^T and dP = dO V^T: two 32-row halves of the 64-row tile; the
+        // B operands are this lane's K and V rows (key 32*wave + l32).
         f32x16_t sacc[2], pacc[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             sacc[mt] = (f32x16_t){};
             pacc[mt] = (f32x16_t){};
-            const int row = 32 * mt + l32;
-            const int sw = nat_swz<C::KCH>(row);
+        }
 #pragma unroll
-            for (int ks = 0; ks < C::NKS; ++ks) {
-                const int off = row * C::ROWB + (((2 * ks + g) ^ sw) << 4);
-                sacc[mt] = mfma_32x32x16(*(const u32x4_t*)(sQ + off), kreg[ks], sacc[mt]);
-                pacc[mt] = mfma_32x32x16(*(const u32x4_t*)(sDO + off), vreg[ks], pacc[mt]);
+        for (int ks = 0; ks < C::NKS; ++ks) {
+            const u32x4_t kb4 = *(const u32x4_t*)(sK + nat[ks] + wave * 32 * C::ROWB);
+            const u32x4_t vb4 = *(const u32x4_t*)(sV + nat[ks] + wave * 32 * C::ROWB);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const u32x4_t qa = *(const u32x4_t*)(sQ + nat[ks] + mt * 32 * C::ROWB);
+                const u32x4_t oa = *(const u32x4_t*)(sDO + nat[ks] + mt * 32 * C::ROWB);
+                sacc[mt] = mfma_32x32x16(qa, kb4, sacc[mt]);
+                pacc[mt] = mfma_32x32x16(oa, vb4, pacc[mt]);
             }
         }
-        // P and dS; element (mt, r) is query row 32*mt + 8*(r/4) + 4*g + r%4.
+        // P (in sacc) and dS (in pacc); element (mt, r) is query row
+        // 32*mt + 8*(r/4) + 4*g + r%4.
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const f32x4_t L = *(const f32x4_t*)(sL + 32 * mt + 8 * rg + 4 * g);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sacc[mt][4 * rg + i] = fast_exp2(fmaf(sacc[mt][4 * rg + i], c2, -L[i]));
+            }
+        if (partial) {  // keys outside a row's interval [a, b) are invisible
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) {
+                    const int r0 = 32 * mt + 8 * rg + 4 * g;
+                    const int4 A4 = *(const int4*)(sA + r0);
+                    const int4 B4 = *(const int4*)(sB + r0);
+                    const int av[4] = {A4.x, A4.y, A4.z, A4.w}, bv[4] = {B4.x, B4.y, B4.z, B4.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool vis = (key >= av[i]) & (key < bv[i]);
+                        sacc[mt][4 * rg + i] = vis ? sacc[mt][4 * rg + i] : 0.f;
+                    }
+                }
+        }
         u32x4_t pb[4], db[4];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 const int r0 = 32 * mt + 8 * rg + 4 * g;
-                const f32x4_t L = *(const f32x4_t*)(sL + r0);
                 const f32x4_t Dl = *(const f32x4_t*)(sD + r0);
-                float pv[4], dsv[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float pr = fast_exp2(fmaf(sacc[mt][4 * rg + i], c2, -L[i]));
-                    if (partial) {
-                        const bool vis = key >= sA[r0 + i] && key < sB[r0 + i];
-                        pr = vis ? pr : 0.f;
-                    }
-                    pv[i] = pr;
-                    dsv[i] = pr * (pacc[mt][4 * rg + i] - Dl[i]);
-                }
+                for (int i = 0; i < 4; ++i)
+                    pacc[mt][4 * rg + i] = sacc[mt][4 * rg + i] * (pacc[mt][4 * rg + i] - Dl[i]);
                 const int kk = 2 * mt + (rg >> 1), w = (rg & 1) * 2;
-                pb[kk][w] = pack_bf16x2(pv[0], pv[1]);
-                pb[kk][w + 1] = pack_bf16x2(pv[2], pv[3]);
-                db[kk][w] = pack_bf16x2(dsv[0], dsv[1]);
-                db[kk][w + 1] = pack_bf16x2(dsv[2], dsv[3]);
-                // dS -> LDS [query][key] for the dQ product
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int qrow = r0 + i, kcol = wave * 32 + l32;
-                    const uint32_t wv = db[kk][w + (i >> 1)];
-                    const uint16_t hv = (i & 1) ? (uint16_t)(wv >> 16) : (uint16_t)(wv & 0xffff);
-                    *(uint16_t*)(sDS + qrow * (C::BK * 2) + (((kcol >> 3) ^ (qrow & 15)) << 4) +
-                                 (kcol & 7) * 2) = hv;
-                }
+                pb[kk][w] = pack_bf16x2(sacc[mt][4 * rg], sacc[mt][4 * rg + 1]);
+                pb[kk][w + 1] = pack_bf16x2(sacc[mt][4 * rg + 2], sacc[mt][4 * rg + 3]);
+                db[kk][w] = pack_bf16x2(pacc[mt][4 * rg], pacc[mt][4 * rg + 1]);
+                db[kk][w + 1] = pack_bf16x2(pacc[mt][4 * rg + 2], pacc[mt][4 * rg + 3]);
+                // dS^T [key][query]: this lane's key row, queries r0..r0+3
+                // (chunk r0/8 = 4mt + rg, half g)
+                *(u32x2_t*)(sDST + dst_w - (dst_x << 4) + (((4 * mt + rg) ^ dst_x) << 4) + 8 * g) =
+                    (u32x2_t){db[kk][w], db[kk][w + 1]};
             }
-        // dV^T += dO^T P and dK^T += Q^T dS
+        // dV^T += dO^T P and dK^T += Q^T dS; the K dimension (queries) of step
+        // kk takes rows 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3.
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt) {
-            const int row = 32 * dt + l32;
-            const int sw = tr_swz(row);
+            u32x4_t oa[4], qa[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const int off = row * (C::BQ * 2) + (((2 * kk + g) ^ sw) << 4);
-                dv_acc[dt] = mfma_32x32x16(*(const u32x4_t*)(sDOT + off), pb[kk], dv_acc[dt]);
-                dk_acc[dt] = mfma_32x32x16(*(const u32x4_t*)(sQT + off), db[kk], dk_acc[dt]);
+                const int o16 = kk * 16 * C::ROWB;
+                const u32x2_t o1 = lds_tr16(sDO + trq[0][dt] + o16), o2 = lds_tr16(sDO + trq[1][dt] + o16);
+                const u32x2_t q1 = lds_tr16(sQ + trq[0][dt] + o16), q2 = lds_tr16(sQ + trq[1][dt] + o16);
+                oa[kk] = (u32x4_t){o1[0], o1[1], o2[0], o2[1]};
+                qa[kk] = (u32x4_t){q1[0], q1[1], q2[0], q2[1]};
+            }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                dv_acc[dt] = mfma_32x32x16(oa[kk], pb[kk], dv_acc[dt]);
+                dk_acc[dt] = mfma_32x32x16(qa[kk], db[kk], dk_acc[dt]);
             }
         }
-        __syncthreads();  // dS of every wave is in LDS
+        __syncthreads();  // dS^T of every wave is in LDS
 
-        // dQ[64 x DH] = dS[64 x 128] K[128 x DH]; wave tiles (mt, nt) of 32 x 32.
-        constexpr int TILES = 2 * C::NDT;
-        constexpr int PER_WAVE = TILES / 4;
+        // dQ[64 x DH] = dS[64 x 128] K[128 x DH]; wave tiles (mt_q, nt) of 32 x 32,
+        // both operands from transpose reads (keys 16ks + 8g + 0..7 in order).
+        const int rows_left = p.S - qt * C::BQ;  // >= 1
+        const int qs = p.Hq * DH;
 #pragma unroll
         for (int tw = 0; tw < PER_WAVE; ++tw) {
-            const int tile = wave * PER_WAVE + tw;
-            const int mt = tile / C::NDT, nt = tile % C::NDT;
+            const int nt = (wave * PER_WAVE + tw) % C::NDT;
             f32x16_t acc = (f32x16_t){};
-            const int arow = 32 * mt + l32, brow = 32 * nt + l32;
+            u32x4_t da[C::BK / 16], ka[C::BK / 16];
 #pragma unroll
             for (int ks = 0; ks < C::BK / 16; ++ks) {
-                const u32x4_t a =
-                    *(const u32x4_t*)(sDS + arow * (C::BK * 2) + (((2 * ks + g) ^ (arow & 15)) << 4));
-                const u32x4_t bo =
-                    *(const u32x4_t*)(sKT + brow * (C::BK * 2) + (((2 * ks + g) ^ (brow & 15)) << 4));
-                acc = mfma_32x32x16(a, bo, acc);
+                const u32x2_t d1 = lds_tr16(sDST + trd[0] + ks * 16 * C::DST_ROWB);
+                const u32x2_t d2 = lds_tr16(sDST + trd[1] + ks * 16 * C::DST_ROWB);
+                const u32x2_t k1 = lds_tr16(sK + trk[0][tw] + ks * 16 * C::ROWB);
+                const u32x2_t k2 = lds_tr16(sK + trk[1][tw] + ks * 16 * C::ROWB);
+                da[ks] = (u32x4_t){d1[0], d1[1], d2[0], d2[1]};
+                ka[ks] = (u32x4_t){k1[0], k1[1], k2[0], k2[1]};
             }
-            // acc: column d = 32*nt + l32, rows 32*mt + 8*(r/4) + 4*g + r%4
-            float* dqh = p.dq + ((int64_t)b * p.S) * q_stride + h * DH + 32 * nt + l32;
+#pragma unroll
+            for (int ks = 0; ks < C::BK / 16; ++ks) acc = mfma_32x32x16(da[ks], ka[ks], acc);
+            // acc: column d = 32*nt + l32, rows 32*mt_q + 8*(r/4) + 4*g + r%4.  Rows
+            // past the shard are clamped onto the last row and add 0.
+            float* dqt = p.dq + (((int64_t)b * p.S + qt * C::BQ) * p.Hq + h) * DH + 32 * nt + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int iq = qt * C::BQ + 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
-                if (iq < p.S) unsafeAtomicAdd(dqh + iq * q_stride, acc[r] * p.scale);
+                const int row = 32 * mt_q + 8 * (r >> 2) + 4 * g + (r & 3);
+                const bool ok = row < rows_left;
+                unsafeAtomicAdd(dqt + (ok ? row : rows_left - 1) * qs, ok ? acc[r] * p.scale : 0.f);
             }
         }
     }
