@@ -181,7 +181,7 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     kern = {}
-    for name in ("fwd_step", "bwd_pre", "bwd_step", "lse_merge", "finalize"):
+    for name in ("fwd_step", "bwd_pre", "bwd_step", "bwd_post", "lse_merge", "finalize"):
         n, ms = ca.ring_attn_timing_read(name)
         if n:
             kern[name] = {"launches": n // args.steps, "ms_per_step": ms / args.steps,

@@ -193,8 +193,9 @@ int get_plan(const Geometry& g, const Plan** out) {
 // Optional per-kernel event timing
 // ---------------------------------------------------------------------------
 
-enum KernelClass { KC_FWD = 0, KC_MERGE, KC_FINALIZE, KC_BWD_PRE, KC_BWD, KC_COUNT };
-const char* kClassNames[KC_COUNT] = {"fwd_step", "lse_merge", "finalize", "bwd_pre", "bwd_step"};
+enum KernelClass { KC_FWD = 0, KC_MERGE, KC_FINALIZE, KC_BWD_PRE, KC_BWD, KC_BWD_POST, KC_COUNT };
+const char* kClassNames[KC_COUNT] = {"fwd_step", "lse_merge", "finalize", "bwd_pre", "bwd_step",
+                                     "bwd_post"};
 
 struct Timing {
     std::mutex mu;
@@ -265,9 +266,14 @@ int64_t fwd_workspace(const Geometry& g) {
     return 2 * o + round_up((int64_t)g.B * g.Hq * g.S * 4, 256);
 }
 
+// Backward workspace: Delta [B, Hq, S_pad] fp32, then the dQ accumulator
+// [B, Hq, S_pad, d] fp32.
+int64_t bwd_delta_bytes(const Geometry& g) {
+    return round_up((int64_t)g.B * g.Hq * round_up(g.S, FWD_BQ) * 4, 256);
+}
 int64_t bwd_workspace(const Geometry& g) {
     const int64_t S_pad = round_up(g.S, FWD_BQ);
-    return round_up((int64_t)g.B * g.Hq * S_pad * 4, 256);
+    return bwd_delta_bytes(g) + round_up((int64_t)g.B * g.Hq * S_pad * g.d * 4, 256);
 }
 
 int check_support(const Geometry& g, bool bwd) {
@@ -490,9 +496,10 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
         if ((rc = get_plan(g, &plan)) != RA_OK) return rc;
         hipStream_t s = (hipStream_t)stream;
         float* delta = (float*)workspace;
+        float* dq_acc = (float*)((unsigned char*)workspace + bwd_delta_bytes(g));
 
         BwdPreArgs pa{};
-        pa.dout = dout; pa.out = out; pa.delta = delta; pa.dq = dq;
+        pa.dout = dout; pa.out = out; pa.delta = delta; pa.dq_acc = dq_acc;
         pa.B = g.B; pa.S = (int32_t)g.S; pa.Hq = g.Hq; pa.S_pad = (int32_t)plan->S_pad; pa.d = g.d;
         rc = hip_rc(timed(KC_BWD_PRE, s, [&] { return launch_bwd_pre(pa, 1, s); }));
         if (rc != RA_OK) return rc;
@@ -500,7 +507,7 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
         const int64_t block_elems = (int64_t)g.B * g.Skv * g.Hkv * g.d;
         BwdArgs a{};
         a.q = (const uint16_t*)q; a.dout = (const uint16_t*)dout; a.lse = lse; a.delta = delta;
-        a.dq = dq;
+        a.dq = dq_acc;
         a.B = g.B; a.S = (int32_t)g.S; a.Skv = (int32_t)g.Skv; a.Hq = g.Hq; a.Hkv = g.Hkv;
         a.nkt = plan->nkt_b;
         a.S_pad = (int32_t)plan->S_pad;
@@ -517,7 +524,10 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
             rc = hip_rc(timed(KC_BWD, s, [&] { return launch_bwd_bf16(a, g.d, s); }));
             if (rc != RA_OK) return rc;
         }
-        return RA_OK;
+        rc = hip_rc(timed(KC_BWD_POST, s, [&] {
+            return launch_dq_finalize(dq_acc, dq, g.B, (int32_t)g.S, g.Hq, (int32_t)plan->S_pad, g.d, s);
+        }));
+        return rc;
     } catch (...) {
         return RA_E_HIP;
     }

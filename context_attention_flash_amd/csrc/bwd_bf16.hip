@@ -9,7 +9,7 @@
 //   S = Q K^T and dP = dO V^T        (C layout: lane = key, 16 query rows)
 //   P = exp(scale*S - lse), dS = P (dP - Delta)
 //   dV^T += dO^T P,  dK^T += Q^T dS  (fp32 accumulators in registers)
-//   dQ += scale * dS K               (fp32 atomics to HBM)
+//   dQ += scale * dS K               (fp32 atomics into a head-major accumulator)
 // Q, dO and K live in LDS in their natural row layout only.  The transposed
 // operands (dO^T, Q^T, and K as the B operand of dQ) come from the gfx950 LDS
 // transpose read ds_read_b64_tr_b16: within each 16-lane group, result lane i,
@@ -148,8 +148,9 @@ __global__ __launch_bounds__(256, 1) void bwd_step_bf16_kernel(BwdArgs p) {
     if (work >= p.total_work) return;
     const int t = work % p.nkt, bh = work / p.nkt;
     const int hk = bh % p.Hkv, b = bh / p.Hkv;
-    const int kt = p.t_order[t];
-    const int e0 = p.t_off[kt], e1 = p.t_off[kt + 1];
+    const cint_ptr ents = as_const(p.t_ent);
+    const int kt = as_const(p.t_order)[t];
+    const int e0 = as_const(p.t_off)[kt], e1 = as_const(p.t_off)[kt + 1];
     const int group = p.Hq / p.Hkv;
 
     const int kv_stride = p.Hkv * DH;
@@ -212,11 +213,40 @@ __global__ __launch_bounds__(256, 1) void bwd_step_bf16_kernel(BwdArgs p) {
     const int dst_w = row_off<8>(wave * 32 + l32, 0);  // dS^T row of this lane's key
     const int dst_x = slot<8>(wave * 32 + l32, 0);     // its chunk swizzle
 
+    // Registers -> LDS: the staged query tile (natural rows) and its row values.
+    auto store_tile = [&](const BwdTileRegs<DH>& T) {
+        if (tid < C::LDT) {
+            const int m = tid / C::KCH, ch = tid % C::KCH;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                *(u32x4_t*)(sQ + row_off<C::KCH>(4 * m + rr, ch)) = T.q[rr];
+                *(u32x4_t*)(sDO + row_off<C::KCH>(4 * m + rr, ch)) = T.o[rr];
+            }
+        }
+        if (tid < C::BQ) {
+            sL[tid] = T.l2;
+            sD[tid] = T.dl;
+            sA[tid] = T.a;
+            sB[tid] = T.b;
+        }
+    };
+
+    // Loop schedule (two barriers per query tile):
+    //   barrier A: tile `it` is in sQ/sDO; every wave is done with the previous dQ
+    //   issue global loads of tile it+1 into registers
+    //   S, dP, P, dS (-> dS^T in LDS), dV, dK
+    //   barrier B: every wave is done with sQ/sDO; dS^T is complete
+    //   store tile it+1 into sQ/sDO (its loads were issued before this
+    //   iteration's dQ atomics, so waiting for them does not wait for those)
+    //   dQ product and atomics
     BwdTileRegs<DH> R;
-    if (n_iter > 0) bwd_load_tile<DH>(R, p, b, hk * group, p.t_ent[e0] & 0x7fffffff, tid);
+    if (n_iter > 0) {
+        bwd_load_tile<DH>(R, p, b, hk * group, ents[e0] & 0x7fffffff, tid);
+        store_tile(R);
+    }
     for (int it = 0; it < n_iter; ++it) {
         const int h = hk * group + it / n_ent;
-        const int ent = p.t_ent[e0 + it % n_ent];
+        const int ent = ents[e0 + it % n_ent];
         const int qt = ent & 0x7fffffff;
         const bool partial = ent < 0;
         // Keep the dK/dV accumulators in AGPRs across iterations (the MFMAs
@@ -224,25 +254,11 @@ __global__ __launch_bounds__(256, 1) void bwd_step_bf16_kernel(BwdArgs p) {
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt) asm volatile("" : "+a"(dk_acc[dt]), "+a"(dv_acc[dt]));
 
-        __syncthreads();  // previous iteration's readers of the Q/dO/dS^T stages are done
-        if (tid < C::LDT) {
-            const int m = tid / C::KCH, ch = tid % C::KCH;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                *(u32x4_t*)(sQ + row_off<C::KCH>(4 * m + rr, ch)) = R.q[rr];
-                *(u32x4_t*)(sDO + row_off<C::KCH>(4 * m + rr, ch)) = R.o[rr];
-            }
-        }
-        if (tid < C::BQ) {
-            sL[tid] = R.l2;
-            sD[tid] = R.dl;
-            sA[tid] = R.a;
-            sB[tid] = R.b;
-        }
-        __syncthreads();
-        if (it + 1 < n_iter)
+        __syncthreads();  // barrier A
+        const bool has_next = it + 1 < n_iter;
+        if (has_next)
             bwd_load_tile<DH>(R, p, b, hk * group + (it + 1) / n_ent,
-                              p.t_ent[e0 + (it + 1) % n_ent] & 0x7fffffff, tid);
+                              ents[e0 + (it + 1) % n_ent] & 0x7fffffff, tid);
 
         // S = Q K^T and dP = dO V^T: two 32-row halves of the 64-row tile; the
         // B operands are this lane's K and V rows (key 32*wave + l32).
@@ -330,12 +346,13 @@ __global__ __launch_bounds__(256, 1) void bwd_step_bf16_kernel(BwdArgs p) {
                 dk_acc[dt] = mfma_32x32x16(qa[kk], db[kk], dk_acc[dt]);
             }
         }
-        __syncthreads();  // dS^T of every wave is in LDS
+        __syncthreads();  // barrier B
+        if (has_next) store_tile(R);
 
         // dQ[64 x DH] = dS[64 x 128] K[128 x DH]; wave tiles (mt_q, nt) of 32 x 32,
         // both operands from transpose reads (keys 16ks + 8g + 0..7 in order).
         const int rows_left = p.S - qt * C::BQ;  // >= 1
-        const int qs = p.Hq * DH;
+        constexpr int qs = DH;  // accumulator rows of one head are contiguous
 #pragma unroll
         for (int tw = 0; tw < PER_WAVE; ++tw) {
             const int nt = (wave * PER_WAVE + tw) % C::NDT;
@@ -354,7 +371,7 @@ __global__ __launch_bounds__(256, 1) void bwd_step_bf16_kernel(BwdArgs p) {
             for (int ks = 0; ks < C::BK / 16; ++ks) acc = mfma_32x32x16(da[ks], ka[ks], acc);
             // acc: column d = 32*nt + l32, rows 32*mt_q + 8*(r/4) + 4*g + r%4.  Rows
             // past the shard are clamped onto the last row and add 0.
-            float* dqt = p.dq + (((int64_t)b * p.S + qt * C::BQ) * p.Hq + h) * DH + 32 * nt + l32;
+            float* dqt = p.dq + (((int64_t)b * p.Hq + h) * p.S_pad + qt * C::BQ) * DH + 32 * nt + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = 32 * mt_q + 8 * (r >> 2) + 4 * g + (r & 3);

@@ -3,7 +3,11 @@
 //                     result (instagit/nanotron page, "Numerically-Stable
 //                     Output Fusion"), one pass over fp32 rows;
 //   K5 finalize    -- running fp32 output -> output dtype;
-//   K3 bwd_pre     -- Delta = rowsum(dout * out) for the backward, and dq = 0.
+//   K3 bwd_pre     -- Delta = rowsum(dout * out) for the backward, and a zeroed
+//                     dQ accumulator;
+//   dq_finalize    -- the dQ accumulator ([B, Hq, S_pad, d], head-major so that
+//                     the atomics of one head spread over the L2 channels) ->
+//                     the caller's dq [B, S, Hq, d].
 #include "kernel_args.h"
 #include "kernel_common.h"
 
@@ -115,7 +119,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs a) {
                 sum += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
             }
         }
-        f32x4_t* dq = (f32x4_t*)a.dq + 2 * gt;
+        const int64_t h = row % a.Hq, bs = row / a.Hq;
+        const int64_t b = bs / a.S, s = bs % a.S;
+        f32x4_t* dq = (f32x4_t*)(a.dq_acc + ((b * a.Hq + h) * a.S_pad + s) * a.d) + 2 * c;
         dq[0] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
         dq[1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     }
@@ -125,6 +131,29 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs a) {
         const int64_t b = bs / a.S, s = bs % a.S;
         a.delta[(b * a.Hq + h) * a.S_pad + s] = sum;
     }
+}
+
+// One thread per 4 floats of a (b, s, h) row of the caller's dq.
+__global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ acc,
+                                                          float* __restrict__ dq, int32_t S,
+                                                          int32_t Hq, int32_t S_pad, int32_t d,
+                                                          int64_t n4) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    const int c4 = d / 4;
+    const int64_t row = i / c4, c = i % c4;         // row = (b * S + s) * Hq + h
+    const int64_t h = row % Hq, bs = row / Hq;
+    const int64_t b = bs / S, s = bs % S;
+    ((f32x4_t*)dq)[i] = ((const f32x4_t*)(acc + ((b * Hq + h) * S_pad + s) * d))[c];
+}
+
+hipError_t launch_dq_finalize(const float* dq_acc, float* dq, int32_t B, int32_t S, int32_t Hq,
+                              int32_t S_pad, int32_t d, hipStream_t s) {
+    const int64_t n4 = (int64_t)B * S * Hq * (d / 4);
+    if (n4 == 0) return hipSuccess;
+    hipLaunchKernelGGL(dq_finalize_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s,
+                       dq_acc, dq, S, Hq, S_pad, d, n4);
+    return hipGetLastError();
 }
 
 hipError_t launch_bwd_pre(const BwdPreArgs& a, int is_bf16, hipStream_t s) {

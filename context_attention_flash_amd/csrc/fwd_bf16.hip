@@ -130,9 +130,10 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
     if (work >= p.total_work) return;
     const int t = work % p.nqt, bh = work / p.nqt;
     const int h = bh % p.Hq, b = bh / p.Hq;
-    const int qt = p.t_order[t];
+    const int qt = as_const(p.t_order)[t];
     const int hk = (h * p.Hkv) / p.Hq;
-    const int e0 = p.t_off[qt], e1 = p.t_off[qt + 1];
+    const cint_ptr ents = as_const(p.t_ent);
+    const int e0 = as_const(p.t_off)[qt], e1 = as_const(p.t_off)[qt + 1];
 
     const int iq = qt * C::BQ + wave * 32 + l32;  // this lane's query row
     const int iqc = min(iq, p.S - 1);
@@ -154,15 +155,15 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
 
     if (e0 < e1) {
         FwdTileRegs<DH> R;
-        fwd_load_tile<DH>(R, kb, vb, row_stride, p.t_ent[e0] & 0x7fffffff, p.Skv, tid);
+        fwd_load_tile<DH>(R, kb, vb, row_stride, ents[e0] & 0x7fffffff, p.Skv, tid);
         fwd_store_tile<DH>(R, smem, tid);
         for (int e = e0; e < e1; ++e) {
             unsigned char* stage = smem + ((e - e0) & 1) * C::STAGE;
             __syncthreads();
             const bool has_next = e + 1 < e1;
             if (has_next)
-                fwd_load_tile<DH>(R, kb, vb, row_stride, p.t_ent[e + 1] & 0x7fffffff, p.Skv, tid);
-            const int ent = p.t_ent[e];
+                fwd_load_tile<DH>(R, kb, vb, row_stride, ents[e + 1] & 0x7fffffff, p.Skv, tid);
+            const int ent = ents[e];
             const int kt = ent & 0x7fffffff;
             const unsigned char* Ks = stage;
             const unsigned char* Vt = stage + C::K_BYTES;

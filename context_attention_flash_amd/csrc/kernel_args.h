@@ -52,7 +52,7 @@ struct BwdArgs {
     const int32_t* t_off;   // [nkt + 1] query-tile lists per key tile
     const int32_t* t_ent;   // query tile index | (partial << 31)
     const int32_t* t_order; // [nkt] key tiles, heaviest first
-    float* dq;              // [B, S, Hq, d] fp32, accumulated with atomics
+    float* dq;              // [B, Hq, S_pad, d] fp32 accumulator (atomics)
     float* dk;              // block j: [B, Skv, Hkv, d] fp32, +=
     float* dv;
     int32_t B, S, Skv, Hq, Hkv, nkt, S_pad;
@@ -65,7 +65,7 @@ struct BwdPreArgs {
     const void* dout;       // [B, S, Hq, d] input dtype
     const void* out;
     float* delta;           // [B, Hq, S_pad]
-    float* dq;              // [B, S, Hq, d] zeroed here
+    float* dq_acc;          // [B, Hq, S_pad, d] zeroed here
     int32_t B, S, Hq, S_pad, d;
 };
 
@@ -77,5 +77,7 @@ hipError_t launch_lse_merge(float* out, float* lse, const float* out_j, const fl
 hipError_t launch_finalize(const float* o, void* out, int is_bf16, int64_t n, hipStream_t s);
 hipError_t launch_bwd_pre(const BwdPreArgs& a, int is_bf16, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_dq_finalize(const float* dq_acc, float* dq, int32_t B, int32_t S, int32_t Hq,
+                              int32_t S_pad, int32_t d, hipStream_t s);
 
 }  // namespace ra

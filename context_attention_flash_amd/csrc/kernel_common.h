@@ -49,6 +49,12 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// Plan arrays (tile lists, orders) are never written while a kernel runs; reading
+// them through the constant address space lets uniform indices use scalar
+// loads, which do not wait behind outstanding vector memory operations.
+typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+__device__ __forceinline__ cint_ptr as_const(const int32_t* p) { return (cint_ptr)(p); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Blocks of a launch are dealt to the 8 XCDs round-robin; this remaps the

@@ -124,7 +124,9 @@ typedef struct ring_attn_desc {
 
 /* Bytes of device workspace ring_attn_fwd (is_bwd = 0) or ring_attn_bwd
  * (is_bwd = 1) needs for this descriptor; negative RA_E_* if the descriptor is
- * invalid (cu_seqlens is not inspected). */
+ * invalid (cu_seqlens is not inspected).  Forward: the fp32 running output
+ * (plus one partial in RA_MERGE_SEPARATE mode).  Backward: Delta and an fp32
+ * dQ accumulator of B * Hq * S_pad * d floats (S_pad = S rounded up to 128). */
 int64_t ring_attn_workspace_bytes(const ring_attn_desc* desc, int is_bwd);
 
 /* Forward of the rank share ("Forward Pass Implementation"): for s = 0..D-1
@@ -187,7 +189,8 @@ int ring_attn_tile_kinds(const ring_attn_desc* desc, const int32_t* cu_seqlens,
 /* Per-kernel timing with HIP events recorded on the launching stream around
  * every kernel the library enqueues (off by default).  ring_attn_timing_read
  * synchronises on the recorded events and reports, for the kernel class
- * `name` ("fwd_step", "lse_merge", "finalize", "bwd_pre", "bwd_step"), the
+ * `name` ("fwd_step", "lse_merge", "finalize", "bwd_pre", "bwd_step",
+ * "bwd_post"), the
  * number of launches and their summed duration in milliseconds since the
  * last reset.  ring_attn_timing_enable(0) disables and resets. */
 int ring_attn_timing_enable(int enable);
