@@ -181,7 +181,7 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     kern = {}
-    for name in ("fwd_step", "bwd_pre", "bwd_step", "bwd_post", "lse_merge", "finalize"):
+    for name in ("fwd_step", "bwd_pre", "bwd_step", "bwd_dq", "bwd_post", "lse_merge", "finalize"):
         n, ms = ca.ring_attn_timing_read(name)
         if n:
             kern[name] = {"launches": n // args.steps, "ms_per_step": ms / args.steps,
@@ -195,8 +195,10 @@ def main():
     value = total_flops / (ms_step * 1e-3) / 1e12
     if "fwd_step" in kern:
         kern["fwd_step"]["TFLOP/s"] = fwd_flops / (kern["fwd_step"]["ms_per_step"] * 1e-3) / 1e12
-    if "bwd_step" in kern:
-        kern["bwd_step"]["TFLOP/s"] = bwd_flops / (kern["bwd_step"]["ms_per_step"] * 1e-3) / 1e12
+    if "bwd_step" in kern:  # dK/dV kernel: S, dP, dV, dK = 8d flops per visible pair
+        kern["bwd_step"]["TFLOP/s"] = 0.8 * bwd_flops / (kern["bwd_step"]["ms_per_step"] * 1e-3) / 1e12
+    if "bwd_dq" in kern:    # dQ kernel: S, dP recomputed, dQ = 6d flops per visible pair
+        kern["bwd_dq"]["TFLOP/s"] = 0.6 * bwd_flops / (kern["bwd_dq"]["ms_per_step"] * 1e-3) / 1e12
 
     dom = "bwd_step" if w.with_grad else "fwd_step"
     dom_flops = bwd_flops if w.with_grad else fwd_flops

@@ -193,9 +193,11 @@ int get_plan(const Geometry& g, const Plan** out) {
 // Optional per-kernel event timing
 // ---------------------------------------------------------------------------
 
-enum KernelClass { KC_FWD = 0, KC_MERGE, KC_FINALIZE, KC_BWD_PRE, KC_BWD, KC_BWD_POST, KC_COUNT };
-const char* kClassNames[KC_COUNT] = {"fwd_step", "lse_merge", "finalize", "bwd_pre", "bwd_step",
-                                     "bwd_post"};
+enum KernelClass {
+    KC_FWD = 0, KC_MERGE, KC_FINALIZE, KC_BWD_PRE, KC_BWD, KC_BWD_DQ, KC_BWD_POST, KC_COUNT
+};
+const char* kClassNames[KC_COUNT] = {"fwd_step", "lse_merge", "finalize", "bwd_pre",
+                                     "bwd_step",  "bwd_dq",    "bwd_post"};
 
 struct Timing {
     std::mutex mu;
@@ -499,7 +501,7 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
         float* dq_acc = (float*)((unsigned char*)workspace + bwd_delta_bytes(g));
 
         BwdPreArgs pa{};
-        pa.dout = dout; pa.out = out; pa.delta = delta; pa.dq_acc = dq_acc;
+        pa.dout = dout; pa.out = out; pa.delta = delta;
         pa.B = g.B; pa.S = (int32_t)g.S; pa.Hq = g.Hq; pa.S_pad = (int32_t)plan->S_pad; pa.d = g.d;
         rc = hip_rc(timed(KC_BWD_PRE, s, [&] { return launch_bwd_pre(pa, 1, s); }));
         if (rc != RA_OK) return rc;
@@ -507,22 +509,42 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
         const int64_t block_elems = (int64_t)g.B * g.Skv * g.Hkv * g.d;
         BwdArgs a{};
         a.q = (const uint16_t*)q; a.dout = (const uint16_t*)dout; a.lse = lse; a.delta = delta;
-        a.dq = dq_acc;
         a.B = g.B; a.S = (int32_t)g.S; a.Skv = (int32_t)g.Skv; a.Hq = g.Hq; a.Hkv = g.Hkv;
         a.nkt = plan->nkt_b;
         a.S_pad = (int32_t)plan->S_pad;
         a.total_work = g.B * g.Hkv * plan->nkt_b;
         a.scale = g.scale;
         a.scale_log2 = g.scale * 1.4426950408889634f;
+        DqArgs qa{};
+        qa.q = (const uint16_t*)q; qa.dout = (const uint16_t*)dout; qa.lse = lse;
+        qa.delta = delta; qa.dq_acc = dq_acc;
+        qa.B = g.B; qa.S = (int32_t)g.S; qa.Skv = (int32_t)g.Skv; qa.Hq = g.Hq; qa.Hkv = g.Hkv;
+        qa.nqt = plan->nqt;
+        qa.S_pad = (int32_t)plan->S_pad;
+        qa.total_work = g.B * g.Hq * plan->nqt;
+        qa.scale = g.scale;
+        qa.scale_log2 = a.scale_log2;
+        bool first = true;
         for (const DevStep& st : plan->steps) {
-            if (st.pairs == 0) continue;
             a.k = (const uint16_t*)k + st.j * block_elems;
             a.v = (const uint16_t*)v + st.j * block_elems;
             a.dk = dk + st.j * block_elems;
             a.dv = dv + st.j * block_elems;
             a.rng = st.rng; a.t_off = st.b_off; a.t_ent = st.b_ent; a.t_order = st.b_order;
-            rc = hip_rc(timed(KC_BWD, s, [&] { return launch_bwd_bf16(a, g.d, s); }));
-            if (rc != RA_OK) return rc;
+            if (st.pairs > 0) {
+                rc = hip_rc(timed(KC_BWD, s, [&] { return launch_bwd_dkdv_bf16(a, g.d, s); }));
+                if (rc != RA_OK) return rc;
+            }
+            // the dQ kernel writes the accumulator on the first step (also when a
+            // step has no visible pair, in which case it writes zeros)
+            qa.k = a.k; qa.v = a.v;
+            qa.rng = st.rng; qa.t_off = st.f_off; qa.t_ent = st.f_ent; qa.t_order = st.f_order;
+            qa.first = first ? 1 : 0;
+            if (st.pairs > 0 || first) {
+                rc = hip_rc(timed(KC_BWD_DQ, s, [&] { return launch_bwd_dq_bf16(qa, g.d, s); }));
+                if (rc != RA_OK) return rc;
+                first = false;
+            }
         }
         rc = hip_rc(timed(KC_BWD_POST, s, [&] {
             return launch_dq_finalize(dq_acc, dq, g.B, (int32_t)g.S, g.Hq, (int32_t)plan->S_pad, g.d, s);

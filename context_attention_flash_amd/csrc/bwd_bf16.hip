@@ -1,26 +1,29 @@
 // K4: one ring step of the attention backward, bf16 operands, fp32
 // accumulation (instagit/nanotron page, "Backward Pass and Gradient
 // Accumulation": per step, the flash backward of (dout, q, k_j, v_j, out, lse)
-// adds into dq, dk_j and dv_j).
+// adds into dq, dk_j and dv_j).  Two kernels share the step:
 //
-// One work-group = one (batch, kv head, 128-key tile of block j); wave w owns
-// keys 32w..32w+31.  It walks every query tile (64 rows) of every query head
-// of the GQA group that sees its keys, and per tile computes
+// K4a bwd_dkdv: one work-group = one (batch, kv head, 128-key tile of block
+// j); wave w owns keys 32w..32w+31.  It walks every 64-row query tile of every
+// query head of the GQA group that sees its keys and computes
 //   S = Q K^T and dP = dO V^T        (C layout: lane = key, 16 query rows)
 //   P = exp(scale*S - lse), dS = P (dP - Delta)
-//   dV^T += dO^T P,  dK^T += Q^T dS  (fp32 accumulators in registers)
-//   dQ += scale * dS K               (fp32 atomics into a head-major accumulator)
-// Q, dO and K live in LDS in their natural row layout only.  The transposed
-// operands (dO^T, Q^T, and K as the B operand of dQ) come from the gfx950 LDS
-// transpose read ds_read_b64_tr_b16: within each 16-lane group, result lane i,
-// element k is the 16-bit value at (address of lane 4k + i/4) + 2*(i%4), so a
-// group turns a 4-row x 16-column K-major block into MFMA operand layout.  P
-// and dS feed the MFMAs straight from the accumulator registers, whose query
+//   dV^T += dO^T P,  dK^T += Q^T dS  (fp32 accumulators in AGPRs)
+// Q, dO, K and V live in LDS in natural rows; dO^T and Q^T come from the gfx950
+// transpose read ds_read_b64_tr_b16 (within each 16-lane group, result lane i,
+// element k is the 16-bit value at (address of lane 4k + i/4) + 2*(i%4)).
+// P and dS feed the MFMAs straight from the accumulator registers, whose query
 // order inside each 16-row group is {0-3, 8-11 | 4-7, 12-15} (lanes 0-31 |
-// 32-63); the transpose reads pick their rows in that same order.  dS goes to
-// LDS as dS^T [key][query] with 8-byte writes for the dQ product.  dK/dV are
-// added to the caller's buffers once at the end: every key tile of a block has
-// one owner per launch.
+// 32-63); the transpose reads pick their rows in that same order.  dK/dV are
+// added to the caller's buffers once at the end (one owner per key tile).
+//
+// K4b bwd_dq: one work-group = one (batch, q head, 128-row query tile), as in
+// the forward: lane = query column, Q and dO in registers, 64-key tiles of K
+// and V streamed through LDS.  It recomputes S^T = K Q^T and dP^T = V dO^T and
+// accumulates dQ^T += K^T dS^T (K^T from transpose reads).  Each (head, query
+// tile) has one owner per launch, so dQ needs no atomics: fp32 atomics on the
+// L2 run about ten times slower than plain stores, and the dQ of a key-tile
+// decomposition would be bound by them.
 #include "kernel_args.h"
 #include "kernel_common.h"
 
@@ -36,14 +39,11 @@ struct BwdCfg {
     static constexpr int KCH = DH / 8;              // 16-byte chunks per natural row
     static constexpr int Q_BYTES = BQ * ROWB;
     static constexpr int K_BYTES = BK * ROWB;
-    static constexpr int DST_ROWB = BQ * 2;         // dS^T row: 64 queries
-    static constexpr int DST_BYTES = BK * DST_ROWB;
     static constexpr int OFF_Q = 0;
     static constexpr int OFF_DO = OFF_Q + Q_BYTES;
     static constexpr int OFF_K = OFF_DO + Q_BYTES;
     static constexpr int OFF_V = OFF_K + K_BYTES;
-    static constexpr int OFF_DST = OFF_V + K_BYTES;
-    static constexpr int OFF_ROW = OFF_DST + DST_BYTES;  // lse2, delta, a, b per query row
+    static constexpr int OFF_ROW = OFF_V + K_BYTES;   // lse2, delta, a, b per query row
     static constexpr int LDS = OFF_ROW + 4 * BQ * 4;
     static constexpr int LDT = BQ * KCH / 4;        // threads taking part in a Q/dO load
     static_assert(LDT == NT || LDT == NT / 2, "tile shape");
@@ -129,14 +129,13 @@ __device__ __forceinline__ void bwd_load_tile(BwdTileRegs<DH>& R, const BwdArgs&
 }
 
 template <int DH>
-__global__ __launch_bounds__(256, 1) void bwd_step_bf16_kernel(BwdArgs p) {
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs p) {
     using C = BwdCfg<DH>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
     unsigned char* sQ = smem + C::OFF_Q;
     unsigned char* sDO = smem + C::OFF_DO;
     unsigned char* sK = smem + C::OFF_K;
     unsigned char* sV = smem + C::OFF_V;
-    unsigned char* sDST = smem + C::OFF_DST;
     float* sL = (float*)(smem + C::OFF_ROW);
     float* sD = sL + C::BQ;
     int32_t* sA = (int32_t*)(sD + C::BQ);
@@ -179,13 +178,8 @@ __global__ __launch_bounds__(256, 1) void bwd_step_bf16_kernel(BwdArgs p) {
 
     // Per-lane LDS offsets.  Every swizzle below depends only on the low four
     // bits of the row, so moving by 16 or 32 rows is a constant offset.
-    //   nat[ks]    : natural read of row l32, chunk 2ks+g (S and dP A operands)
+    //   nat[ks]    : natural read of row l32, chunk 2ks+g (S and dP operands)
     //   trq[r][dt] : transpose read of rows {4g, 8+4g} + j/4, head-dim block dt
-    //   trd[r]     : transpose read of dS^T rows {8g, 8g+4} + j/4, query block mt_q
-    //   trk[r][tw] : transpose read of K rows {8g, 8g+4} + j/4, head-dim block nt
-    constexpr int TILES = 2 * C::NDT;
-    constexpr int PER_WAVE = TILES / 4;
-    const int mt_q = (wave * PER_WAVE) / C::NDT;
     const int j = lane & 15, gsel = (lane >> 4) & 1;
     int nat[C::NKS];
 #pragma unroll
@@ -198,20 +192,6 @@ __global__ __launch_bounds__(256, 1) void bwd_step_bf16_kernel(BwdArgs p) {
             const int col = 32 * dt + 16 * gsel + 4 * (j & 3);
             trq[r][dt] = row_off<C::KCH>(8 * r + 4 * g + (j >> 2), col >> 3) + (col & 7) * 2;
         }
-    int trd[2], trk[2][PER_WAVE];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int colq = 32 * mt_q + 16 * gsel + 4 * (j & 3);
-        trd[r] = row_off<8>(8 * g + 4 * r + (j >> 2), colq >> 3) + (colq & 7) * 2;
-#pragma unroll
-        for (int tw = 0; tw < PER_WAVE; ++tw) {
-            const int nt = (wave * PER_WAVE + tw) % C::NDT;
-            const int cold = 32 * nt + 16 * gsel + 4 * (j & 3);
-            trk[r][tw] = row_off<C::KCH>(8 * g + 4 * r + (j >> 2), cold >> 3) + (cold & 7) * 2;
-        }
-    }
-    const int dst_w = row_off<8>(wave * 32 + l32, 0);  // dS^T row of this lane's key
-    const int dst_x = slot<8>(wave * 32 + l32, 0);     // its chunk swizzle
 
     // Registers -> LDS: the staged query tile (natural rows) and its row values.
     auto store_tile = [&](const BwdTileRegs<DH>& T) {
@@ -232,13 +212,11 @@ __global__ __launch_bounds__(256, 1) void bwd_step_bf16_kernel(BwdArgs p) {
     };
 
     // Loop schedule (two barriers per query tile):
-    //   barrier A: tile `it` is in sQ/sDO; every wave is done with the previous dQ
+    //   barrier A: tile `it` is in sQ/sDO
     //   issue global loads of tile it+1 into registers
-    //   S, dP, P, dS (-> dS^T in LDS), dV, dK
-    //   barrier B: every wave is done with sQ/sDO; dS^T is complete
-    //   store tile it+1 into sQ/sDO (its loads were issued before this
-    //   iteration's dQ atomics, so waiting for them does not wait for those)
-    //   dQ product and atomics
+    //   S, dP, P, dS, dV, dK
+    //   barrier B: every wave is done with sQ/sDO
+    //   store tile it+1 into sQ/sDO
     BwdTileRegs<DH> R;
     if (n_iter > 0) {
         bwd_load_tile<DH>(R, p, b, hk * group, ents[e0] & 0x7fffffff, tid);
@@ -322,10 +300,6 @@ __global__ __launch_bounds__(256, 1) void bwd_step_bf16_kernel(BwdArgs p) {
                 pb[kk][w + 1] = pack_bf16x2(sacc[mt][4 * rg + 2], sacc[mt][4 * rg + 3]);
                 db[kk][w] = pack_bf16x2(pacc[mt][4 * rg], pacc[mt][4 * rg + 1]);
                 db[kk][w + 1] = pack_bf16x2(pacc[mt][4 * rg + 2], pacc[mt][4 * rg + 3]);
-                // dS^T [key][query]: this lane's key row, queries r0..r0+3
-                // (chunk r0/8 = 4mt + rg, half g)
-                *(u32x2_t*)(sDST + dst_w - (dst_x << 4) + (((4 * mt + rg) ^ dst_x) << 4) + 8 * g) =
-                    (u32x2_t){db[kk][w], db[kk][w + 1]};
             }
         // dV^T += dO^T P and dK^T += Q^T dS; the K dimension (queries) of step
         // kk takes rows 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3.
@@ -348,37 +322,6 @@ __global__ __launch_bounds__(256, 1) void bwd_step_bf16_kernel(BwdArgs p) {
         }
         __syncthreads();  // barrier B
         if (has_next) store_tile(R);
-
-        // dQ[64 x DH] = dS[64 x 128] K[128 x DH]; wave tiles (mt_q, nt) of 32 x 32,
-        // both operands from transpose reads (keys 16ks + 8g + 0..7 in order).
-        const int rows_left = p.S - qt * C::BQ;  // >= 1
-        constexpr int qs = DH;  // accumulator rows of one head are contiguous
-#pragma unroll
-        for (int tw = 0; tw < PER_WAVE; ++tw) {
-            const int nt = (wave * PER_WAVE + tw) % C::NDT;
-            f32x16_t acc = (f32x16_t){};
-            u32x4_t da[C::BK / 16], ka[C::BK / 16];
-#pragma unroll
-            for (int ks = 0; ks < C::BK / 16; ++ks) {
-                const u32x2_t d1 = lds_tr16(sDST + trd[0] + ks * 16 * C::DST_ROWB);
-                const u32x2_t d2 = lds_tr16(sDST + trd[1] + ks * 16 * C::DST_ROWB);
-                const u32x2_t k1 = lds_tr16(sK + trk[0][tw] + ks * 16 * C::ROWB);
-                const u32x2_t k2 = lds_tr16(sK + trk[1][tw] + ks * 16 * C::ROWB);
-                da[ks] = (u32x4_t){d1[0], d1[1], d2[0], d2[1]};
-                ka[ks] = (u32x4_t){k1[0], k1[1], k2[0], k2[1]};
-            }
-#pragma unroll
-            for (int ks = 0; ks < C::BK / 16; ++ks) acc = mfma_32x32x16(da[ks], ka[ks], acc);
-            // acc: column d = 32*nt + l32, rows 32*mt_q + 8*(r/4) + 4*g + r%4.  Rows
-            // past the shard are clamped onto the last row and add 0.
-            float* dqt = p.dq + (((int64_t)b * p.Hq + h) * p.S_pad + qt * C::BQ) * DH + 32 * nt + l32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 32 * mt_q + 8 * (r >> 2) + 4 * g + (r & 3);
-                const bool ok = row < rows_left;
-                unsafeAtomicAdd(dqt + (ok ? row : rows_left - 1) * qs, ok ? acc[r] * p.scale : 0.f);
-            }
-        }
     }
 
     // dK_j += scale * dK^T acc, dV_j += dV^T acc (this lane's key, 64 head-dim values)
@@ -403,13 +346,214 @@ __global__ __launch_bounds__(256, 1) void bwd_step_bf16_kernel(BwdArgs p) {
     }
 }
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, hipStream_t s) {
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int head_dim, hipStream_t s) {
     const int grid = (a.total_work + 7) / 8 * 8;
     if (grid == 0) return hipSuccess;
     if (head_dim == 128)
-        hipLaunchKernelGGL(bwd_step_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a);
     else if (head_dim == 64)
-        hipLaunchKernelGGL(bwd_step_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// K4b: dQ of one ring step (query-stationary, no atomics)
+// ---------------------------------------------------------------------------
+
+template <int DH>
+struct DqCfg {
+    static constexpr int NT = 256;
+    static constexpr int BQ = FWD_BQ, BK = FWD_BK;   // 4 waves x 32 queries, 64 keys
+    static constexpr int NKS = DH / 16;
+    static constexpr int NDT = DH / 32;
+    static constexpr int ROWB = DH * 2;
+    static constexpr int KCH = DH / 8;
+    static constexpr int K_BYTES = BK * ROWB;
+    static constexpr int STAGE = 2 * K_BYTES;        // K and V tiles, natural rows
+    static constexpr int LDS = 2 * STAGE;
+    static constexpr int KLD = BK * KCH / NT;        // 16-byte chunks per thread per tensor
+    static_assert(KLD >= 1, "tile shape");
+};
+
+template <int DH>
+struct DqTileRegs {
+    u32x4_t k[DqCfg<DH>::KLD], v[DqCfg<DH>::KLD];
+};
+
+template <int DH>
+__device__ __forceinline__ void dq_load_tile(DqTileRegs<DH>& R, const uint16_t* kb,
+                                             const uint16_t* vb, int kv_stride, int kt, int Skv,
+                                             int tid) {
+    using C = DqCfg<DH>;
+#pragma unroll
+    for (int c = 0; c < C::KLD; ++c) {
+        const int idx = tid + C::NT * c;
+        const int row = idx / C::KCH, ch = idx % C::KCH;
+        const int64_t key = min(kt * C::BK + row, Skv - 1);
+        R.k[c] = *(const u32x4_t*)(kb + key * kv_stride + ch * 8);
+        R.v[c] = *(const u32x4_t*)(vb + key * kv_stride + ch * 8);
+    }
+}
+
+template <int DH>
+__device__ __forceinline__ void dq_store_tile(const DqTileRegs<DH>& R, unsigned char* stage,
+                                              int tid) {
+    using C = DqCfg<DH>;
+#pragma unroll
+    for (int c = 0; c < C::KLD; ++c) {
+        const int idx = tid + C::NT * c;
+        const int row = idx / C::KCH, ch = idx % C::KCH;
+        *(u32x4_t*)(stage + row_off<C::KCH>(row, ch)) = R.k[c];
+        *(u32x4_t*)(stage + C::K_BYTES + row_off<C::KCH>(row, ch)) = R.v[c];
+    }
+}
+
+template <int DH>
+__global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(DqArgs p) {
+    using C = DqCfg<DH>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+    const int work = xcd_work_index(blockIdx.x, gridDim.x);
+    if (work >= p.total_work) return;
+    const int t = work % p.nqt, bh = work / p.nqt;
+    const int h = bh % p.Hq, b = bh / p.Hq;
+    const int qt = as_const(p.t_order)[t];
+    const int hk = (h * p.Hkv) / p.Hq;
+    const cint_ptr ents = as_const(p.t_ent);
+    const int e0 = as_const(p.t_off)[qt], e1 = as_const(p.t_off)[qt + 1];
+
+    const int iq = qt * C::BQ + wave * 32 + l32;  // this lane's query row
+    const int iqc = min(iq, p.S - 1);
+    const bool valid = iq < p.S;
+    const int q_stride = p.Hq * DH;
+    const uint16_t* qrow = p.q + ((int64_t)b * p.S + iqc) * q_stride + h * DH;
+    const uint16_t* orow = p.dout + ((int64_t)b * p.S + iqc) * q_stride + h * DH;
+    u32x4_t qreg[C::NKS], oreg[C::NKS];
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+        qreg[ks] = *(const u32x4_t*)(qrow + 16 * ks + 8 * g);
+        oreg[ks] = *(const u32x4_t*)(orow + 16 * ks + 8 * g);
+    }
+    const float Lraw = p.lse[((int64_t)b * p.Hq + h) * p.S + iqc];
+    const float L2 = (!valid || Lraw == -INFINITY) ? INFINITY : Lraw * kLog2e;
+    const float Dl = valid ? p.delta[((int64_t)b * p.Hq + h) * p.S_pad + iqc] : 0.f;
+    const int ra = p.rng[2 * iq], rb = p.rng[2 * iq + 1];
+
+    const int kv_stride = p.Hkv * DH;
+    const uint16_t* kb = p.k + (int64_t)b * p.Skv * kv_stride + hk * DH;
+    const uint16_t* vb = p.v + (int64_t)b * p.Skv * kv_stride + hk * DH;
+
+    // per-lane LDS offsets (see the dK/dV kernel)
+    const int j = lane & 15, gsel = (lane >> 4) & 1;
+    int nat[C::NKS];
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) nat[ks] = row_off<C::KCH>(l32, 2 * ks + g);
+    int trk[2][C::NDT];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) {
+            const int col = 32 * dt + 16 * gsel + 4 * (j & 3);
+            trk[r][dt] = row_off<C::KCH>(8 * r + 4 * g + (j >> 2), col >> 3) + (col & 7) * 2;
+        }
+
+    f32x16_t acc[C::NDT];
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) acc[dt] = (f32x16_t){};
+    const float c2 = p.scale_log2;
+
+    if (e0 < e1) {
+        DqTileRegs<DH> R;
+        dq_load_tile<DH>(R, kb, vb, kv_stride, ents[e0] & 0x7fffffff, p.Skv, tid);
+        dq_store_tile<DH>(R, smem, tid);
+        for (int e = e0; e < e1; ++e) {
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) asm volatile("" : "+a"(acc[dt]));
+            unsigned char* stage = smem + ((e - e0) & 1) * C::STAGE;
+            __syncthreads();
+            const bool has_next = e + 1 < e1;
+            if (has_next) dq_load_tile<DH>(R, kb, vb, kv_stride, ents[e + 1] & 0x7fffffff, p.Skv, tid);
+            const int ent = ents[e];
+            const int kt = ent & 0x7fffffff;
+            const unsigned char* Ks = stage;
+            const unsigned char* Vs = stage + C::K_BYTES;
+
+            // S^T = K Q^T and dP^T = V dO^T for the 64 keys (two 32-key halves)
+            f32x16_t sacc[2], pacc[2];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                sacc[mt] = (f32x16_t){};
+                pacc[mt] = (f32x16_t){};
+            }
+#pragma unroll
+            for (int ks = 0; ks < C::NKS; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    const u32x4_t ka = *(const u32x4_t*)(Ks + nat[ks] + mt * 32 * C::ROWB);
+                    const u32x4_t va = *(const u32x4_t*)(Vs + nat[ks] + mt * 32 * C::ROWB);
+                    sacc[mt] = mfma_32x32x16(ka, qreg[ks], sacc[mt]);
+                    pacc[mt] = mfma_32x32x16(va, oreg[ks], pacc[mt]);
+                }
+            // P = exp(scale*S - lse) and dS = P (dP - Delta); element (mt, r) is key
+            // 32*mt + 8*(r/4) + 4*g + r%4 of the tile.
+            u32x4_t db[4];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    float pv[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        float pr = fast_exp2(fmaf(sacc[mt][r + u], c2, -L2));
+                        if (ent < 0) {
+                            const int key = kt * C::BK + 32 * mt + 8 * ((r + u) >> 2) + 4 * g + ((r + u) & 3);
+                            pr = ((key >= ra) & (key < rb)) ? pr : 0.f;
+                        }
+                        pv[u] = pr * (pacc[mt][r + u] - Dl);
+                    }
+                    db[2 * mt + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(pv[0], pv[1]);
+                }
+            // dQ^T += K^T dS^T; the K dimension (keys) of step kk takes rows
+            // 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3, as dS is held.
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const u32x2_t a1 = lds_tr16(Ks + trk[0][dt] + kk * 16 * C::ROWB);
+                    const u32x2_t a2 = lds_tr16(Ks + trk[1][dt] + kk * 16 * C::ROWB);
+                    acc[dt] = mfma_32x32x16((u32x4_t){a1[0], a1[1], a2[0], a2[1]}, db[kk], acc[dt]);
+                }
+            if (has_next) dq_store_tile<DH>(R, smem + (((e - e0) & 1) ^ 1) * C::STAGE, tid);
+        }
+    }
+
+    // dq_acc (+)= scale * acc in the accumulator layout: element (dt, r) of this
+    // lane is head-dim index 32*dt + 8*(r/4) + 4*g + r%4 of query row iq.
+    f32x4_t* dst = (f32x4_t*)p.dq_acc +
+                   (((int64_t)b * p.Hq + h) * (p.S_pad / 32) + (qt * 4 + wave)) * (8 * DH) + lane;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            f32x4_t o = {acc[dt][4 * rg] * p.scale, acc[dt][4 * rg + 1] * p.scale,
+                         acc[dt][4 * rg + 2] * p.scale, acc[dt][4 * rg + 3] * p.scale};
+            f32x4_t* ptr = dst + (dt * 4 + rg) * 64;
+            if (!p.first) o += *ptr;
+            *ptr = o;
+        }
+}
+
+hipError_t launch_bwd_dq_bf16(const DqArgs& a, int head_dim, hipStream_t s) {
+    const int grid = (a.total_work + 7) / 8 * 8;
+    if (grid == 0) return hipSuccess;
+    if (head_dim == 128)
+        hipLaunchKernelGGL(bwd_dq_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a);
+    else if (head_dim == 64)
+        hipLaunchKernelGGL(bwd_dq_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

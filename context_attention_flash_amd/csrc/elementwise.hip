@@ -3,11 +3,11 @@
 //                     result (instagit/nanotron page, "Numerically-Stable
 //                     Output Fusion"), one pass over fp32 rows;
 //   K5 finalize    -- running fp32 output -> output dtype;
-//   K3 bwd_pre     -- Delta = rowsum(dout * out) for the backward, and a zeroed
-//                     dQ accumulator;
-//   dq_finalize    -- the dQ accumulator ([B, Hq, S_pad, d], head-major so that
-//                     the atomics of one head spread over the L2 channels) ->
-//                     the caller's dq [B, S, Hq, d].
+//   K3 bwd_pre     -- Delta = rowsum(dout * out) for the backward;
+//   dq_finalize    -- the dQ accumulator (kept in the MFMA accumulator layout of
+//                     the dQ kernel: per 32-row group of one head,
+//                     [d/32][4][64 lanes][4] floats) -> the caller's dq
+//                     [B, S, Hq, d].
 #include "kernel_args.h"
 #include "kernel_common.h"
 
@@ -119,11 +119,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs a) {
                 sum += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
             }
         }
-        const int64_t h = row % a.Hq, bs = row / a.Hq;
-        const int64_t b = bs / a.S, s = bs % a.S;
-        f32x4_t* dq = (f32x4_t*)(a.dq_acc + ((b * a.Hq + h) * a.S_pad + s) * a.d) + 2 * c;
-        dq[0] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-        dq[1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     }
     for (int off = lanes_per_row / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
     if (row < rows && c == 0) {
@@ -133,7 +128,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs a) {
     }
 }
 
-// One thread per 4 floats of a (b, s, h) row of the caller's dq.
+// One thread per 4 floats of a (b, s, h) row of the caller's dq.  Head-dim
+// index dd = 4c lives in accumulator lane (s % 32) + 32 * ((dd / 4) % 2), slot
+// (dd / 32) * 4 + (dd / 8) % 4 of the row group s / 32.
 __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restrict__ acc,
                                                           float* __restrict__ dq, int32_t S,
                                                           int32_t Hq, int32_t S_pad, int32_t d,
@@ -141,10 +138,14 @@ __global__ __launch_bounds__(256) void dq_finalize_kernel(const float* __restric
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n4) return;
     const int c4 = d / 4;
-    const int64_t row = i / c4, c = i % c4;         // row = (b * S + s) * Hq + h
+    const int64_t row = i / c4;                 // row = (b * S + s) * Hq + h
+    const int dd = (int)(i % c4) * 4;
     const int64_t h = row % Hq, bs = row / Hq;
     const int64_t b = bs / S, s = bs % S;
-    ((f32x4_t*)dq)[i] = ((const f32x4_t*)(acc + ((b * Hq + h) * S_pad + s) * d))[c];
+    const int64_t grp = (b * Hq + h) * (S_pad / 32) + s / 32;
+    const int lane = (int)(s % 32) + 32 * ((dd >> 2) & 1);
+    const int slotidx = (dd >> 5) * 4 + ((dd >> 3) & 3);
+    ((f32x4_t*)dq)[i] = ((const f32x4_t*)acc)[grp * (8 * d) + slotidx * 64 + lane];
 }
 
 hipError_t launch_dq_finalize(const float* dq_acc, float* dq, int32_t B, int32_t S, int32_t Hq,

@@ -52,7 +52,6 @@ struct BwdArgs {
     const int32_t* t_off;   // [nkt + 1] query-tile lists per key tile
     const int32_t* t_ent;   // query tile index | (partial << 31)
     const int32_t* t_order; // [nkt] key tiles, heaviest first
-    float* dq;              // [B, Hq, S_pad, d] fp32 accumulator (atomics)
     float* dk;              // block j: [B, Skv, Hkv, d] fp32, +=
     float* dv;
     int32_t B, S, Skv, Hq, Hkv, nkt, S_pad;
@@ -61,11 +60,30 @@ struct BwdArgs {
     float scale_log2;       // softmax scale * log2(e)
 };
 
+// K4b: dQ of one ring step.  Uses the forward's per-query-tile lists.
+struct DqArgs {
+    const uint16_t* q;      // [B, S, Hq, d] bf16
+    const uint16_t* k;      // block j: [B, Skv, Hkv, d]
+    const uint16_t* v;
+    const uint16_t* dout;   // [B, S, Hq, d]
+    const float* lse;       // [B, Hq, S]
+    const float* delta;     // [B, Hq, S_pad]
+    const int32_t* rng;     // [S_pad][2]
+    const int32_t* t_off;   // [nqt + 1] key-tile lists per query tile
+    const int32_t* t_ent;   // key tile index | (partial << 31)
+    const int32_t* t_order; // [nqt] query tiles, heaviest first
+    float* dq_acc;          // fp32 accumulator in the forward's running-output layout
+    int32_t B, S, Skv, Hq, Hkv, nqt, S_pad;
+    int32_t total_work;     // B * Hq * nqt
+    int32_t first;          // first active step: write instead of add
+    float scale;
+    float scale_log2;
+};
+
 struct BwdPreArgs {
     const void* dout;       // [B, S, Hq, d] input dtype
     const void* out;
     float* delta;           // [B, Hq, S_pad]
-    float* dq_acc;          // [B, Hq, S_pad, d] zeroed here
     int32_t B, S, Hq, S_pad, d;
 };
 
@@ -76,7 +94,8 @@ hipError_t launch_lse_merge(float* out, float* lse, const float* out_j, const fl
                             int32_t B, int64_t S, int32_t H, int32_t d, hipStream_t s);
 hipError_t launch_finalize(const float* o, void* out, int is_bf16, int64_t n, hipStream_t s);
 hipError_t launch_bwd_pre(const BwdPreArgs& a, int is_bf16, hipStream_t s);
-hipError_t launch_bwd_bf16(const BwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_bwd_dq_bf16(const DqArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_dq_finalize(const float* dq_acc, float* dq, int32_t B, int32_t S, int32_t Hq,
                               int32_t S_pad, int32_t d, hipStream_t s);
 

@@ -189,8 +189,8 @@ int ring_attn_tile_kinds(const ring_attn_desc* desc, const int32_t* cu_seqlens,
 /* Per-kernel timing with HIP events recorded on the launching stream around
  * every kernel the library enqueues (off by default).  ring_attn_timing_read
  * synchronises on the recorded events and reports, for the kernel class
- * `name` ("fwd_step", "lse_merge", "finalize", "bwd_pre", "bwd_step",
- * "bwd_post"), the
+ * `name` ("fwd_step", "lse_merge", "finalize", "bwd_pre", "bwd_step" (dK/dV),
+ * "bwd_dq", "bwd_post"), the
  * number of launches and their summed duration in milliseconds since the
  * last reset.  ring_attn_timing_enable(0) disables and resets. */
 int ring_attn_timing_enable(int enable);
