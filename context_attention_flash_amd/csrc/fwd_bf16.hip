@@ -15,9 +15,15 @@
 //   O^T[d x 32] += V^T[d x 64] * P^T[64 x 32]; the P^T operand is read
 //   straight from the S^T accumulator registers, which hold keys
 //   {0-3, 8-11} (lanes 0-31) and {4-7, 12-15} (lanes 32-63) of every 16-key
-//   step, so V^T is stored in LDS with that key order inside each 16-key group.
-// K and V^T tiles are double-buffered in LDS (global -> registers -> LDS),
-// XOR-swizzled so the 16-byte MFMA operand reads are free of bank conflicts.
+//   step; V^T comes from the gfx950 LDS transpose read ds_read_b64_tr_b16 on
+//   the natural V rows, picking the key rows in that same order.
+// K and V tiles are double-buffered in LDS in natural rows (global ->
+// registers -> LDS), XOR-swizzled so that 16-row operand reads and 4-row
+// transpose reads are free of bank conflicts.
+// The running max m only moves when a tile's max exceeds it by more than 8
+// (log2 units): exp2(s - m) then stays <= 256, which changes no result beyond
+// rounding, and the O rescale is skipped by the whole wave in almost every
+// tile.
 #include "kernel_args.h"
 #include "kernel_common.h"
 
@@ -32,31 +38,38 @@ struct FwdCfg {
     static constexpr int ROWB = DH * 2;        // bytes of one K row
     static constexpr int KCH = DH / 8;         // 16-byte chunks per K row
     static constexpr int K_BYTES = BK * ROWB;
-    static constexpr int V_BYTES = DH * BK * 2;
-    static constexpr int STAGE = K_BYTES + V_BYTES;
-    static constexpr int KLD = BK * KCH / NT;  // 16-byte K loads per thread per tile
-    static constexpr int VLD = (BK / 4) * (DH / 4) / NT;  // 4x4 V blocks per thread
+    static constexpr int STAGE = 2 * K_BYTES;  // K and V tiles, natural rows
+    static constexpr int KLD = BK * KCH / NT;  // 16-byte chunks per thread per tensor
     static constexpr int OUT_STRIDE = ROWB + 16;          // epilogue staging row
     static constexpr int LDS = 2 * STAGE > 4 * 32 * OUT_STRIDE ? 2 * STAGE : 4 * 32 * OUT_STRIDE;
-    static_assert(KLD >= 1 && VLD >= 1, "tile shape");
+    static_assert(KLD >= 1, "tile shape");
 };
 
-// K rows hold KCH 16-byte chunks; chunk c of row r is stored at c ^ swz(r).
-template <int KCH>
-__device__ __forceinline__ int k_swz(int row) {
-    return KCH == 16 ? (row & 15) : ((row >> 1) & 7);
+// 16-byte slot of logical chunk c in row r (rows of 16 chunks = 256 B, or 8
+// chunks = 128 B, two rows per bank cycle): 16 consecutive rows at one chunk,
+// and 4 consecutive rows x 2 chunks, hit distinct banks.
+template <int NCH>
+__device__ __forceinline__ int fslot(int r, int c) {
+    if (NCH == 16) return c ^ (((r & 7) << 1) | ((r >> 3) & 1));
+    return c ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
 }
-// V^T rows hold 64 keys = 8 chunks; chunk c of row d is stored at c ^ ((d>>1)&7).
-__device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
+template <int NCH>
+__device__ __forceinline__ int frow_off(int r, int c) {
+    return r * (NCH * 16) + (fslot<NCH>(r, c) << 4);
+}
 
-// Position of key group m (keys 4m..4m+3 of a 16-key group) inside that group
-// of a V^T row: order {0-3, 8-11, 4-7, 12-15}.
-__device__ __forceinline__ int v_group_slot(int m) { return m == 1 ? 2 : (m == 2 ? 1 : m); }
+typedef short fi16x4_t __attribute__((ext_vector_type(4)));
+// LDS transpose read: within each 16-lane group, result lane i, element k is
+// the 16-bit value at (address of lane 4k + i/4) + 2*(i%4).
+__device__ __forceinline__ u32x2_t fwd_tr16(const unsigned char* p) {
+    const fi16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) fi16x4_t*)(p));
+    return __builtin_bit_cast(u32x2_t, r);
+}
 
 template <int DH>
 struct FwdTileRegs {
-    u32x4_t k[FwdCfg<DH>::KLD];
-    u32x2_t v[FwdCfg<DH>::VLD][4];
+    u32x4_t k[FwdCfg<DH>::KLD], v[FwdCfg<DH>::KLD];
 };
 
 template <int DH>
@@ -68,18 +81,9 @@ __device__ __forceinline__ void fwd_load_tile(FwdTileRegs<DH>& R, const uint16_t
     for (int c = 0; c < C::KLD; ++c) {
         const int idx = tid + C::NT * c;
         const int row = idx / C::KCH, ch = idx % C::KCH;
-        const int key = min(kt * C::BK + row, Skv - 1);
+        const int64_t key = min(kt * C::BK + row, Skv - 1);
         R.k[c] = *(const u32x4_t*)(kb + key * row_stride + ch * 8);
-    }
-#pragma unroll
-    for (int c = 0; c < C::VLD; ++c) {
-        const int idx = tid + C::NT * c;
-        const int dg = idx % (DH / 4), kg = idx / (DH / 4);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int key = min(kt * C::BK + kg * 4 + rr, Skv - 1);
-            R.v[c][rr] = *(const u32x2_t*)(vb + key * row_stride + dg * 4);
-        }
+        R.v[c] = *(const u32x4_t*)(vb + key * row_stride + ch * 8);
     }
 }
 
@@ -87,35 +91,12 @@ template <int DH>
 __device__ __forceinline__ void fwd_store_tile(const FwdTileRegs<DH>& R, unsigned char* stage,
                                                int tid) {
     using C = FwdCfg<DH>;
-    unsigned char* Ks = stage;
-    unsigned char* Vt = stage + C::K_BYTES;
 #pragma unroll
     for (int c = 0; c < C::KLD; ++c) {
         const int idx = tid + C::NT * c;
         const int row = idx / C::KCH, ch = idx % C::KCH;
-        *(u32x4_t*)(Ks + row * C::ROWB + ((ch ^ k_swz<C::KCH>(row)) << 4)) = R.k[c];
-    }
-#pragma unroll
-    for (int c = 0; c < C::VLD; ++c) {
-        const int idx = tid + C::NT * c;
-        const int dg = idx % (DH / 4), kg = idx / (DH / 4);
-        const int sp = 16 * (kg >> 2) + 4 * v_group_slot(kg & 3);  // stored key position
-        const int chunk = sp >> 3, inner = (sp & 7) * 2;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int d = dg * 4 + e;
-            const int w = e >> 1;
-            uint32_t a0 = R.v[c][0][w], a1 = R.v[c][1][w], a2 = R.v[c][2][w], a3 = R.v[c][3][w];
-            u32x2_t o;
-            if (e & 1) {
-                o[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-                o[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-            } else {
-                o[0] = (a0 & 0xffffu) | (a1 << 16);
-                o[1] = (a2 & 0xffffu) | (a3 << 16);
-            }
-            *(u32x2_t*)(Vt + d * (C::BK * 2) + ((chunk ^ v_swz(d)) << 4) + inner) = o;
-        }
+        *(u32x4_t*)(stage + frow_off<C::KCH>(row, ch)) = R.k[c];
+        *(u32x4_t*)(stage + C::K_BYTES + frow_off<C::KCH>(row, ch)) = R.v[c];
     }
 }
 
@@ -147,11 +128,27 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
     const uint16_t* kb = (const uint16_t*)p.k + (int64_t)b * p.Skv * row_stride + hk * DH;
     const uint16_t* vb = (const uint16_t*)p.v + (int64_t)b * p.Skv * row_stride + hk * DH;
 
+    // per-lane LDS offsets: natural K reads of row l32 (+32 mt), chunk 2ks+g;
+    // transpose reads of V rows {4g, 8+4g} + j/4 (+16 kk), head-dim block dt.
+    const int j = lane & 15, gsel = (lane >> 4) & 1;
+    int nat[C::NKS];
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) nat[ks] = frow_off<C::KCH>(l32, 2 * ks + g);
+    int trv[2][C::NDT];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) {
+            const int col = 32 * dt + 16 * gsel + 4 * (j & 3);
+            trv[r][dt] = frow_off<C::KCH>(8 * r + 4 * g + (j >> 2), col >> 3) + (col & 7) * 2;
+        }
+
     f32x16_t oacc[C::NDT];
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] = (f32x16_t){};
     float m_run = -INFINITY, l_run = 0.f;
     const float c2 = p.scale_log2;
+    constexpr float kSlack = 8.f;  // log2 units the running max may lag behind
 
     if (e0 < e1) {
         FwdTileRegs<DH> R;
@@ -166,41 +163,43 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
             const int ent = ents[e];
             const int kt = ent & 0x7fffffff;
             const unsigned char* Ks = stage;
-            const unsigned char* Vt = stage + C::K_BYTES;
+            const unsigned char* Vs = stage + C::K_BYTES;
 
             // S^T = K Q^T for the 64 keys of the tile (two 32-key halves)
             f32x16_t sacc[2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                sacc[mt] = (f32x16_t){};
-                const int row = 32 * mt + l32;
-                const unsigned char* kr = Ks + row * C::ROWB;
-                const int sw = k_swz<C::KCH>(row);
+            for (int mt = 0; mt < 2; ++mt) sacc[mt] = (f32x16_t){};
 #pragma unroll
-                for (int ks = 0; ks < C::NKS; ++ks) {
-                    const u32x4_t a = *(const u32x4_t*)(kr + (((2 * ks + g) ^ sw) << 4));
+            for (int ks = 0; ks < C::NKS; ++ks)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    const u32x4_t a = *(const u32x4_t*)(Ks + nat[ks] + mt * 32 * C::ROWB);
                     sacc[mt] = mfma_32x32x16(a, qreg[ks], sacc[mt]);
                 }
-            }
             if (ent < 0) {  // partial tile: keys outside [ra, rb) are invisible
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = kt * C::BK + 32 * mt + (r >> 2) * 8 + g * 4 + (r & 3);
-                        if (key < ra || key >= rb) sacc[mt][r] = -INFINITY;
+                        sacc[mt][r] = ((key >= ra) & (key < rb)) ? sacc[mt][r] : -INFINITY;
                     }
             }
-            float mx = sacc[0][0];
+            float mx = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[1][r]));
+            mx = pair_max(mx) * c2;
+            // move the reference max only when this tile exceeds it by > kSlack
+            const bool bump = mx > m_run + kSlack;
+            if (__builtin_amdgcn_ballot_w64(bump)) {
+                // lanes that do not move keep alpha = 1 (m_run may be -inf there)
+                const float alpha = bump ? fast_exp2(m_run - mx) : 1.f;  // 0 if m_run = -inf
+                m_run = bump ? mx : m_run;
+                l_run *= alpha;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
-            mx = pair_max(mx);
-            const float m_new = fmaxf(m_run, mx * c2);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_use);
-            m_run = m_new;
+                for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] *= alpha;
+            }
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
             u32x4_t pb[4];
             float rs = 0.f;
@@ -213,22 +212,18 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
                     rs += p0 + p1;
                     pb[2 * mt + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
                 }
-            l_run = l_run * alpha + rs;
-#pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] *= alpha;
+            l_run += rs;
 
-            // O^T += V^T P^T
+            // O^T += V^T P^T; the K dimension (keys) of step kk takes rows
+            // 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3, as P is held.
 #pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt) {
-                const int row = 32 * dt + l32;
-                const unsigned char* vr = Vt + row * (C::BK * 2);
-                const int sw = v_swz(row);
+            for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const u32x4_t a = *(const u32x4_t*)(vr + (((2 * kk + g) ^ sw) << 4));
-                    oacc[dt] = mfma_32x32x16(a, pb[kk], oacc[dt]);
+                    const u32x2_t a1 = fwd_tr16(Vs + trv[0][dt] + kk * 16 * C::ROWB);
+                    const u32x2_t a2 = fwd_tr16(Vs + trv[1][dt] + kk * 16 * C::ROWB);
+                    oacc[dt] = mfma_32x32x16((u32x4_t){a1[0], a1[1], a2[0], a2[1]}, pb[kk], oacc[dt]);
                 }
-            }
             if (has_next) fwd_store_tile<DH>(R, smem + (((e - e0) & 1) ^ 1) * C::STAGE, tid);
         }
     }
