@@ -185,9 +185,11 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
                         sacc[mt][r] = ((key >= ra) & (key < rb)) ? sacc[mt][r] : -INFINITY;
                     }
             }
+            // linear chain: the compiler fuses pairs into v_max3_f32 (built with
+            // -fno-honor-nans, so no per-operand quieting is emitted)
             float mx = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[1][r]));
+            for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, sacc[0][r]), sacc[1][r]);
             mx = pair_max(mx) * c2;
             // move the reference max only when this tile exceeds it by > kSlack
             const bool bump = mx > m_run + kSlack;
@@ -201,6 +203,8 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
             }
             const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
+            // P rounded to bf16 for P V; the row sum stays in fp32 (a sum of the
+            // rounded values would cost up to 2^-9 in lse on rows with few keys)
             u32x4_t pb[4];
             float rs = 0.f;
 #pragma unroll
