@@ -280,6 +280,9 @@ int64_t bwd_workspace(const Geometry& g) {
 
 int check_support(const Geometry& g, bool bwd) {
     if (g.d != 64 && g.d != 128) return RA_E_UNSUPPORTED;
+    // kernels address one batch entry of a block, and of q, with 32-bit offsets
+    if ((int64_t)g.Skv * g.Hkv * g.d >= (1LL << 31) || (int64_t)g.S * g.Hq * g.d >= (1LL << 31))
+        return RA_E_SHAPE;
     if (bwd && g.dtype != RA_BF16) return RA_E_UNSUPPORTED;
     return RA_OK;
 }

@@ -38,7 +38,7 @@ struct FwdCfg {
     static constexpr int ROWB = DH * 2;        // bytes of one K row
     static constexpr int KCH = DH / 8;         // 16-byte chunks per K row
     static constexpr int K_BYTES = BK * ROWB;
-    static constexpr int STAGE = 2 * K_BYTES;  // K and V tiles, natural rows
+    static constexpr int STAGE = 2 * K_BYTES;  // one K and one V tile, natural rows
     static constexpr int KLD = BK * KCH / NT;  // 16-byte chunks per thread per tensor
     static constexpr int OUT_STRIDE = ROWB + 16;          // epilogue staging row
     static constexpr int LDS = 2 * STAGE > 4 * 32 * OUT_STRIDE ? 2 * STAGE : 4 * 32 * OUT_STRIDE;
@@ -67,36 +67,27 @@ __device__ __forceinline__ u32x2_t fwd_tr16(const unsigned char* p) {
     return __builtin_bit_cast(u32x2_t, r);
 }
 
+// One 64-key tile of K or V straight from global memory into LDS
+// (global_load_lds_dwordx4: the 16 bytes of lane l land at the wave-uniform
+// LDS base + 16*l).  Instruction c of wave w fills LDS chunks
+// 256c + 64w + lane, so the lane whose slot is physical chunk p of row r loads
+// logical chunk p ^ swizzle(r) of that row.  Offsets are 32-bit: the host
+// checks that a block of one batch entry holds fewer than 2^31 elements.
 template <int DH>
-struct FwdTileRegs {
-    u32x4_t k[FwdCfg<DH>::KLD], v[FwdCfg<DH>::KLD];
-};
-
-template <int DH>
-__device__ __forceinline__ void fwd_load_tile(FwdTileRegs<DH>& R, const uint16_t* kb,
-                                              const uint16_t* vb, int64_t row_stride,
-                                              int kt, int Skv, int tid) {
+__device__ __forceinline__ void fwd_load_lds(unsigned char* stage, const uint16_t* base,
+                                             int row_stride, int kt, int Skv, int wave,
+                                             int lane) {
     using C = FwdCfg<DH>;
 #pragma unroll
     for (int c = 0; c < C::KLD; ++c) {
-        const int idx = tid + C::NT * c;
-        const int row = idx / C::KCH, ch = idx % C::KCH;
-        const int64_t key = min(kt * C::BK + row, Skv - 1);
-        R.k[c] = *(const u32x4_t*)(kb + key * row_stride + ch * 8);
-        R.v[c] = *(const u32x4_t*)(vb + key * row_stride + ch * 8);
-    }
-}
-
-template <int DH>
-__device__ __forceinline__ void fwd_store_tile(const FwdTileRegs<DH>& R, unsigned char* stage,
-                                               int tid) {
-    using C = FwdCfg<DH>;
-#pragma unroll
-    for (int c = 0; c < C::KLD; ++c) {
-        const int idx = tid + C::NT * c;
-        const int row = idx / C::KCH, ch = idx % C::KCH;
-        *(u32x4_t*)(stage + frow_off<C::KCH>(row, ch)) = R.k[c];
-        *(u32x4_t*)(stage + C::K_BYTES + frow_off<C::KCH>(row, ch)) = R.v[c];
+        const int idx = C::NT * c + 64 * wave + lane;
+        const int row = idx / C::KCH, pc = idx % C::KCH;
+        const int lc = fslot<C::KCH>(row, pc);  // XOR swizzle: its own inverse
+        const int key = min(kt * C::BK + row, Skv - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(base + (key * row_stride + lc * 8)),
+            (__attribute__((address_space(3))) void*)(stage + (C::NT * c + 64 * wave) * 16), 16,
+            0, 0);
     }
 }
 
@@ -150,85 +141,108 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
     const float c2 = p.scale_log2;
     constexpr float kSlack = 8.f;  // log2 units the running max may lag behind
 
-    if (e0 < e1) {
-        FwdTileRegs<DH> R;
-        fwd_load_tile<DH>(R, kb, vb, row_stride, ents[e0] & 0x7fffffff, p.Skv, tid);
-        fwd_store_tile<DH>(R, smem, tid);
-        for (int e = e0; e < e1; ++e) {
-            unsigned char* stage = smem + ((e - e0) & 1) * C::STAGE;
-            __syncthreads();
-            const bool has_next = e + 1 < e1;
-            if (has_next)
-                fwd_load_tile<DH>(R, kb, vb, row_stride, ents[e + 1] & 0x7fffffff, p.Skv, tid);
-            const int ent = ents[e];
-            const int kt = ent & 0x7fffffff;
-            const unsigned char* Ks = stage;
-            const unsigned char* Vs = stage + C::K_BYTES;
+    // Software pipeline over the step's key tiles (n of them): K runs one tile
+    // ahead of V, so that S(i+1) = K(i+1) Q^T is issued on the MFMA pipe
+    // while the vector ALUs work on the softmax of tile i.  LDS holds two K
+    // stages and two V stages; in iteration i the wave reads K stage (i+1)%2
+    // and V stage i%2, and the threads refill K stage i%2 with tile i+2 and V
+    // stage (i+1)%2 with tile i+1 (both free since iteration i-1).
+    const int n = e1 - e0;
+    unsigned char* Kst[2] = {smem, smem + C::K_BYTES};
+    unsigned char* Vst[2] = {smem + 2 * C::K_BYTES, smem + 3 * C::K_BYTES};
+    const int rs32 = p.Hkv * DH;
 
-            // S^T = K Q^T for the 64 keys of the tile (two 32-key halves)
-            f32x16_t sacc[2];
+    auto s_tile = [&](f32x16_t (&sacc)[2], const unsigned char* Ks) {
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) sacc[mt] = (f32x16_t){};
+        for (int mt = 0; mt < 2; ++mt) sacc[mt] = (f32x16_t){};
 #pragma unroll
-            for (int ks = 0; ks < C::NKS; ++ks)
+        for (int ks = 0; ks < C::NKS; ++ks)
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    const u32x4_t a = *(const u32x4_t*)(Ks + nat[ks] + mt * 32 * C::ROWB);
-                    sacc[mt] = mfma_32x32x16(a, qreg[ks], sacc[mt]);
-                }
-            if (ent < 0) {  // partial tile: keys outside [ra, rb) are invisible
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kt * C::BK + 32 * mt + (r >> 2) * 8 + g * 4 + (r & 3);
-                        sacc[mt][r] = ((key >= ra) & (key < rb)) ? sacc[mt][r] : -INFINITY;
-                    }
+            for (int mt = 0; mt < 2; ++mt) {
+                const u32x4_t a = *(const u32x4_t*)(Ks + nat[ks] + mt * 32 * C::ROWB);
+                sacc[mt] = mfma_32x32x16(a, qreg[ks], sacc[mt]);
             }
-            // linear chain: the compiler fuses pairs into v_max3_f32 (built with
-            // -fno-honor-nans, so no per-operand quieting is emitted)
-            float mx = fmaxf(sacc[0][0], sacc[1][0]);
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, sacc[0][r]), sacc[1][r]);
-            mx = pair_max(mx) * c2;
-            // move the reference max only when this tile exceeds it by > kSlack
-            const bool bump = mx > m_run + kSlack;
-            if (__builtin_amdgcn_ballot_w64(bump)) {
-                // lanes that do not move keep alpha = 1 (m_run may be -inf there)
-                const float alpha = bump ? fast_exp2(m_run - mx) : 1.f;  // 0 if m_run = -inf
-                m_run = bump ? mx : m_run;
-                l_run *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] *= alpha;
-            }
-            const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    };
 
-            // P rounded to bf16 for P V; the row sum stays in fp32 (a sum of the
-            // rounded values would cost up to 2^-9 in lse on rows with few keys)
-            u32x4_t pb[4];
-            float rs = 0.f;
+    // softmax of tile i (scores in sacc) and O^T += V^T P^T
+    auto pv_tile = [&](f32x16_t (&sacc)[2], int ent, const unsigned char* Vs) {
+        const int kt = ent & 0x7fffffff;
+        if (ent < 0) {  // partial tile: keys outside [ra, rb) are invisible
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const float p0 = fast_exp2(fmaf(sacc[mt][r], c2, -m_use));
-                    const float p1 = fast_exp2(fmaf(sacc[mt][r + 1], c2, -m_use));
-                    rs += p0 + p1;
-                    pb[2 * mt + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kt * C::BK + 32 * mt + (r >> 2) * 8 + g * 4 + (r & 3);
+                    sacc[mt][r] = ((key >= ra) & (key < rb)) ? sacc[mt][r] : -INFINITY;
                 }
-            l_run += rs;
+        }
+        // linear chain: the compiler fuses pairs into v_max3_f32 (built with
+        // -fno-honor-nans, so no per-operand quieting is emitted)
+        float mx = fmaxf(sacc[0][0], sacc[1][0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, sacc[0][r]), sacc[1][r]);
+        mx = pair_max(mx) * c2;
+        // move the reference max only when this tile exceeds it by > kSlack
+        const bool bump = mx > m_run + kSlack;
+        if (__builtin_amdgcn_ballot_w64(bump)) {
+            // lanes that do not move keep alpha = 1 (m_run may be -inf there)
+            const float alpha = bump ? fast_exp2(m_run - mx) : 1.f;  // 0 if m_run = -inf
+            m_run = bump ? mx : m_run;
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] *= alpha;
+        }
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        // P rounded to bf16 for P V; the row sum stays in fp32 (a sum of the
+        // rounded values would cost up to 2^-9 in lse on rows with few keys)
+        u32x4_t pb[4];
+        float rsum = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = fast_exp2(fmaf(sacc[mt][r], c2, -m_use));
+                const float p1 = fast_exp2(fmaf(sacc[mt][r + 1], c2, -m_use));
+                rsum += p0 + p1;
+                pb[2 * mt + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+            }
+        l_run += rsum;
+        // O^T += V^T P^T; the K dimension (keys) of step kk takes rows
+        // 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3, as P is held.
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const u32x2_t a1 = fwd_tr16(Vs + trv[0][dt] + kk * 16 * C::ROWB);
+                const u32x2_t a2 = fwd_tr16(Vs + trv[1][dt] + kk * 16 * C::ROWB);
+                oacc[dt] = mfma_32x32x16((u32x4_t){a1[0], a1[1], a2[0], a2[1]}, pb[kk], oacc[dt]);
+            }
+    };
 
-            // O^T += V^T P^T; the K dimension (keys) of step kk takes rows
-            // 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3, as P is held.
-#pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const u32x2_t a1 = fwd_tr16(Vs + trv[0][dt] + kk * 16 * C::ROWB);
-                    const u32x2_t a2 = fwd_tr16(Vs + trv[1][dt] + kk * 16 * C::ROWB);
-                    oacc[dt] = mfma_32x32x16((u32x4_t){a1[0], a1[1], a2[0], a2[1]}, pb[kk], oacc[dt]);
-                }
-            if (has_next) fwd_store_tile<DH>(R, smem + (((e - e0) & 1) ^ 1) * C::STAGE, tid);
+    // iteration i: refill, overlap S(i+1) with softmax(i), P V of tile i
+    auto body = [&](int i, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS loads have landed
+        __syncthreads();  // K(i+1) and V(i) are in LDS; the stages refilled below are free
+        if (i + 2 < n)
+            fwd_load_lds<DH>(Kst[i & 1], kb, rs32, ents[e0 + i + 2] & 0x7fffffff, p.Skv, wave, lane);
+        if (i + 1 < n)
+            fwd_load_lds<DH>(Vst[(i + 1) & 1], vb, rs32, ents[e0 + i + 1] & 0x7fffffff, p.Skv, wave,
+                             lane);
+        if (i + 1 < n) s_tile(nxt, Kst[(i + 1) & 1]);
+        pv_tile(cur, ents[e0 + i], Vst[i & 1]);
+    };
+
+    if (n > 0) {
+        fwd_load_lds<DH>(Kst[0], kb, rs32, ents[e0] & 0x7fffffff, p.Skv, wave, lane);
+        fwd_load_lds<DH>(Vst[0], vb, rs32, ents[e0] & 0x7fffffff, p.Skv, wave, lane);
+        if (n > 1) fwd_load_lds<DH>(Kst[1], kb, rs32, ents[e0 + 1] & 0x7fffffff, p.Skv, wave, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        f32x16_t sa[2], sb[2];
+        s_tile(sa, Kst[0]);
+        for (int i = 0; i < n; i += 2) {
+            body(i, sa, sb);
+            if (i + 1 < n) body(i + 1, sb, sa);
         }
     }
 
