@@ -152,16 +152,22 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
     unsigned char* Vst[2] = {smem + 2 * C::K_BYTES, smem + 3 * C::K_BYTES};
     const int rs32 = p.Hkv * DH;
 
+    // S^T = K Q^T; the K operands of step ks+1 are read while step ks runs
     auto s_tile = [&](f32x16_t (&sacc)[2], const unsigned char* Ks) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) sacc[mt] = (f32x16_t){};
+        u32x4_t ka[2][2];
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks)
+        for (int mt = 0; mt < 2; ++mt) ka[0][mt] = *(const u32x4_t*)(Ks + nat[0] + mt * 32 * C::ROWB);
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const u32x4_t a = *(const u32x4_t*)(Ks + nat[ks] + mt * 32 * C::ROWB);
-                sacc[mt] = mfma_32x32x16(a, qreg[ks], sacc[mt]);
-            }
+        for (int ks = 0; ks < C::NKS; ++ks) {
+            if (ks + 1 < C::NKS)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+                    ka[(ks + 1) & 1][mt] = *(const u32x4_t*)(Ks + nat[ks + 1] + mt * 32 * C::ROWB);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) sacc[mt] = mfma_32x32x16(ka[ks & 1][mt], qreg[ks], sacc[mt]);
+        }
     };
 
     // softmax of tile i (scores in sacc) and O^T += V^T P^T
@@ -208,15 +214,25 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
             }
         l_run += rsum;
         // O^T += V^T P^T; the K dimension (keys) of step kk takes rows
-        // 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3, as P is held.
+        // 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3, as P is held.  The V^T
+        // operands of step kk+1 are read while the MFMAs of step kk run.
+        u32x4_t va[2][C::NDT];
+        auto read_v = [&](u32x4_t (&dst)[C::NDT], int kk) {
 #pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
+            for (int dt = 0; dt < C::NDT; ++dt) {
                 const u32x2_t a1 = fwd_tr16(Vs + trv[0][dt] + kk * 16 * C::ROWB);
                 const u32x2_t a2 = fwd_tr16(Vs + trv[1][dt] + kk * 16 * C::ROWB);
-                oacc[dt] = mfma_32x32x16((u32x4_t){a1[0], a1[1], a2[0], a2[1]}, pb[kk], oacc[dt]);
+                dst[dt] = (u32x4_t){a1[0], a1[1], a2[0], a2[1]};
             }
+        };
+        read_v(va[0], 0);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (kk + 1 < 4) read_v(va[(kk + 1) & 1], kk + 1);
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+                oacc[dt] = mfma_32x32x16(va[kk & 1][dt], pb[kk], oacc[dt]);
+        }
     };
 
     // iteration i: refill, overlap S(i+1) with softmax(i), P V of tile i
