@@ -377,36 +377,25 @@ struct DqCfg {
     static_assert(KLD >= 1, "tile shape");
 };
 
+// One 64-key tile of K or V straight from global memory into LDS
+// (global_load_lds_dwordx4: the 16 bytes of lane l land at the wave-uniform
+// LDS base + 16*l).  Instruction c of wave w fills LDS chunks 256c + 64w +
+// lane, so the lane whose slot is physical chunk p of row r loads logical
+// chunk p ^ swizzle(r).
 template <int DH>
-struct DqTileRegs {
-    u32x4_t k[DqCfg<DH>::KLD], v[DqCfg<DH>::KLD];
-};
-
-template <int DH>
-__device__ __forceinline__ void dq_load_tile(DqTileRegs<DH>& R, const uint16_t* kb,
-                                             const uint16_t* vb, int kv_stride, int kt, int Skv,
-                                             int tid) {
+__device__ __forceinline__ void dq_load_lds(unsigned char* stage, const uint16_t* base,
+                                            int kv_stride, int kt, int Skv, int wave, int lane) {
     using C = DqCfg<DH>;
 #pragma unroll
     for (int c = 0; c < C::KLD; ++c) {
-        const int idx = tid + C::NT * c;
-        const int row = idx / C::KCH, ch = idx % C::KCH;
-        const int64_t key = min(kt * C::BK + row, Skv - 1);
-        R.k[c] = *(const u32x4_t*)(kb + key * kv_stride + ch * 8);
-        R.v[c] = *(const u32x4_t*)(vb + key * kv_stride + ch * 8);
-    }
-}
-
-template <int DH>
-__device__ __forceinline__ void dq_store_tile(const DqTileRegs<DH>& R, unsigned char* stage,
-                                              int tid) {
-    using C = DqCfg<DH>;
-#pragma unroll
-    for (int c = 0; c < C::KLD; ++c) {
-        const int idx = tid + C::NT * c;
-        const int row = idx / C::KCH, ch = idx % C::KCH;
-        *(u32x4_t*)(stage + row_off<C::KCH>(row, ch)) = R.k[c];
-        *(u32x4_t*)(stage + C::K_BYTES + row_off<C::KCH>(row, ch)) = R.v[c];
+        const int idx = C::NT * c + 64 * wave + lane;
+        const int row = idx / C::KCH, pc = idx % C::KCH;
+        const int lc = slot<C::KCH>(row, pc);  // XOR swizzle: its own inverse
+        const int key = min(kt * C::BK + row, Skv - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(base + (key * kv_stride + lc * 8)),
+            (__attribute__((address_space(3))) void*)(stage + (C::NT * c + 64 * wave) * 16), 16,
+            0, 0);
     }
 }
 
@@ -467,37 +456,53 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(DqArgs p) {
     const float c2 = p.scale_log2;
 
     if (e0 < e1) {
-        DqTileRegs<DH> R;
-        dq_load_tile<DH>(R, kb, vb, kv_stride, ents[e0] & 0x7fffffff, p.Skv, tid);
-        dq_store_tile<DH>(R, smem, tid);
+        dq_load_lds<DH>(smem, kb, kv_stride, ents[e0] & 0x7fffffff, p.Skv, wave, lane);
+        dq_load_lds<DH>(smem + C::K_BYTES, vb, kv_stride, ents[e0] & 0x7fffffff, p.Skv, wave, lane);
         for (int e = e0; e < e1; ++e) {
 #pragma unroll
             for (int dt = 0; dt < C::NDT; ++dt) asm volatile("" : "+a"(acc[dt]));
             unsigned char* stage = smem + ((e - e0) & 1) * C::STAGE;
-            __syncthreads();
-            const bool has_next = e + 1 < e1;
-            if (has_next) dq_load_tile<DH>(R, kb, vb, kv_stride, ents[e + 1] & 0x7fffffff, p.Skv, tid);
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS loads have landed
+            __syncthreads();  // tile e is in LDS; the other stage is free
+            if (e + 1 < e1) {
+                unsigned char* nxt = smem + (((e - e0) & 1) ^ 1) * C::STAGE;
+                const int ktn = ents[e + 1] & 0x7fffffff;
+                dq_load_lds<DH>(nxt, kb, kv_stride, ktn, p.Skv, wave, lane);
+                dq_load_lds<DH>(nxt + C::K_BYTES, vb, kv_stride, ktn, p.Skv, wave, lane);
+            }
             const int ent = ents[e];
             const int kt = ent & 0x7fffffff;
             const unsigned char* Ks = stage;
             const unsigned char* Vs = stage + C::K_BYTES;
 
-            // S^T = K Q^T and dP^T = V dO^T for the 64 keys (two 32-key halves)
+            // S^T = K Q^T and dP^T = V dO^T for the 64 keys (two 32-key halves);
+            // the operands of step ks+1 are read while step ks runs
             f32x16_t sacc[2], pacc[2];
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 sacc[mt] = (f32x16_t){};
                 pacc[mt] = (f32x16_t){};
             }
+            u32x4_t ka[2][2], va[2][2];
 #pragma unroll
-            for (int ks = 0; ks < C::NKS; ++ks)
+            for (int mt = 0; mt < 2; ++mt) {
+                ka[0][mt] = *(const u32x4_t*)(Ks + nat[0] + mt * 32 * C::ROWB);
+                va[0][mt] = *(const u32x4_t*)(Vs + nat[0] + mt * 32 * C::ROWB);
+            }
+#pragma unroll
+            for (int ks = 0; ks < C::NKS; ++ks) {
+                if (ks + 1 < C::NKS)
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) {
+                        ka[(ks + 1) & 1][mt] = *(const u32x4_t*)(Ks + nat[ks + 1] + mt * 32 * C::ROWB);
+                        va[(ks + 1) & 1][mt] = *(const u32x4_t*)(Vs + nat[ks + 1] + mt * 32 * C::ROWB);
+                    }
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {
-                    const u32x4_t ka = *(const u32x4_t*)(Ks + nat[ks] + mt * 32 * C::ROWB);
-                    const u32x4_t va = *(const u32x4_t*)(Vs + nat[ks] + mt * 32 * C::ROWB);
-                    sacc[mt] = mfma_32x32x16(ka, qreg[ks], sacc[mt]);
-                    pacc[mt] = mfma_32x32x16(va, oreg[ks], pacc[mt]);
+                    sacc[mt] = mfma_32x32x16(ka[ks & 1][mt], qreg[ks], sacc[mt]);
+                    pacc[mt] = mfma_32x32x16(va[ks & 1][mt], oreg[ks], pacc[mt]);
                 }
+            }
             // P = exp(scale*S - lse) and dS = P (dP - Delta); element (mt, r) is key
             // 32*mt + 8*(r/4) + 4*g + r%4 of the tile.
             u32x4_t db[4];
@@ -518,16 +523,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(DqArgs p) {
                     db[2 * mt + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(pv[0], pv[1]);
                 }
             // dQ^T += K^T dS^T; the K dimension (keys) of step kk takes rows
-            // 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3, as dS is held.
+            // 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3, as dS is held.  The K^T
+            // operands of step kk+1 are read while step kk runs.
+            u32x4_t kt4[2][C::NDT];
+            auto read_kt = [&](u32x4_t (&dst)[C::NDT], int kk) {
 #pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt)
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
+                for (int dt = 0; dt < C::NDT; ++dt) {
                     const u32x2_t a1 = lds_tr16(Ks + trk[0][dt] + kk * 16 * C::ROWB);
                     const u32x2_t a2 = lds_tr16(Ks + trk[1][dt] + kk * 16 * C::ROWB);
-                    acc[dt] = mfma_32x32x16((u32x4_t){a1[0], a1[1], a2[0], a2[1]}, db[kk], acc[dt]);
+                    dst[dt] = (u32x4_t){a1[0], a1[1], a2[0], a2[1]};
                 }
-            if (has_next) dq_store_tile<DH>(R, smem + (((e - e0) & 1) ^ 1) * C::STAGE, tid);
+            };
+            read_kt(kt4[0], 0);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                if (kk + 1 < 4) read_kt(kt4[(kk + 1) & 1], kk + 1);
+#pragma unroll
+                for (int dt = 0; dt < C::NDT; ++dt)
+                    acc[dt] = mfma_32x32x16(kt4[kk & 1][dt], db[kk], acc[dt]);
+            }
         }
     }
 
