@@ -32,9 +32,11 @@ struct DevStep {
     int64_t pairs = 0;
     const int32_t* rng = nullptr;
     const int32_t* f_off = nullptr;
+    const int32_t* f_mid = nullptr;
     const int32_t* f_ent = nullptr;
     const int32_t* f_order = nullptr;
     const int32_t* b_off = nullptr;
+    const int32_t* b_mid = nullptr;
     const int32_t* b_ent = nullptr;
     const int32_t* b_order = nullptr;
 };
@@ -68,19 +70,27 @@ struct HostArrays {
     }
 };
 
+// Tile lists: list l holds entries off[l] .. off[l+1]-1, the FULL tiles first
+// (in tile order) and from mid[l] on the PARTIAL ones, so that a kernel can run
+// its unmasked and its masked loop without a per-tile branch.
 void build_lists(const std::vector<int8_t>& kinds, int64_t nrows, int64_t ncols, bool by_row,
-                 std::vector<int32_t>& off, std::vector<int32_t>& ent,
+                 std::vector<int32_t>& off, std::vector<int32_t>& mid, std::vector<int32_t>& ent,
                  std::vector<int32_t>& order) {
     // by_row: lists per row tile (forward, per query tile over key tiles);
     // else lists per column tile (backward, per key tile over query tiles).
     const int64_t nlists = by_row ? nrows : ncols, nitems = by_row ? ncols : nrows;
     off.assign(nlists + 1, 0);
+    mid.assign(nlists, 0);
     ent.clear();
     for (int64_t l = 0; l < nlists; ++l) {
-        for (int64_t it = 0; it < nitems; ++it) {
-            const int8_t k = by_row ? kinds[l * ncols + it] : kinds[it * ncols + l];
-            if (k == TILE_EMPTY) continue;
-            ent.push_back((int32_t)it | (k == TILE_PARTIAL ? (int32_t)0x80000000u : 0));
+        for (int pass = 0; pass < 2; ++pass) {
+            const int8_t want = pass == 0 ? TILE_FULL : TILE_PARTIAL;
+            if (pass == 1) mid[l] = (int32_t)ent.size();
+            for (int64_t it = 0; it < nitems; ++it) {
+                const int8_t k = by_row ? kinds[l * ncols + it] : kinds[it * ncols + l];
+                if (k != want) continue;
+                ent.push_back((int32_t)it | (k == TILE_PARTIAL ? (int32_t)0x80000000u : 0));
+            }
         }
         off[l + 1] = (int32_t)ent.size();
     }
@@ -101,7 +111,7 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
     const int64_t nqt_b = (g.S + BWD_BQ - 1) / BWD_BQ;
 
     HostArrays H;
-    struct Idx { size_t rng, foff, fent, ford, boff, bent, bord; };
+    struct Idx { size_t rng, foff, fmid, fent, ford, boff, bmid, bent, bord; };
     std::vector<Idx> idx;
     std::vector<StepRanges> all(g.nb);
     int64_t total_pairs = 0;
@@ -127,15 +137,17 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
         }
         Idx ix;
         ix.rng = H.add(std::move(rng));
-        std::vector<int32_t> off, ent, order;
+        std::vector<int32_t> off, mid, ent, order;
         classify(sr, g.S, g.Skv, FWD_BQ, FWD_BK, kinds);
-        build_lists(kinds, plan->nqt, nkt_f, true, off, ent, order);
+        build_lists(kinds, plan->nqt, nkt_f, true, off, mid, ent, order);
         ix.foff = H.add(std::move(off));
+        ix.fmid = H.add(std::move(mid));
         ix.fent = H.add(std::move(ent));
         ix.ford = H.add(std::move(order));
         classify(sr, g.S, g.Skv, BWD_BQ, BWD_BK, kinds);
-        build_lists(kinds, nqt_b, plan->nkt_b, false, off, ent, order);
+        build_lists(kinds, nqt_b, plan->nkt_b, false, off, mid, ent, order);
         ix.boff = H.add(std::move(off));
+        ix.bmid = H.add(std::move(mid));
         ix.bent = H.add(std::move(ent));
         ix.bord = H.add(std::move(order));
         plan->steps.push_back(ds);
@@ -163,9 +175,11 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
         DevStep& d = plan->steps[k];
         d.rng = P(idx[k].rng);
         d.f_off = P(idx[k].foff);
+        d.f_mid = P(idx[k].fmid);
         d.f_ent = P(idx[k].fent);
         d.f_order = P(idx[k].ford);
         d.b_off = P(idx[k].boff);
+        d.b_mid = P(idx[k].bmid);
         d.b_ent = P(idx[k].bent);
         d.b_order = P(idx[k].bord);
     }
@@ -268,14 +282,14 @@ int64_t fwd_workspace(const Geometry& g) {
     return 2 * o + round_up((int64_t)g.B * g.Hq * g.S * 4, 256);
 }
 
-// Backward workspace: Delta [B, Hq, S_pad] fp32, then the dQ accumulator
-// [B, Hq, S_pad, d] fp32.
-int64_t bwd_delta_bytes(const Geometry& g) {
+// Backward workspace: the per-row arrays lse2 and -Delta, [B, Hq, S_pad] fp32
+// each, then the dQ accumulator [B, Hq, S_pad, d] fp32.
+int64_t bwd_row_bytes(const Geometry& g) {
     return round_up((int64_t)g.B * g.Hq * round_up(g.S, FWD_BQ) * 4, 256);
 }
 int64_t bwd_workspace(const Geometry& g) {
     const int64_t S_pad = round_up(g.S, FWD_BQ);
-    return bwd_delta_bytes(g) + round_up((int64_t)g.B * g.Hq * S_pad * g.d * 4, 256);
+    return 2 * bwd_row_bytes(g) + round_up((int64_t)g.B * g.Hq * S_pad * g.d * 4, 256);
 }
 
 int check_support(const Geometry& g, bool bwd) {
@@ -448,7 +462,7 @@ int ring_attn_fwd(const ring_attn_desc* desc, const void* q, const void* k, cons
                 const DevStep& st = plan->steps[i];
                 a.k = (const unsigned char*)k + st.j * block_elems * eb;
                 a.v = (const unsigned char*)v + st.j * block_elems * eb;
-                a.rng = st.rng; a.t_off = st.f_off; a.t_ent = st.f_ent; a.t_order = st.f_order;
+                a.rng = st.rng; a.t_off = st.f_off; a.t_mid = st.f_mid; a.t_ent = st.f_ent; a.t_order = st.f_order;
                 a.mode = n == 1 ? FWD_SOLO : (i == 0 ? FWD_FIRST : (i + 1 == n ? FWD_LAST : FWD_MERGE));
                 if ((rc = hip_rc(launch_step(a))) != RA_OK) return rc;
             }
@@ -461,7 +475,7 @@ int ring_attn_fwd(const ring_attn_desc* desc, const void* q, const void* k, cons
                 const DevStep& st = plan->steps[i];
                 a.k = (const unsigned char*)k + st.j * block_elems * eb;
                 a.v = (const unsigned char*)v + st.j * block_elems * eb;
-                a.rng = st.rng; a.t_off = st.f_off; a.t_ent = st.f_ent; a.t_order = st.f_order;
+                a.rng = st.rng; a.t_off = st.f_off; a.t_mid = st.f_mid; a.t_ent = st.f_ent; a.t_order = st.f_order;
                 a.mode = FWD_PARTIAL;
                 a.o_part = i == 0 ? o_run : o_j;
                 a.lse_part = i == 0 ? lse : l_j;
@@ -500,18 +514,19 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
         const Plan* plan = nullptr;
         if ((rc = get_plan(g, &plan)) != RA_OK) return rc;
         hipStream_t s = (hipStream_t)stream;
-        float* delta = (float*)workspace;
-        float* dq_acc = (float*)((unsigned char*)workspace + bwd_delta_bytes(g));
+        float* lse2 = (float*)workspace;
+        float* ndelta = (float*)((unsigned char*)workspace + bwd_row_bytes(g));
+        float* dq_acc = (float*)((unsigned char*)workspace + 2 * bwd_row_bytes(g));
 
         BwdPreArgs pa{};
-        pa.dout = dout; pa.out = out; pa.delta = delta;
+        pa.dout = dout; pa.out = out; pa.lse = lse; pa.lse2 = lse2; pa.ndelta = ndelta;
         pa.B = g.B; pa.S = (int32_t)g.S; pa.Hq = g.Hq; pa.S_pad = (int32_t)plan->S_pad; pa.d = g.d;
         rc = hip_rc(timed(KC_BWD_PRE, s, [&] { return launch_bwd_pre(pa, 1, s); }));
         if (rc != RA_OK) return rc;
 
         const int64_t block_elems = (int64_t)g.B * g.Skv * g.Hkv * g.d;
         BwdArgs a{};
-        a.q = (const uint16_t*)q; a.dout = (const uint16_t*)dout; a.lse = lse; a.delta = delta;
+        a.q = (const uint16_t*)q; a.dout = (const uint16_t*)dout; a.lse2 = lse2; a.ndelta = ndelta;
         a.B = g.B; a.S = (int32_t)g.S; a.Skv = (int32_t)g.Skv; a.Hq = g.Hq; a.Hkv = g.Hkv;
         a.nkt = plan->nkt_b;
         a.S_pad = (int32_t)plan->S_pad;
@@ -519,8 +534,8 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
         a.scale = g.scale;
         a.scale_log2 = g.scale * 1.4426950408889634f;
         DqArgs qa{};
-        qa.q = (const uint16_t*)q; qa.dout = (const uint16_t*)dout; qa.lse = lse;
-        qa.delta = delta; qa.dq_acc = dq_acc;
+        qa.q = (const uint16_t*)q; qa.dout = (const uint16_t*)dout; qa.lse2 = lse2;
+        qa.ndelta = ndelta; qa.dq_acc = dq_acc;
         qa.B = g.B; qa.S = (int32_t)g.S; qa.Skv = (int32_t)g.Skv; qa.Hq = g.Hq; qa.Hkv = g.Hkv;
         qa.nqt = plan->nqt;
         qa.S_pad = (int32_t)plan->S_pad;
@@ -533,7 +548,7 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
             a.v = (const uint16_t*)v + st.j * block_elems;
             a.dk = dk + st.j * block_elems;
             a.dv = dv + st.j * block_elems;
-            a.rng = st.rng; a.t_off = st.b_off; a.t_ent = st.b_ent; a.t_order = st.b_order;
+            a.rng = st.rng; a.t_off = st.b_off; a.t_mid = st.b_mid; a.t_ent = st.b_ent; a.t_order = st.b_order;
             if (st.pairs > 0) {
                 rc = hip_rc(timed(KC_BWD, s, [&] { return launch_bwd_dkdv_bf16(a, g.d, s); }));
                 if (rc != RA_OK) return rc;
@@ -541,7 +556,7 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
             // the dQ kernel writes the accumulator on the first step (also when a
             // step has no visible pair, in which case it writes zeros)
             qa.k = a.k; qa.v = a.v;
-            qa.rng = st.rng; qa.t_off = st.f_off; qa.t_ent = st.f_ent; qa.t_order = st.f_order;
+            qa.rng = st.rng; qa.t_off = st.f_off; qa.t_mid = st.f_mid; qa.t_ent = st.f_ent; qa.t_order = st.f_order;
             qa.first = first ? 1 : 0;
             if (st.pairs > 0 || first) {
                 rc = hip_rc(timed(KC_BWD_DQ, s, [&] { return launch_bwd_dq_bf16(qa, g.d, s); }));

@@ -4,14 +4,16 @@
 // adds into dq, dk_j and dv_j).  Two kernels share the step:
 //
 // K4a bwd_dkdv: one work-group = one (batch, kv head, 128-key tile of block
-// j); wave w owns keys 32w..32w+31.  It walks every 64-row query tile of every
-// query head of the GQA group that sees its keys and computes
+// j); wave w owns keys 32w..32w+31, whose K and V rows stay in registers.  It
+// walks every 64-row query tile of every query head of the GQA group that sees
+// its keys and computes
 //   S = Q K^T and dP = dO V^T        (C layout: lane = key, 16 query rows)
 //   P = exp(scale*S - lse), dS = P (dP - Delta)
 //   dV^T += dO^T P,  dK^T += Q^T dS  (fp32 accumulators in AGPRs)
-// Q, dO, K and V live in LDS in natural rows; dO^T and Q^T come from the gfx950
-// transpose read ds_read_b64_tr_b16 (within each 16-lane group, result lane i,
-// element k is the 16-bit value at (address of lane 4k + i/4) + 2*(i%4)).
+// Query tiles stream through two LDS stages (natural rows); dO^T and Q^T
+// come from the gfx950 transpose read ds_read_b64_tr_b16 (within each 16-lane
+// group, result lane i, element k is the 16-bit value at (address of lane 4k +
+// i/4) + 2*(i%4)).
 // P and dS feed the MFMAs straight from the accumulator registers, whose query
 // order inside each 16-row group is {0-3, 8-11 | 4-7, 12-15} (lanes 0-31 |
 // 32-63); the transpose reads pick their rows in that same order.  dK/dV are
@@ -24,6 +26,8 @@
 // tile) has one owner per launch, so dQ needs no atomics: fp32 atomics on the
 // L2 run about ten times slower than plain stores, and the dQ of a key-tile
 // decomposition would be bound by them.
+#include <type_traits>
+
 #include "kernel_args.h"
 #include "kernel_common.h"
 
@@ -38,15 +42,16 @@ struct BwdCfg {
     static constexpr int ROWB = DH * 2;             // natural row (bytes)
     static constexpr int KCH = DH / 8;              // 16-byte chunks per natural row
     static constexpr int Q_BYTES = BQ * ROWB;
-    static constexpr int K_BYTES = BK * ROWB;
+    // one stage: Q, dO (natural rows), then the row values of the tile:
+    // lse2[64], -Delta[64] (fp32) and the key interval [a, b) of each row
     static constexpr int OFF_Q = 0;
-    static constexpr int OFF_DO = OFF_Q + Q_BYTES;
-    static constexpr int OFF_K = OFF_DO + Q_BYTES;
-    static constexpr int OFF_V = OFF_K + K_BYTES;
-    static constexpr int OFF_ROW = OFF_V + K_BYTES;   // lse2, delta, a, b per query row
-    static constexpr int LDS = OFF_ROW + 4 * BQ * 4;
-    static constexpr int LDT = BQ * KCH / 4;        // threads taking part in a Q/dO load
-    static_assert(LDT == NT || LDT == NT / 2, "tile shape");
+    static constexpr int OFF_DO = Q_BYTES;
+    static constexpr int OFF_L = 2 * Q_BYTES;
+    static constexpr int OFF_ND = OFF_L + BQ * 4;
+    static constexpr int OFF_RNG = OFF_ND + BQ * 4;
+    static constexpr int STAGE = OFF_RNG + BQ * 8;
+    static constexpr int QLD = Q_BYTES / 16 / NT;   // 16-byte chunks per thread per tensor
+    static_assert(QLD >= 1 && BQ * 16 == 1024, "tile shape");
 };
 
 // 16-byte slot of logical chunk c in row r.  Rows of 16 chunks (256 B) and of
@@ -86,60 +91,70 @@ __device__ __forceinline__ u32x4_t tr_operand(const unsigned char* base, int r1,
     return (u32x4_t){a[0], a[1], b[0], b[1]};
 }
 
-// Global -> registers: 4 consecutive query rows x one 16-byte chunk of Q and
-// dO, plus the per-row values of row tid.
+// One 64-row query tile (head h, tile qt) straight from global memory into a
+// stage.  Q and dO come through buffer loads into LDS (buffer_load_dwordx4 ...
+// lds: the 16 bytes of lane l land at the wave-uniform LDS base + 16*l).  The
+// buffer of a batch entry spans its S rows, so the rows of a last partial tile
+// past S read as zeros; the per-lane part of every offset is fixed (voff, the
+// XOR swizzle applied through the source chunk as in the dQ kernel) and the
+// tile moves only the scalar offset.  Wave 0 also brings the 1 KB of row
+// values: lanes 0-15 lse2, 16-31 -Delta, 32-63 the intervals.
 template <int DH>
-struct BwdTileRegs {
-    u32x4_t q[4], o[4];
-    float l2, dl;   // lse * log2(e) (+inf: row sees no key) and Delta
-    int a, b;       // visible key interval
+struct DkdvLoader {
+    using C = BwdCfg<DH>;
+    __amdgpu_buffer_rsrc_t rq, ro;
+    int voff[C::QLD];
+    int row_stride;     // bytes per query row (all heads)
+
+    __device__ __forceinline__ void init(const BwdArgs& p, int b, int wave, int lane) {
+        const int q_stride = p.Hq * DH;
+        row_stride = q_stride * 2;
+        const int bytes = p.S * row_stride;   // < 2^32: the ABI bounds S * Hq * d
+        rq = __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + (int64_t)b * p.S * q_stride), (short)0,
+                                               bytes, 0x00020000);
+        ro = __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + (int64_t)b * p.S * q_stride), (short)0,
+                                               bytes, 0x00020000);
+#pragma unroll
+        for (int c = 0; c < C::QLD; ++c) {
+            const int idx = C::NT * c + 64 * wave + lane;
+            const int row = idx / C::KCH, pc = idx % C::KCH;
+            voff[c] = row * row_stride + slot<C::KCH>(row, pc) * 16;
+        }
+    }
+
+    __device__ __forceinline__ void load(unsigned char* stage, const BwdArgs& p, int b, int h,
+                                         int qt, int wave, int lane) const {
+        const int soff = qt * C::BQ * row_stride + h * DH * 2;
+#pragma unroll
+        for (int c = 0; c < C::QLD; ++c) {
+            const int dst = (C::NT * c + 64 * wave) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rq, (__attribute__((address_space(3))) void*)(stage + C::OFF_Q + dst), 16, voff[c],
+                soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ro, (__attribute__((address_space(3))) void*)(stage + C::OFF_DO + dst), 16, voff[c],
+                soff, 0, 0);
+        }
+        if (wave == 0) {
+            const int64_t r0 = ((int64_t)b * p.Hq + h) * p.S_pad + qt * C::BQ;
+            const void* src = lane < 16   ? (const void*)(p.lse2 + r0 + 4 * lane)
+                              : lane < 32 ? (const void*)(p.ndelta + r0 + 4 * (lane - 16))
+                                          : (const void*)(p.rng + 2 * qt * C::BQ + 4 * (lane - 32));
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(stage + C::OFF_L),
+                                             16, 0, 0);
+        }
+    }
 };
 
 template <int DH>
-__device__ __forceinline__ void bwd_load_tile(BwdTileRegs<DH>& R, const BwdArgs& p, int b, int h,
-                                              int qt, int tid) {
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_bf16_kernel(BwdArgs p) {
     using C = BwdCfg<DH>;
-    const int q_stride = p.Hq * DH;
-    if (tid < C::LDT) {
-        const uint16_t* qh = p.q + ((int64_t)b * p.S) * q_stride + h * DH;
-        const uint16_t* oh = p.dout + ((int64_t)b * p.S) * q_stride + h * DH;
-        const int m = tid / C::KCH, ch = tid % C::KCH;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int row = min(qt * C::BQ + 4 * m + rr, p.S - 1);
-            R.q[rr] = *(const u32x4_t*)(qh + (int64_t)row * q_stride + ch * 8);
-            R.o[rr] = *(const u32x4_t*)(oh + (int64_t)row * q_stride + ch * 8);
-        }
-    }
-    if (tid < C::BQ) {
-        const int iq = qt * C::BQ + tid;
-        const int iqc = min(iq, p.S - 1);
-        const float L = p.lse[((int64_t)b * p.Hq + h) * p.S + iqc];
-        R.dl = p.delta[((int64_t)b * p.Hq + h) * p.S_pad + iqc];
-        R.a = p.rng[2 * iqc];
-        R.b = p.rng[2 * iqc + 1];
-        R.l2 = L == -INFINITY ? INFINITY : L * kLog2e;
-        if (iq >= p.S) {  // rows past the shard contribute nothing
-            R.l2 = INFINITY;
-            R.dl = 0.f;
-            R.a = 0;
-            R.b = 0;
-        }
-    }
-}
-
-template <int DH>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs p) {
-    using C = BwdCfg<DH>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
-    unsigned char* sQ = smem + C::OFF_Q;
-    unsigned char* sDO = smem + C::OFF_DO;
-    unsigned char* sK = smem + C::OFF_K;
-    unsigned char* sV = smem + C::OFF_V;
-    float* sL = (float*)(smem + C::OFF_ROW);
-    float* sD = sL + C::BQ;
-    int32_t* sA = (int32_t*)(sD + C::BQ);
-    int32_t* sB = sA + C::BQ;
+    // Two stages as separate objects: every access below names its stage
+    // statically, which lets the compiler see that the transpose reads of one
+    // stage never overlap the direct-to-LDS loads into the other (it would
+    // otherwise wait for those loads before every transpose read).
+    __shared__ __attribute__((aligned(16))) unsigned char stA[C::STAGE];
+    __shared__ __attribute__((aligned(16))) unsigned char stB[C::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
@@ -151,19 +166,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs p) {
     const int kt = as_const(p.t_order)[t];
     const int e0 = as_const(p.t_off)[kt], e1 = as_const(p.t_off)[kt + 1];
     const int group = p.Hq / p.Hkv;
+    // the list holds the FULL tiles first, the PARTIAL ones from entry m on;
+    // iterations [0, nF) walk the full tiles of every head of the group, the
+    // rest the partial ones
+    const int m = as_const(p.t_mid)[kt];
+    const int nF = (m - e0) * group;
+    const int n_iter = (e1 - e0) * group;
 
     const int kv_stride = p.Hkv * DH;
-    const uint16_t* kb = p.k + (int64_t)b * p.Skv * kv_stride + hk * DH;
-    const uint16_t* vb = p.v + (int64_t)b * p.Skv * kv_stride + hk * DH;
     const int key = kt * C::BK + wave * 32 + l32;   // this lane's key (C-layout column)
     const int keyc = min(key, p.Skv - 1);
 
-    // K and V tiles of the work-group in LDS (natural rows).
-    for (int idx = tid; idx < C::BK * C::KCH; idx += C::NT) {
-        const int r = idx / C::KCH, ch = idx % C::KCH;
-        const int64_t kr = min(kt * C::BK + r, p.Skv - 1);
-        *(u32x4_t*)(sK + row_off<C::KCH>(r, ch)) = *(const u32x4_t*)(kb + kr * kv_stride + ch * 8);
-        *(u32x4_t*)(sV + row_off<C::KCH>(r, ch)) = *(const u32x4_t*)(vb + kr * kv_stride + ch * 8);
+    // This lane's K and V row are the B operands of S and dP for every tile.
+    u32x4_t kreg[C::NKS], vreg[C::NKS];
+    {
+        const uint16_t* kr = p.k + ((int64_t)b * p.Skv + keyc) * kv_stride + hk * DH;
+        const uint16_t* vr = p.v + ((int64_t)b * p.Skv + keyc) * kv_stride + hk * DH;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+            kreg[ks] = *(const u32x4_t*)(kr + 16 * ks + 8 * g);
+            vreg[ks] = *(const u32x4_t*)(vr + 16 * ks + 8 * g);
+        }
     }
 
     f32x16_t dk_acc[C::NDT], dv_acc[C::NDT];
@@ -173,8 +196,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs p) {
         dv_acc[dt] = (f32x16_t){};
     }
     const float c2 = p.scale_log2;
-    const int n_ent = e1 - e0;
-    const int n_iter = n_ent * group;
 
     // Per-lane LDS offsets.  Every swizzle below depends only on the low four
     // bits of the row, so moving by 16 or 32 rows is a constant offset.
@@ -193,135 +214,162 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(BwdArgs p) {
             trq[r][dt] = row_off<C::KCH>(8 * r + 4 * g + (j >> 2), col >> 3) + (col & 7) * 2;
         }
 
-    // Registers -> LDS: the staged query tile (natural rows) and its row values.
-    auto store_tile = [&](const BwdTileRegs<DH>& T) {
-        if (tid < C::LDT) {
-            const int m = tid / C::KCH, ch = tid % C::KCH;
+    // Iteration it -> (query head, list entry).  The entry of the next tile
+    // is fetched one iteration ahead so that its scalar load is off the path.
+    DkdvLoader<DH> ld;
+    ld.init(p, b, wave, lane);
+    auto entry_of = [&](int it) {
+        const bool full = it < nF;
+        const int n = full ? m - e0 : e1 - m;
+        const int jt = full ? it : it - nF;
+        return ents[(full ? e0 : m) + jt % n];
+    };
+    auto head_of = [&](int it) {
+        const bool full = it < nF;
+        const int n = full ? m - e0 : e1 - m;
+        return hk * group + (full ? it : it - nF) / n;
+    };
+    auto load = [&](int it, int ent, unsigned char* st) {
+        ld.load(st, p, b, head_of(it), ent & 0x7fffffff, wave, lane);
+    };
+
+    // S = Q K^T and dP - Delta = dO V^T - Delta for the 32-row half mt of the
+    // tile in stage `st`; the dP accumulators start from -Delta of their rows
+    // (element r is query row 32*mt + 8*(r/4) + 4*g + r%4).
+    auto s_half = [&](const unsigned char* st, int mt, f32x16_t& sacc, f32x16_t& pacc) {
+        const float* nd = (const float*)(st + C::OFF_ND);
+        sacc = (f32x16_t){};
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                *(u32x4_t*)(sQ + row_off<C::KCH>(4 * m + rr, ch)) = T.q[rr];
-                *(u32x4_t*)(sDO + row_off<C::KCH>(4 * m + rr, ch)) = T.o[rr];
-            }
+        for (int rg = 0; rg < 4; ++rg) {
+            const f32x4_t x = *(const f32x4_t*)(nd + 32 * mt + 8 * rg + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pacc[4 * rg + i] = x[i];
         }
-        if (tid < C::BQ) {
-            sL[tid] = T.l2;
-            sD[tid] = T.dl;
-            sA[tid] = T.a;
-            sB[tid] = T.b;
+        // the operands of step ks+1 are read while step ks runs
+        u32x4_t qa[2], oa[2];
+        qa[0] = *(const u32x4_t*)(st + C::OFF_Q + nat[0] + mt * 32 * C::ROWB);
+        oa[0] = *(const u32x4_t*)(st + C::OFF_DO + nat[0] + mt * 32 * C::ROWB);
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+            if (ks + 1 < C::NKS) {
+                qa[(ks + 1) & 1] = *(const u32x4_t*)(st + C::OFF_Q + nat[ks + 1] + mt * 32 * C::ROWB);
+                oa[(ks + 1) & 1] = *(const u32x4_t*)(st + C::OFF_DO + nat[ks + 1] + mt * 32 * C::ROWB);
+            }
+            sacc = mfma_32x32x16(qa[ks & 1], kreg[ks], sacc);
+            pacc = mfma_32x32x16(oa[ks & 1], vreg[ks], pacc);
         }
     };
 
-    // Loop schedule (two barriers per query tile):
-    //   barrier A: tile `it` is in sQ/sDO
-    //   issue global loads of tile it+1 into registers
-    //   S, dP, P, dS, dV, dK
-    //   barrier B: every wave is done with sQ/sDO
-    //   store tile it+1 into sQ/sDO
-    BwdTileRegs<DH> R;
-    if (n_iter > 0) {
-        bwd_load_tile<DH>(R, p, b, hk * group, ents[e0] & 0x7fffffff, tid);
-        store_tile(R);
-    }
-    for (int it = 0; it < n_iter; ++it) {
-        const int h = hk * group + it / n_ent;
-        const int ent = ents[e0 + it % n_ent];
-        const int qt = ent & 0x7fffffff;
-        const bool partial = ent < 0;
-        // Keep the dK/dV accumulators in AGPRs across iterations (the MFMAs
-        // accumulate there directly; no VALU touches them inside the loop).
+    // P = exp2(S * scale * log2(e) - lse2) and dS = P (dP - Delta) of half mt,
+    // packed to bf16 as the B operands of dV^T and dK^T for the query blocks
+    // kk = 2*mt and 2*mt + 1.
+    auto p_half = [&](const unsigned char* st, int mt, auto partial_tag, const f32x16_t& sacc,
+                      const f32x16_t& pacc, u32x4_t (&pb)[2], u32x4_t (&db)[2]) {
+        constexpr bool PARTIAL = decltype(partial_tag)::value;
+        const float* L2 = (const float*)(st + C::OFF_L);
+        const int32_t* R = (const int32_t*)(st + C::OFF_RNG);
 #pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt) asm volatile("" : "+a"(dk_acc[dt]), "+a"(dv_acc[dt]));
+        for (int rg = 0; rg < 4; ++rg) {
+            const int r0 = 32 * mt + 8 * rg + 4 * g;
+            const f32x4_t L = *(const f32x4_t*)(L2 + r0);
+            float pr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(sacc[4 * rg + i], c2, -L[i]));
+            if (PARTIAL) {  // keys outside a row's interval [a, b) are invisible
+                const int4 ab0 = *(const int4*)(R + 2 * r0);
+                const int4 ab1 = *(const int4*)(R + 2 * r0 + 4);
+                const int av[4] = {ab0.x, ab0.z, ab1.x, ab1.z};
+                const int bv[4] = {ab0.y, ab0.w, ab1.y, ab1.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pr[i] = ((key >= av[i]) & (key < bv[i])) ? pr[i] : 0.f;
+            }
+            float ds[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ds[i] = pr[i] * pacc[4 * rg + i];
+            const int kk = rg >> 1, w = (rg & 1) * 2;
+            pb[kk][w] = pack_bf16x2(pr[0], pr[1]);
+            pb[kk][w + 1] = pack_bf16x2(pr[2], pr[3]);
+            db[kk][w] = pack_bf16x2(ds[0], ds[1]);
+            db[kk][w + 1] = pack_bf16x2(ds[2], ds[3]);
+        }
+    };
 
-        __syncthreads();  // barrier A
-        const bool has_next = it + 1 < n_iter;
-        if (has_next)
-            bwd_load_tile<DH>(R, p, b, hk * group + (it + 1) / n_ent,
-                              ents[e0 + (it + 1) % n_ent] & 0x7fffffff, tid);
-
-        // S = Q K^T and dP = dO V^T: two 32-row halves of the 64-row tile; the
-        // B operands are this lane's K and V rows (key 32*wave + l32).
-        f32x16_t sacc[2], pacc[2];
+    // dV^T += dO^T P and dK^T += Q^T dS over the query rows of half mt; the K
+    // dimension of query block kk takes rows 16kk + 4g + 0..3 and
+    // 16kk + 8 + 4g + 0..3.
+    auto d_half = [&](const unsigned char* st, int mt, const u32x4_t (&pb)[2],
+                      const u32x4_t (&db)[2]) {
+        // the operands of head-dim block dt+1 are read while block dt runs
+        u32x4_t oa[2][2], qa[2][2];
+        auto read = [&](int dt, u32x4_t (&o)[2], u32x4_t (&q)[2]) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            sacc[mt] = (f32x16_t){};
-            pacc[mt] = (f32x16_t){};
-        }
-#pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) {
-            const u32x4_t kb4 = *(const u32x4_t*)(sK + nat[ks] + wave * 32 * C::ROWB);
-            const u32x4_t vb4 = *(const u32x4_t*)(sV + nat[ks] + wave * 32 * C::ROWB);
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const u32x4_t qa = *(const u32x4_t*)(sQ + nat[ks] + mt * 32 * C::ROWB);
-                const u32x4_t oa = *(const u32x4_t*)(sDO + nat[ks] + mt * 32 * C::ROWB);
-                sacc[mt] = mfma_32x32x16(qa, kb4, sacc[mt]);
-                pacc[mt] = mfma_32x32x16(oa, vb4, pacc[mt]);
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int o16 = (2 * mt + k2) * 16 * C::ROWB;
+                const u32x2_t o1 = lds_tr16(st + C::OFF_DO + trq[0][dt] + o16);
+                const u32x2_t o2 = lds_tr16(st + C::OFF_DO + trq[1][dt] + o16);
+                const u32x2_t q1 = lds_tr16(st + C::OFF_Q + trq[0][dt] + o16);
+                const u32x2_t q2 = lds_tr16(st + C::OFF_Q + trq[1][dt] + o16);
+                o[k2] = (u32x4_t){o1[0], o1[1], o2[0], o2[1]};
+                q[k2] = (u32x4_t){q1[0], q1[1], q2[0], q2[1]};
             }
-        }
-        // P (in sacc) and dS (in pacc); element (mt, r) is query row
-        // 32*mt + 8*(r/4) + 4*g + r%4.
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const f32x4_t L = *(const f32x4_t*)(sL + 32 * mt + 8 * rg + 4 * g);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sacc[mt][4 * rg + i] = fast_exp2(fmaf(sacc[mt][4 * rg + i], c2, -L[i]));
-            }
-        if (partial) {  // keys outside a row's interval [a, b) are invisible
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int rg = 0; rg < 4; ++rg) {
-                    const int r0 = 32 * mt + 8 * rg + 4 * g;
-                    const int4 A4 = *(const int4*)(sA + r0);
-                    const int4 B4 = *(const int4*)(sB + r0);
-                    const int av[4] = {A4.x, A4.y, A4.z, A4.w}, bv[4] = {B4.x, B4.y, B4.z, B4.w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const bool vis = (key >= av[i]) & (key < bv[i]);
-                        sacc[mt][4 * rg + i] = vis ? sacc[mt][4 * rg + i] : 0.f;
-                    }
-                }
-        }
-        u32x4_t pb[4], db[4];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int r0 = 32 * mt + 8 * rg + 4 * g;
-                const f32x4_t Dl = *(const f32x4_t*)(sD + r0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    pacc[mt][4 * rg + i] = sacc[mt][4 * rg + i] * (pacc[mt][4 * rg + i] - Dl[i]);
-                const int kk = 2 * mt + (rg >> 1), w = (rg & 1) * 2;
-                pb[kk][w] = pack_bf16x2(sacc[mt][4 * rg], sacc[mt][4 * rg + 1]);
-                pb[kk][w + 1] = pack_bf16x2(sacc[mt][4 * rg + 2], sacc[mt][4 * rg + 3]);
-                db[kk][w] = pack_bf16x2(pacc[mt][4 * rg], pacc[mt][4 * rg + 1]);
-                db[kk][w + 1] = pack_bf16x2(pacc[mt][4 * rg + 2], pacc[mt][4 * rg + 3]);
-            }
-        // dV^T += dO^T P and dK^T += Q^T dS; the K dimension (queries) of step
-        // kk takes rows 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3.
+        };
+        read(0, oa[0], qa[0]);
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt) {
-            u32x4_t oa[4], qa[4];
+            if (dt + 1 < C::NDT) read(dt + 1, oa[(dt + 1) & 1], qa[(dt + 1) & 1]);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int o16 = kk * 16 * C::ROWB;
-                const u32x2_t o1 = lds_tr16(sDO + trq[0][dt] + o16), o2 = lds_tr16(sDO + trq[1][dt] + o16);
-                const u32x2_t q1 = lds_tr16(sQ + trq[0][dt] + o16), q2 = lds_tr16(sQ + trq[1][dt] + o16);
-                oa[kk] = (u32x4_t){o1[0], o1[1], o2[0], o2[1]};
-                qa[kk] = (u32x4_t){q1[0], q1[1], q2[0], q2[1]};
-            }
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                dv_acc[dt] = mfma_32x32x16(oa[kk], pb[kk], dv_acc[dt]);
-                dk_acc[dt] = mfma_32x32x16(qa[kk], db[kk], dk_acc[dt]);
+            for (int k2 = 0; k2 < 2; ++k2) {
+                dv_acc[dt] = mfma_32x32x16(oa[dt & 1][k2], pb[k2], dv_acc[dt]);
+                dk_acc[dt] = mfma_32x32x16(qa[dt & 1][k2], db[k2], dk_acc[dt]);
             }
         }
-        __syncthreads();  // barrier B
-        if (has_next) store_tile(R);
+    };
+
+    // One query tile, pipelined in halves: S/dP of half 1 run on the matrix
+    // cores while P/dS of half 0 run on the vector ALUs, then dV/dK of half 0
+    // while P/dS of half 1.
+    auto tile = [&](const unsigned char* st, auto partial_tag) {
+        f32x16_t s0, p0, s1, p1;
+        u32x4_t pb0[2], db0[2], pb1[2], db1[2];
+        // the scheduling fences keep each slice's operand reads inside it,
+        // which bounds the registers in flight
+        s_half(st, 0, s0, p0);
+        __builtin_amdgcn_sched_barrier(0);
+        s_half(st, 1, s1, p1);
+        p_half(st, 0, partial_tag, s0, p0, pb0, db0);
+        __builtin_amdgcn_sched_barrier(0);
+        d_half(st, 0, pb0, db0);
+        p_half(st, 1, partial_tag, s1, p1, pb1, db1);
+        __builtin_amdgcn_sched_barrier(0);
+        d_half(st, 1, pb1, db1);
+    };
+
+    // Two LDS stages: the barrier at the top of iteration `it` makes tile it
+    // visible and frees the stage of tile it-1, which then receives tile it+1.
+    // Even iterations use stage A, odd ones stage B.
+    int ent_nx = n_iter > 1 ? entry_of(1) : 0;   // entry of tile it+1
+    auto step = [&](int it, unsigned char* cur, unsigned char* nxt, auto partial_tag) {
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) asm volatile("" : "+a"(dk_acc[dt]), "+a"(dv_acc[dt]));
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile it have landed
+        __syncthreads();
+        const int ent = ent_nx;
+        if (it + 1 < n_iter) load(it + 1, ent, nxt);
+        if (it + 2 < n_iter) ent_nx = entry_of(it + 2);
+        tile(cur, partial_tag);
+    };
+    // The unmasked loop covers an even number of iterations; a last full tile
+    // left over goes through the masked loop, where the mask keeps every key.
+    const int nF2 = nF & ~1;
+    if (n_iter > 0) load(0, entry_of(0), stA);
+    int it = 0;
+    for (; it < nF2; it += 2) {
+        step(it, stA, stB, std::false_type{});
+        step(it + 1, stB, stA, std::false_type{});
+    }
+    for (; it < n_iter; it += 2) {
+        step(it, stA, stB, std::true_type{});
+        if (it + 1 < n_iter) step(it + 1, stB, stA, std::true_type{});
     }
 
     // dK_j += scale * dK^T acc, dV_j += dV^T acc (this lane's key, 64 head-dim values)
@@ -372,37 +420,61 @@ struct DqCfg {
     static constexpr int KCH = DH / 8;
     static constexpr int K_BYTES = BK * ROWB;
     static constexpr int STAGE = 2 * K_BYTES;        // K and V tiles, natural rows
-    static constexpr int LDS = 2 * STAGE;
     static constexpr int KLD = BK * KCH / NT;        // 16-byte chunks per thread per tensor
     static_assert(KLD >= 1, "tile shape");
 };
 
-// One 64-key tile of K or V straight from global memory into LDS
-// (global_load_lds_dwordx4: the 16 bytes of lane l land at the wave-uniform
-// LDS base + 16*l).  Instruction c of wave w fills LDS chunks 256c + 64w +
-// lane, so the lane whose slot is physical chunk p of row r loads logical
-// chunk p ^ swizzle(r).
+// K and V tiles of 64 keys through buffer loads into LDS (the 16 bytes of
+// lane l land at the wave-uniform LDS base + 16*l).  The buffers span the
+// Skv rows of the batch entry, so keys past Skv read as zeros; the per-lane
+// part of each offset (row and XOR-swizzled source chunk) is fixed and a tile
+// moves only the scalar offset.
 template <int DH>
-__device__ __forceinline__ void dq_load_lds(unsigned char* stage, const uint16_t* base,
-                                            int kv_stride, int kt, int Skv, int wave, int lane) {
+struct DqLoader {
     using C = DqCfg<DH>;
+    __amdgpu_buffer_rsrc_t rk, rv;
+    int voff[C::KLD];
+    int row_stride;   // bytes per key row (all kv heads)
+    int head_off;     // bytes to this kv head
+
+    __device__ __forceinline__ void init(const DqArgs& p, int b, int hk, int wave, int lane) {
+        const int kv_stride = p.Hkv * DH;
+        row_stride = kv_stride * 2;
+        head_off = hk * DH * 2;
+        const int bytes = p.Skv * row_stride;   // < 2^32: the ABI bounds Skv * Hkv * d
+        rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + (int64_t)b * p.Skv * kv_stride), (short)0,
+                                               bytes, 0x00020000);
+        rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (int64_t)b * p.Skv * kv_stride), (short)0,
+                                               bytes, 0x00020000);
 #pragma unroll
-    for (int c = 0; c < C::KLD; ++c) {
-        const int idx = C::NT * c + 64 * wave + lane;
-        const int row = idx / C::KCH, pc = idx % C::KCH;
-        const int lc = slot<C::KCH>(row, pc);  // XOR swizzle: its own inverse
-        const int key = min(kt * C::BK + row, Skv - 1);
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(base + (key * kv_stride + lc * 8)),
-            (__attribute__((address_space(3))) void*)(stage + (C::NT * c + 64 * wave) * 16), 16,
-            0, 0);
+        for (int c = 0; c < C::KLD; ++c) {
+            const int idx = C::NT * c + 64 * wave + lane;
+            const int row = idx / C::KCH, pc = idx % C::KCH;
+            voff[c] = row * row_stride + slot<C::KCH>(row, pc) * 16;
+        }
     }
-}
+
+    __device__ __forceinline__ void load(unsigned char* stage, int kt, int wave) const {
+        const int soff = kt * C::BK * row_stride + head_off;
+#pragma unroll
+        for (int c = 0; c < C::KLD; ++c) {
+            const int dst = (C::NT * c + 64 * wave) * 16;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rk, (__attribute__((address_space(3))) void*)(stage + dst), 16, voff[c], soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rv, (__attribute__((address_space(3))) void*)(stage + C::K_BYTES + dst), 16, voff[c],
+                soff, 0, 0);
+        }
+    }
+};
 
 template <int DH>
-__global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(DqArgs p) {
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_bf16_kernel(DqArgs p) {
     using C = DqCfg<DH>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
+    // two stages as separate objects, named statically below (see the dK/dV
+    // kernel: the transpose reads then need not wait for the loads in flight)
+    __shared__ __attribute__((aligned(16))) unsigned char stA[C::STAGE];
+    __shared__ __attribute__((aligned(16))) unsigned char stB[C::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
@@ -414,10 +486,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(DqArgs p) {
     const int hk = (h * p.Hkv) / p.Hq;
     const cint_ptr ents = as_const(p.t_ent);
     const int e0 = as_const(p.t_off)[qt], e1 = as_const(p.t_off)[qt + 1];
+    const int m = as_const(p.t_mid)[qt];   // FULL tiles in [e0, m), PARTIAL in [m, e1)
 
     const int iq = qt * C::BQ + wave * 32 + l32;  // this lane's query row
     const int iqc = min(iq, p.S - 1);
-    const bool valid = iq < p.S;
     const int q_stride = p.Hq * DH;
     const uint16_t* qrow = p.q + ((int64_t)b * p.S + iqc) * q_stride + h * DH;
     const uint16_t* orow = p.dout + ((int64_t)b * p.S + iqc) * q_stride + h * DH;
@@ -427,14 +499,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(DqArgs p) {
         qreg[ks] = *(const u32x4_t*)(qrow + 16 * ks + 8 * g);
         oreg[ks] = *(const u32x4_t*)(orow + 16 * ks + 8 * g);
     }
-    const float Lraw = p.lse[((int64_t)b * p.Hq + h) * p.S + iqc];
-    const float L2 = (!valid || Lraw == -INFINITY) ? INFINITY : Lraw * kLog2e;
-    const float Dl = valid ? p.delta[((int64_t)b * p.Hq + h) * p.S_pad + iqc] : 0.f;
+    const float L2 = p.lse2[((int64_t)b * p.Hq + h) * p.S_pad + iq];   // +inf on padding rows
+    const float nD = p.ndelta[((int64_t)b * p.Hq + h) * p.S_pad + iq];
     const int ra = p.rng[2 * iq], rb = p.rng[2 * iq + 1];
 
-    const int kv_stride = p.Hkv * DH;
-    const uint16_t* kb = p.k + (int64_t)b * p.Skv * kv_stride + hk * DH;
-    const uint16_t* vb = p.v + (int64_t)b * p.Skv * kv_stride + hk * DH;
+    DqLoader<DH> ld;
+    ld.init(p, b, hk, wave, lane);
 
     // per-lane LDS offsets (see the dK/dV kernel)
     const int j = lane & 15, gsel = (lane >> 4) & 1;
@@ -455,94 +525,106 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(DqArgs p) {
     for (int dt = 0; dt < C::NDT; ++dt) acc[dt] = (f32x16_t){};
     const float c2 = p.scale_log2;
 
-    if (e0 < e1) {
-        dq_load_lds<DH>(smem, kb, kv_stride, ents[e0] & 0x7fffffff, p.Skv, wave, lane);
-        dq_load_lds<DH>(smem + C::K_BYTES, vb, kv_stride, ents[e0] & 0x7fffffff, p.Skv, wave, lane);
-        for (int e = e0; e < e1; ++e) {
+    // One key tile: S^T = K Q^T and dP^T = V dO^T (two 32-key halves), then
+    // P = exp(scale*S - lse), dS = P (dP - Delta) (element (mt, r) is key
+    // 32*mt + 8*(r/4) + 4*g + r%4 of the tile), then dQ^T += K^T dS^T.
+    auto tile = [&](const unsigned char* Ks, int kt, auto partial_tag) {
+        constexpr bool PARTIAL = decltype(partial_tag)::value;
+        const unsigned char* Vs = Ks + C::K_BYTES;
+        f32x16_t sacc[2], pacc[2];
 #pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt) asm volatile("" : "+a"(acc[dt]));
-            unsigned char* stage = smem + ((e - e0) & 1) * C::STAGE;
-            __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS loads have landed
-            __syncthreads();  // tile e is in LDS; the other stage is free
-            if (e + 1 < e1) {
-                unsigned char* nxt = smem + (((e - e0) & 1) ^ 1) * C::STAGE;
-                const int ktn = ents[e + 1] & 0x7fffffff;
-                dq_load_lds<DH>(nxt, kb, kv_stride, ktn, p.Skv, wave, lane);
-                dq_load_lds<DH>(nxt + C::K_BYTES, vb, kv_stride, ktn, p.Skv, wave, lane);
-            }
-            const int ent = ents[e];
-            const int kt = ent & 0x7fffffff;
-            const unsigned char* Ks = stage;
-            const unsigned char* Vs = stage + C::K_BYTES;
-
-            // S^T = K Q^T and dP^T = V dO^T for the 64 keys (two 32-key halves);
-            // the operands of step ks+1 are read while step ks runs
-            f32x16_t sacc[2], pacc[2];
+        for (int mt = 0; mt < 2; ++mt) {
+            sacc[mt] = (f32x16_t){};
+            pacc[mt] = (f32x16_t){};
+        }
+        // the operands of step ks+1 are read while step ks runs
+        u32x4_t ka[2][2], va[2][2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                sacc[mt] = (f32x16_t){};
-                pacc[mt] = (f32x16_t){};
-            }
-            u32x4_t ka[2][2], va[2][2];
+        for (int mt = 0; mt < 2; ++mt) {
+            ka[0][mt] = *(const u32x4_t*)(Ks + nat[0] + mt * 32 * C::ROWB);
+            va[0][mt] = *(const u32x4_t*)(Vs + nat[0] + mt * 32 * C::ROWB);
+        }
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                ka[0][mt] = *(const u32x4_t*)(Ks + nat[0] + mt * 32 * C::ROWB);
-                va[0][mt] = *(const u32x4_t*)(Vs + nat[0] + mt * 32 * C::ROWB);
-            }
-#pragma unroll
-            for (int ks = 0; ks < C::NKS; ++ks) {
-                if (ks + 1 < C::NKS)
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt) {
-                        ka[(ks + 1) & 1][mt] = *(const u32x4_t*)(Ks + nat[ks + 1] + mt * 32 * C::ROWB);
-                        va[(ks + 1) & 1][mt] = *(const u32x4_t*)(Vs + nat[ks + 1] + mt * 32 * C::ROWB);
-                    }
+        for (int ks = 0; ks < C::NKS; ++ks) {
+            if (ks + 1 < C::NKS)
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {
-                    sacc[mt] = mfma_32x32x16(ka[ks & 1][mt], qreg[ks], sacc[mt]);
-                    pacc[mt] = mfma_32x32x16(va[ks & 1][mt], oreg[ks], pacc[mt]);
+                    ka[(ks + 1) & 1][mt] = *(const u32x4_t*)(Ks + nat[ks + 1] + mt * 32 * C::ROWB);
+                    va[(ks + 1) & 1][mt] = *(const u32x4_t*)(Vs + nat[ks + 1] + mt * 32 * C::ROWB);
                 }
-            }
-            // P = exp(scale*S - lse) and dS = P (dP - Delta); element (mt, r) is key
-            // 32*mt + 8*(r/4) + 4*g + r%4 of the tile.
-            u32x4_t db[4];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    float pv[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        float pr = fast_exp2(fmaf(sacc[mt][r + u], c2, -L2));
-                        if (ent < 0) {
-                            const int key = kt * C::BK + 32 * mt + 8 * ((r + u) >> 2) + 4 * g + ((r + u) & 3);
-                            pr = ((key >= ra) & (key < rb)) ? pr : 0.f;
-                        }
-                        pv[u] = pr * (pacc[mt][r + u] - Dl);
-                    }
-                    db[2 * mt + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(pv[0], pv[1]);
-                }
-            // dQ^T += K^T dS^T; the K dimension (keys) of step kk takes rows
-            // 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3, as dS is held.  The K^T
-            // operands of step kk+1 are read while step kk runs.
-            u32x4_t kt4[2][C::NDT];
-            auto read_kt = [&](u32x4_t (&dst)[C::NDT], int kk) {
-#pragma unroll
-                for (int dt = 0; dt < C::NDT; ++dt) {
-                    const u32x2_t a1 = lds_tr16(Ks + trk[0][dt] + kk * 16 * C::ROWB);
-                    const u32x2_t a2 = lds_tr16(Ks + trk[1][dt] + kk * 16 * C::ROWB);
-                    dst[dt] = (u32x4_t){a1[0], a1[1], a2[0], a2[1]};
-                }
-            };
-            read_kt(kt4[0], 0);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                if (kk + 1 < 4) read_kt(kt4[(kk + 1) & 1], kk + 1);
-#pragma unroll
-                for (int dt = 0; dt < C::NDT; ++dt)
-                    acc[dt] = mfma_32x32x16(kt4[kk & 1][dt], db[kk], acc[dt]);
+            for (int mt = 0; mt < 2; ++mt) {
+                sacc[mt] = mfma_32x32x16(ka[ks & 1][mt], qreg[ks], sacc[mt]);
+                pacc[mt] = mfma_32x32x16(va[ks & 1][mt], oreg[ks], pacc[mt]);
             }
         }
+        u32x4_t db[4];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                float pv[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    float pr = fast_exp2(fmaf(sacc[mt][r + u], c2, -L2));
+                    if (PARTIAL) {  // keys outside [ra, rb) are invisible
+                        const int key = kt * C::BK + 32 * mt + 8 * ((r + u) >> 2) + 4 * g + ((r + u) & 3);
+                        pr = ((key >= ra) & (key < rb)) ? pr : 0.f;
+                    }
+                    pv[u] = pr * (pacc[mt][r + u] + nD);
+                }
+                db[2 * mt + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(pv[0], pv[1]);
+            }
+        // dQ^T += K^T dS^T; the K dimension (keys) of step kk takes rows
+        // 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3, as dS is held.  The K^T
+        // operands of step kk+1 are read while step kk runs.
+        u32x4_t kt4[2][C::NDT];
+        auto read_kt = [&](u32x4_t (&dst)[C::NDT], int kk) {
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) {
+                const u32x2_t a1 = lds_tr16(Ks + trk[0][dt] + kk * 16 * C::ROWB);
+                const u32x2_t a2 = lds_tr16(Ks + trk[1][dt] + kk * 16 * C::ROWB);
+                dst[dt] = (u32x4_t){a1[0], a1[1], a2[0], a2[1]};
+            }
+        };
+        read_kt(kt4[0], 0);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (kk + 1 < 4) read_kt(kt4[(kk + 1) & 1], kk + 1);
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+                acc[dt] = mfma_32x32x16(kt4[kk & 1][dt], db[kk], acc[dt]);
+        }
+    };
+
+    // Two LDS stages, even list positions in stage A: the barrier at the top
+    // of position e makes tile e visible and frees the other stage, which
+    // then receives tile e+1.  The entry of tile e+1 is fetched a position
+    // ahead.  Full tiles run unmasked in pairs; a last odd full tile joins the
+    // masked loop (its mask keeps every key).
+    const int n = e1 - e0;
+    const int nF2 = (m - e0) & ~1;
+    int ent_nx = n > 1 ? ents[e0 + 1] : 0;
+    auto step = [&](int i, const unsigned char* cur, unsigned char* nxt, auto partial_tag) {
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) asm volatile("" : "+a"(acc[dt]));
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile i have landed
+        __syncthreads();
+        const int ent = ents[e0 + i];
+        const int enx = ent_nx;
+        if (i + 2 < n) ent_nx = ents[e0 + i + 2];
+        if (i + 1 < n) ld.load(nxt, enx & 0x7fffffff, wave);
+        tile(cur, ent & 0x7fffffff, partial_tag);
+    };
+    if (n > 0) ld.load(stA, ents[e0] & 0x7fffffff, wave);
+    int i = 0;
+    for (; i < nF2; i += 2) {
+        step(i, stA, stB, std::false_type{});
+        step(i + 1, stB, stA, std::false_type{});
+    }
+    for (; i < n; i += 2) {
+        step(i, stA, stB, std::true_type{});
+        if (i + 1 < n) step(i + 1, stB, stA, std::true_type{});
     }
 
     // dq_acc (+)= scale * acc in the accumulator layout: element (dt, r) of this

@@ -3,7 +3,8 @@
 //                     result (instagit/nanotron page, "Numerically-Stable
 //                     Output Fusion"), one pass over fp32 rows;
 //   K5 finalize    -- running fp32 output -> output dtype;
-//   K3 bwd_pre     -- Delta = rowsum(dout * out) for the backward;
+//   K3 bwd_pre     -- per-row values of the backward: -Delta = -rowsum(dout *
+//                     out) and the lse in base 2;
 //   dq_finalize    -- the dQ accumulator (kept in the MFMA accumulator layout of
 //                     the dQ kernel: per 32-row group of one head,
 //                     [d/32][4][64 lanes][4] floats) -> the caller's dq
@@ -94,25 +95,33 @@ hipError_t launch_finalize(const float* o, void* out, int is_bf16, int64_t n, hi
     return hipGetLastError();
 }
 
-// K3: one group of d/8 lanes per (b, s, h) row; each lane reads 8 elements.
+// K3: one group of d/8 lanes per padded row (b, s, h), rows ordered
+// [B][S_pad][Hq]; each lane reads 8 elements of dout and of out.  Writes
+// -Delta = -rowsum(dout * out) and lse2 = lse * log2(e) (+inf where lse is
+// -inf, i.e. the row sees no key), and 0 / +inf on the padding rows s >= S,
+// so that the backward kernels need no per-row special cases.
 template <bool BF16>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs a) {
     const int lanes_per_row = a.d / 8;
     const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t row = gt / lanes_per_row;
     const int c = (int)(gt % lanes_per_row);
-    const int64_t rows = (int64_t)a.B * a.S * a.Hq;
+    const int64_t rows = (int64_t)a.B * a.S_pad * a.Hq;
+    const int64_t h = row % a.Hq, bs = row / a.Hq;
+    const int64_t b = bs / a.S_pad, s = bs % a.S_pad;
+    const bool live = row < rows && s < a.S;
     float sum = 0.f;
-    if (row < rows) {
+    if (live) {
+        const int64_t src = ((b * a.S + s) * a.Hq + h) * lanes_per_row + c;
         if (BF16) {
-            const u32x4_t x = *((const u32x4_t*)a.dout + gt);
-            const u32x4_t y = *((const u32x4_t*)a.out + gt);
+            const u32x4_t x = *((const u32x4_t*)a.dout + src);
+            const u32x4_t y = *((const u32x4_t*)a.out + src);
 #pragma unroll
             for (int w = 0; w < 4; ++w)
                 sum += bf16_lo(x[w]) * bf16_lo(y[w]) + bf16_hi(x[w]) * bf16_hi(y[w]);
         } else {
-            const f32x4_t* xp = (const f32x4_t*)a.dout + 2 * gt;
-            const f32x4_t* yp = (const f32x4_t*)a.out + 2 * gt;
+            const f32x4_t* xp = (const f32x4_t*)a.dout + 2 * src;
+            const f32x4_t* yp = (const f32x4_t*)a.out + 2 * src;
 #pragma unroll
             for (int w = 0; w < 2; ++w) {
                 const f32x4_t x = xp[w], y = yp[w];
@@ -122,9 +131,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs a) {
     }
     for (int off = lanes_per_row / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
     if (row < rows && c == 0) {
-        const int64_t h = row % a.Hq, bs = row / a.Hq;
-        const int64_t b = bs / a.S, s = bs % a.S;
-        a.delta[(b * a.Hq + h) * a.S_pad + s] = sum;
+        const int64_t dst = (b * a.Hq + h) * a.S_pad + s;
+        float l2 = INFINITY;
+        if (live) {
+            const float L = a.lse[(b * a.Hq + h) * a.S + s];
+            l2 = L == -INFINITY ? INFINITY : L * kLog2e;
+        }
+        a.ndelta[dst] = -sum;
+        a.lse2[dst] = l2;
     }
 }
 
@@ -158,7 +172,7 @@ hipError_t launch_dq_finalize(const float* dq_acc, float* dq, int32_t B, int32_t
 }
 
 hipError_t launch_bwd_pre(const BwdPreArgs& a, int is_bf16, hipStream_t s) {
-    const int64_t threads = (int64_t)a.B * a.S * a.Hq * (a.d / 8);
+    const int64_t threads = (int64_t)a.B * a.S_pad * a.Hq * (a.d / 8);
     if (threads == 0) return hipSuccess;
     const unsigned grid = (unsigned)((threads + 255) / 256);
     if (is_bf16)

@@ -28,6 +28,7 @@ struct FwdArgs {
     const void* v;
     const int32_t* rng;     // [S_pad][2] visible local key interval [a, b) per query row
     const int32_t* t_off;   // [nqt + 1] tile-list offsets per query tile
+    const int32_t* t_mid;   // [nqt] first PARTIAL entry of each list (FULL ones before it)
     const int32_t* t_ent;   // key tile index | (partial << 31)
     const int32_t* t_order; // [nqt] query tiles, heaviest first
     float* o_run;           // running fp32 output (layout private to the kernel family)
@@ -46,10 +47,11 @@ struct BwdArgs {
     const uint16_t* k;      // block j: [B, Skv, Hkv, d]
     const uint16_t* v;
     const uint16_t* dout;   // [B, S, Hq, d]
-    const float* lse;       // [B, Hq, S]
-    const float* delta;     // [B, Hq, S_pad] rowsum(dout * out)
+    const float* lse2;      // [B, Hq, S_pad] lse * log2(e); +inf for rows that see nothing
+    const float* ndelta;    // [B, Hq, S_pad] -rowsum(dout * out); 0 on padding rows
     const int32_t* rng;     // [S_pad][2]
     const int32_t* t_off;   // [nkt + 1] query-tile lists per key tile
+    const int32_t* t_mid;   // [nkt] first PARTIAL entry of each list
     const int32_t* t_ent;   // query tile index | (partial << 31)
     const int32_t* t_order; // [nkt] key tiles, heaviest first
     float* dk;              // block j: [B, Skv, Hkv, d] fp32, +=
@@ -66,10 +68,11 @@ struct DqArgs {
     const uint16_t* k;      // block j: [B, Skv, Hkv, d]
     const uint16_t* v;
     const uint16_t* dout;   // [B, S, Hq, d]
-    const float* lse;       // [B, Hq, S]
-    const float* delta;     // [B, Hq, S_pad]
+    const float* lse2;      // [B, Hq, S_pad] as in BwdArgs
+    const float* ndelta;    // [B, Hq, S_pad]
     const int32_t* rng;     // [S_pad][2]
     const int32_t* t_off;   // [nqt + 1] key-tile lists per query tile
+    const int32_t* t_mid;   // [nqt] first PARTIAL entry of each list
     const int32_t* t_ent;   // key tile index | (partial << 31)
     const int32_t* t_order; // [nqt] query tiles, heaviest first
     float* dq_acc;          // fp32 accumulator in the forward's running-output layout
@@ -80,10 +83,13 @@ struct DqArgs {
     float scale_log2;
 };
 
+// Per-row values of the backward, over the padded rows [B, Hq, S_pad].
 struct BwdPreArgs {
     const void* dout;       // [B, S, Hq, d] input dtype
     const void* out;
-    float* delta;           // [B, Hq, S_pad]
+    const float* lse;       // [B, Hq, S]
+    float* lse2;            // [B, Hq, S_pad]
+    float* ndelta;          // [B, Hq, S_pad]
     int32_t B, S, Hq, S_pad, d;
 };
 

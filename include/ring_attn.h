@@ -125,8 +125,10 @@ typedef struct ring_attn_desc {
 /* Bytes of device workspace ring_attn_fwd (is_bwd = 0) or ring_attn_bwd
  * (is_bwd = 1) needs for this descriptor; negative RA_E_* if the descriptor is
  * invalid (cu_seqlens is not inspected).  Forward: the fp32 running output
- * (plus one partial in RA_MERGE_SEPARATE mode).  Backward: Delta and an fp32
- * dQ accumulator of B * Hq * S_pad * d floats (S_pad = S rounded up to 128). */
+ * (plus one partial in RA_MERGE_SEPARATE mode).  Backward: two per-row fp32
+ * arrays of B * Hq * S_pad floats (the lse in base 2 and -Delta, Delta =
+ * rowsum(dout * out)) and an fp32 dQ accumulator of B * Hq * S_pad * d floats
+ * (S_pad = S rounded up to 128; each part starts on a 256-byte boundary). */
 int64_t ring_attn_workspace_bytes(const ring_attn_desc* desc, int is_bwd);
 
 /* Forward of the rank share ("Forward Pass Implementation"): for s = 0..D-1

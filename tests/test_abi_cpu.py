@@ -171,7 +171,7 @@ def test_workspace_sizes():
     desc = ca.make_desc(1, 32, 32, 128, 32768, 8, 7, True, ca.BASIC)
     S_pad = 4096
     assert ca.ring_attn_workspace_bytes(desc, False) == 32 * S_pad * 128 * 4
-    assert ca.ring_attn_workspace_bytes(desc, True) == 32 * S_pad * 4 + 32 * S_pad * 128 * 4
+    assert ca.ring_attn_workspace_bytes(desc, True) == 2 * 32 * S_pad * 4 + 32 * S_pad * 128 * 4
     desc.merge_mode = ca.RA_MERGE_SEPARATE
     assert ca.ring_attn_workspace_bytes(desc, False) == 2 * 32 * 4096 * 128 * 4 + 32 * 4096 * 4
     desc.world = 0
