@@ -51,6 +51,12 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"linking failed:\n{res.stdout}\n{res.stderr}")
+    # every kernel launched from host code must have its launch stub in the
+    # library (a stub the host pass failed to emit only shows up at load time)
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "__device_stub__" in ln]
+    if nm.returncode != 0 or missing:
+        raise RuntimeError(f"library check failed: {nm.stderr.strip()} undefined kernel stubs {missing}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -50,24 +50,11 @@ struct BwdCfg {
     static constexpr int OFF_ND = OFF_L + BQ * 4;
     static constexpr int OFF_RNG = OFF_ND + BQ * 4;
     static constexpr int STAGE = OFF_RNG + BQ * 8;
-    static constexpr int QLD = Q_BYTES / 16 / NT;   // 16-byte chunks per thread per tensor
-    static_assert(QLD >= 1 && BQ * 16 == 1024, "tile shape");
+    static_assert(BQ * 16 == 1024, "row values: one 16-byte chunk per lane of a wave");
 };
 
-// 16-byte slot of logical chunk c in row r.  Rows of 16 chunks (256 B) and of
-// 8 chunks (128 B, two rows per bank cycle) have their own XOR patterns; both
-// keep 16 consecutive rows at one chunk, and 4 consecutive rows x 2 chunks,
-// free of bank conflicts.
 template <int NCH>
-__device__ __forceinline__ int slot(int r, int c) {
-    if (NCH == 16) return c ^ (((r & 7) << 1) | ((r >> 3) & 1));
-    return c ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
-}
-
-template <int NCH>
-__device__ __forceinline__ int row_off(int r, int c) {
-    return r * (NCH * 16) + (slot<NCH>(r, c) << 4);
-}
+__device__ __forceinline__ int row_off(int r, int c) { return swz_off<NCH>(r, c); }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
@@ -102,39 +89,18 @@ __device__ __forceinline__ u32x4_t tr_operand(const unsigned char* base, int r1,
 template <int DH>
 struct DkdvLoader {
     using C = BwdCfg<DH>;
-    __amdgpu_buffer_rsrc_t rq, ro;
-    int voff[C::QLD];
-    int row_stride;     // bytes per query row (all heads)
+    BufTileLoader<DH, C::BQ> lq, lo;
 
     __device__ __forceinline__ void init(const BwdArgs& p, int b, int wave, int lane) {
-        const int q_stride = p.Hq * DH;
-        row_stride = q_stride * 2;
-        const int bytes = p.S * row_stride;   // < 2^32: the ABI bounds S * Hq * d
-        rq = __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + (int64_t)b * p.S * q_stride), (short)0,
-                                               bytes, 0x00020000);
-        ro = __builtin_amdgcn_make_buffer_rsrc((void*)(p.dout + (int64_t)b * p.S * q_stride), (short)0,
-                                               bytes, 0x00020000);
-#pragma unroll
-        for (int c = 0; c < C::QLD; ++c) {
-            const int idx = C::NT * c + 64 * wave + lane;
-            const int row = idx / C::KCH, pc = idx % C::KCH;
-            voff[c] = row * row_stride + slot<C::KCH>(row, pc) * 16;
-        }
+        const int64_t batch = (int64_t)b * p.S * p.Hq * DH;
+        lq.init(p.q + batch, p.S, p.Hq, 0, wave, lane);
+        lo.init(p.dout + batch, p.S, p.Hq, 0, wave, lane);
     }
 
     __device__ __forceinline__ void load(unsigned char* stage, const BwdArgs& p, int b, int h,
                                          int qt, int wave, int lane) const {
-        const int soff = qt * C::BQ * row_stride + h * DH * 2;
-#pragma unroll
-        for (int c = 0; c < C::QLD; ++c) {
-            const int dst = (C::NT * c + 64 * wave) * 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rq, (__attribute__((address_space(3))) void*)(stage + C::OFF_Q + dst), 16, voff[c],
-                soff, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ro, (__attribute__((address_space(3))) void*)(stage + C::OFF_DO + dst), 16, voff[c],
-                soff, 0, 0);
-        }
+        lq.load(stage + C::OFF_Q, qt, wave, h);
+        lo.load(stage + C::OFF_DO, qt, wave, h);
         if (wave == 0) {
             const int64_t r0 = ((int64_t)b * p.Hq + h) * p.S_pad + qt * C::BQ;
             const void* src = lane < 16   ? (const void*)(p.lse2 + r0 + 4 * lane)
@@ -420,52 +386,6 @@ struct DqCfg {
     static constexpr int KCH = DH / 8;
     static constexpr int K_BYTES = BK * ROWB;
     static constexpr int STAGE = 2 * K_BYTES;        // K and V tiles, natural rows
-    static constexpr int KLD = BK * KCH / NT;        // 16-byte chunks per thread per tensor
-    static_assert(KLD >= 1, "tile shape");
-};
-
-// K and V tiles of 64 keys through buffer loads into LDS (the 16 bytes of
-// lane l land at the wave-uniform LDS base + 16*l).  The buffers span the
-// Skv rows of the batch entry, so keys past Skv read as zeros; the per-lane
-// part of each offset (row and XOR-swizzled source chunk) is fixed and a tile
-// moves only the scalar offset.
-template <int DH>
-struct DqLoader {
-    using C = DqCfg<DH>;
-    __amdgpu_buffer_rsrc_t rk, rv;
-    int voff[C::KLD];
-    int row_stride;   // bytes per key row (all kv heads)
-    int head_off;     // bytes to this kv head
-
-    __device__ __forceinline__ void init(const DqArgs& p, int b, int hk, int wave, int lane) {
-        const int kv_stride = p.Hkv * DH;
-        row_stride = kv_stride * 2;
-        head_off = hk * DH * 2;
-        const int bytes = p.Skv * row_stride;   // < 2^32: the ABI bounds Skv * Hkv * d
-        rk = __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + (int64_t)b * p.Skv * kv_stride), (short)0,
-                                               bytes, 0x00020000);
-        rv = __builtin_amdgcn_make_buffer_rsrc((void*)(p.v + (int64_t)b * p.Skv * kv_stride), (short)0,
-                                               bytes, 0x00020000);
-#pragma unroll
-        for (int c = 0; c < C::KLD; ++c) {
-            const int idx = C::NT * c + 64 * wave + lane;
-            const int row = idx / C::KCH, pc = idx % C::KCH;
-            voff[c] = row * row_stride + slot<C::KCH>(row, pc) * 16;
-        }
-    }
-
-    __device__ __forceinline__ void load(unsigned char* stage, int kt, int wave) const {
-        const int soff = kt * C::BK * row_stride + head_off;
-#pragma unroll
-        for (int c = 0; c < C::KLD; ++c) {
-            const int dst = (C::NT * c + 64 * wave) * 16;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rk, (__attribute__((address_space(3))) void*)(stage + dst), 16, voff[c], soff, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rv, (__attribute__((address_space(3))) void*)(stage + C::K_BYTES + dst), 16, voff[c],
-                soff, 0, 0);
-        }
-    }
 };
 
 template <int DH>
@@ -503,8 +423,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const float nD = p.ndelta[((int64_t)b * p.Hq + h) * p.S_pad + iq];
     const int ra = p.rng[2 * iq], rb = p.rng[2 * iq + 1];
 
-    DqLoader<DH> ld;
-    ld.init(p, b, hk, wave, lane);
+    KvLoader<DH, C::BK> ld;   // K and V tiles of 64 keys
+    ld.init(p.k, p.v, b, p.Skv, p.Hkv, hk, wave, lane);
 
     // per-lane LDS offsets (see the dK/dV kernel)
     const int j = lane & 15, gsel = (lane >> 4) & 1;
@@ -613,10 +533,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const int ent = ents[e0 + i];
         const int enx = ent_nx;
         if (i + 2 < n) ent_nx = ents[e0 + i + 2];
-        if (i + 1 < n) ld.load(nxt, enx & 0x7fffffff, wave);
+        if (i + 1 < n) ld.load(nxt, nxt + C::K_BYTES, enx & 0x7fffffff, wave);
         tile(cur, ent & 0x7fffffff, partial_tag);
     };
-    if (n > 0) ld.load(stA, ents[e0] & 0x7fffffff, wave);
+    if (n > 0) ld.load(stA, stA + C::K_BYTES, ents[e0] & 0x7fffffff, wave);
     int i = 0;
     for (; i < nF2; i += 2) {
         step(i, stA, stB, std::false_type{});

@@ -17,13 +17,17 @@
 //   {0-3, 8-11} (lanes 0-31) and {4-7, 12-15} (lanes 32-63) of every 16-key
 //   step; V^T comes from the gfx950 LDS transpose read ds_read_b64_tr_b16 on
 //   the natural V rows, picking the key rows in that same order.
-// K and V tiles are double-buffered in LDS in natural rows (global ->
-// registers -> LDS), XOR-swizzled so that 16-row operand reads and 4-row
-// transpose reads are free of bank conflicts.
+// K and V tiles are double-buffered in LDS in natural rows (buffer loads
+// straight into LDS), XOR-swizzled so that 16-row operand reads and 4-row
+// transpose reads are free of bank conflicts.  Each tile list holds its FULL
+// tiles before its PARTIAL ones, and the kernel runs an unmasked loop and then
+// a masked one.
 // The running max m only moves when a tile's max exceeds it by more than 8
 // (log2 units): exp2(s - m) then stays <= 256, which changes no result beyond
 // rounding, and the O rescale is skipped by the whole wave in almost every
 // tile.
+#include <type_traits>
+
 #include "kernel_args.h"
 #include "kernel_common.h"
 
@@ -38,25 +42,9 @@ struct FwdCfg {
     static constexpr int ROWB = DH * 2;        // bytes of one K row
     static constexpr int KCH = DH / 8;         // 16-byte chunks per K row
     static constexpr int K_BYTES = BK * ROWB;
-    static constexpr int STAGE = 2 * K_BYTES;  // one K and one V tile, natural rows
-    static constexpr int KLD = BK * KCH / NT;  // 16-byte chunks per thread per tensor
     static constexpr int OUT_STRIDE = ROWB + 16;          // epilogue staging row
-    static constexpr int LDS = 2 * STAGE > 4 * 32 * OUT_STRIDE ? 2 * STAGE : 4 * 32 * OUT_STRIDE;
-    static_assert(KLD >= 1, "tile shape");
+    static_assert(32 * OUT_STRIDE <= K_BYTES, "a wave stages its output rows in one stage");
 };
-
-// 16-byte slot of logical chunk c in row r (rows of 16 chunks = 256 B, or 8
-// chunks = 128 B, two rows per bank cycle): 16 consecutive rows at one chunk,
-// and 4 consecutive rows x 2 chunks, hit distinct banks.
-template <int NCH>
-__device__ __forceinline__ int fslot(int r, int c) {
-    if (NCH == 16) return c ^ (((r & 7) << 1) | ((r >> 3) & 1));
-    return c ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
-}
-template <int NCH>
-__device__ __forceinline__ int frow_off(int r, int c) {
-    return r * (NCH * 16) + (fslot<NCH>(r, c) << 4);
-}
 
 typedef short fi16x4_t __attribute__((ext_vector_type(4)));
 // LDS transpose read: within each 16-lane group, result lane i, element k is
@@ -67,34 +55,17 @@ __device__ __forceinline__ u32x2_t fwd_tr16(const unsigned char* p) {
     return __builtin_bit_cast(u32x2_t, r);
 }
 
-// One 64-key tile of K or V straight from global memory into LDS
-// (global_load_lds_dwordx4: the 16 bytes of lane l land at the wave-uniform
-// LDS base + 16*l).  Instruction c of wave w fills LDS chunks
-// 256c + 64w + lane, so the lane whose slot is physical chunk p of row r loads
-// logical chunk p ^ swizzle(r) of that row.  Offsets are 32-bit: the host
-// checks that a block of one batch entry holds fewer than 2^31 elements.
-template <int DH>
-__device__ __forceinline__ void fwd_load_lds(unsigned char* stage, const uint16_t* base,
-                                             int row_stride, int kt, int Skv, int wave,
-                                             int lane) {
-    using C = FwdCfg<DH>;
-#pragma unroll
-    for (int c = 0; c < C::KLD; ++c) {
-        const int idx = C::NT * c + 64 * wave + lane;
-        const int row = idx / C::KCH, pc = idx % C::KCH;
-        const int lc = fslot<C::KCH>(row, pc);  // XOR swizzle: its own inverse
-        const int key = min(kt * C::BK + row, Skv - 1);
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(base + (key * row_stride + lc * 8)),
-            (__attribute__((address_space(3))) void*)(stage + (C::NT * c + 64 * wave) * 16), 16,
-            0, 0);
-    }
-}
-
 template <int DH>
 __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
     using C = FwdCfg<DH>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
+    // K and V stages as separate objects, each access naming its stage
+    // statically: the compiler can then see that the transpose reads of V
+    // never overlap the loads in flight into the other stages (it would
+    // otherwise wait for those loads before every transpose read).
+    __shared__ __attribute__((aligned(16))) unsigned char KA[C::K_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char KB[C::K_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char VA[C::K_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char VB[C::K_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
@@ -106,6 +77,7 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
     const int hk = (h * p.Hkv) / p.Hq;
     const cint_ptr ents = as_const(p.t_ent);
     const int e0 = as_const(p.t_off)[qt], e1 = as_const(p.t_off)[qt + 1];
+    const int m_full = as_const(p.t_mid)[qt];   // FULL tiles in [e0, m_full), PARTIAL after
 
     const int iq = qt * C::BQ + wave * 32 + l32;  // this lane's query row
     const int iqc = min(iq, p.S - 1);
@@ -115,23 +87,26 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
     for (int ks = 0; ks < C::NKS; ++ks) qreg[ks] = *(const u32x4_t*)(qrow + 16 * ks + 8 * g);
     const int ra = p.rng[2 * iq], rb = p.rng[2 * iq + 1];
 
-    const int64_t row_stride = (int64_t)p.Hkv * DH;
-    const uint16_t* kb = (const uint16_t*)p.k + (int64_t)b * p.Skv * row_stride + hk * DH;
-    const uint16_t* vb = (const uint16_t*)p.v + (int64_t)b * p.Skv * row_stride + hk * DH;
+    BufTileLoader<DH, C::BK> lk, lv;   // K and V tiles of 64 keys
+    {
+        const int64_t batch = (int64_t)b * p.Skv * p.Hkv * DH;
+        lk.init((const uint16_t*)p.k + batch, p.Skv, p.Hkv, hk, wave, lane);
+        lv.init((const uint16_t*)p.v + batch, p.Skv, p.Hkv, hk, wave, lane);
+    }
 
     // per-lane LDS offsets: natural K reads of row l32 (+32 mt), chunk 2ks+g;
     // transpose reads of V rows {4g, 8+4g} + j/4 (+16 kk), head-dim block dt.
     const int j = lane & 15, gsel = (lane >> 4) & 1;
     int nat[C::NKS];
 #pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) nat[ks] = frow_off<C::KCH>(l32, 2 * ks + g);
+    for (int ks = 0; ks < C::NKS; ++ks) nat[ks] = swz_off<C::KCH>(l32, 2 * ks + g);
     int trv[2][C::NDT];
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt) {
             const int col = 32 * dt + 16 * gsel + 4 * (j & 3);
-            trv[r][dt] = frow_off<C::KCH>(8 * r + 4 * g + (j >> 2), col >> 3) + (col & 7) * 2;
+            trv[r][dt] = swz_off<C::KCH>(8 * r + 4 * g + (j >> 2), col >> 3) + (col & 7) * 2;
         }
 
     f32x16_t oacc[C::NDT];
@@ -143,14 +118,11 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
 
     // Software pipeline over the step's key tiles (n of them): K runs one tile
     // ahead of V, so that S(i+1) = K(i+1) Q^T is issued on the MFMA pipe
-    // while the vector ALUs work on the softmax of tile i.  LDS holds two K
-    // stages and two V stages; in iteration i the wave reads K stage (i+1)%2
-    // and V stage i%2, and the threads refill K stage i%2 with tile i+2 and V
-    // stage (i+1)%2 with tile i+1 (both free since iteration i-1).
+    // while the vector ALUs work on the softmax of tile i.  Tile i sits in
+    // K/V stage A when i is even, B when odd; in iteration i the wave reads K
+    // of tile i+1 and V of tile i, and the threads load K of tile i+2 and V of
+    // tile i+1 into the stages freed in iteration i-1.
     const int n = e1 - e0;
-    unsigned char* Kst[2] = {smem, smem + C::K_BYTES};
-    unsigned char* Vst[2] = {smem + 2 * C::K_BYTES, smem + 3 * C::K_BYTES};
-    const int rs32 = p.Hkv * DH;
 
     // S^T = K Q^T; the K operands of step ks+1 are read while step ks runs
     auto s_tile = [&](f32x16_t (&sacc)[2], const unsigned char* Ks) {
@@ -171,9 +143,9 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
     };
 
     // softmax of tile i (scores in sacc) and O^T += V^T P^T
-    auto pv_tile = [&](f32x16_t (&sacc)[2], int ent, const unsigned char* Vs) {
-        const int kt = ent & 0x7fffffff;
-        if (ent < 0) {  // partial tile: keys outside [ra, rb) are invisible
+    auto pv_tile = [&](f32x16_t (&sacc)[2], int kt, const unsigned char* Vs, auto partial_tag) {
+        constexpr bool PARTIAL = decltype(partial_tag)::value;
+        if (PARTIAL) {  // keys outside [ra, rb) are invisible
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -188,16 +160,12 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, sacc[0][r]), sacc[1][r]);
         mx = pair_max(mx) * c2;
-        // move the reference max only when this tile exceeds it by > kSlack
+        // move the reference max only when this tile exceeds it by > kSlack;
+        // lanes that do not move keep alpha = 1 (m_run may be -inf there)
         const bool bump = mx > m_run + kSlack;
-        if (__builtin_amdgcn_ballot_w64(bump)) {
-            // lanes that do not move keep alpha = 1 (m_run may be -inf there)
-            const float alpha = bump ? fast_exp2(m_run - mx) : 1.f;  // 0 if m_run = -inf
-            m_run = bump ? mx : m_run;
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] *= alpha;
-        }
+        const float alpha = bump ? fast_exp2(m_run - mx) : 1.f;  // 0 if m_run = -inf
+        m_run = bump ? mx : m_run;
+        l_run *= alpha;
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
         // P rounded to bf16 for P V; the row sum stays in fp32 (a sum of the
         // rounded values would cost up to 2^-9 in lse on rows with few keys)
@@ -213,6 +181,11 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
                 pb[2 * mt + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
             }
         l_run += rsum;
+        // the O rescale is skipped by the whole wave in almost every tile
+        if (__builtin_amdgcn_ballot_w64(bump)) {
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] *= alpha;
+        }
         // O^T += V^T P^T; the K dimension (keys) of step kk takes rows
         // 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3, as P is held.  The V^T
         // operands of step kk+1 are read while the MFMAs of step kk run.
@@ -235,30 +208,47 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
         }
     };
 
-    // iteration i: refill, overlap S(i+1) with softmax(i), P V of tile i
-    auto body = [&](int i, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS loads have landed
+    // Key-tile indices of tiles i, i+1 and i+2 (0 past the list), the last
+    // one fetched an iteration ahead.
+    auto ent_at = [&](int i) { return i < n ? ents[e0 + i] & 0x7fffffff : 0; };
+    int kt0 = ent_at(0), kt1 = ent_at(1), kt2 = ent_at(2);
+
+    // iteration i: refill, S(i+1) on the matrix cores with softmax(i), P V of
+    // tile i.  S(i+1) of the last tile reads a stale stage and is discarded.
+    auto body = [&](int i, f32x16_t (&cur)[2], f32x16_t (&nxt)[2], const unsigned char* Kn,
+                    unsigned char* Kl, const unsigned char* Vc, unsigned char* Vl,
+                    auto partial_tag) {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into LDS have landed
         __syncthreads();  // K(i+1) and V(i) are in LDS; the stages refilled below are free
-        if (i + 2 < n)
-            fwd_load_lds<DH>(Kst[i & 1], kb, rs32, ents[e0 + i + 2] & 0x7fffffff, p.Skv, wave, lane);
-        if (i + 1 < n)
-            fwd_load_lds<DH>(Vst[(i + 1) & 1], vb, rs32, ents[e0 + i + 1] & 0x7fffffff, p.Skv, wave,
-                             lane);
-        if (i + 1 < n) s_tile(nxt, Kst[(i + 1) & 1]);
-        pv_tile(cur, ents[e0 + i], Vst[i & 1]);
+        if (i + 2 < n) lk.load(Kl, kt2, wave);
+        if (i + 1 < n) lv.load(Vl, kt1, wave);
+        const int kt = kt0;
+        kt0 = kt1;
+        kt1 = kt2;
+        kt2 = ent_at(i + 3);
+        s_tile(nxt, Kn);
+        pv_tile(cur, kt, Vc, partial_tag);
     };
 
     if (n > 0) {
-        fwd_load_lds<DH>(Kst[0], kb, rs32, ents[e0] & 0x7fffffff, p.Skv, wave, lane);
-        fwd_load_lds<DH>(Vst[0], vb, rs32, ents[e0] & 0x7fffffff, p.Skv, wave, lane);
-        if (n > 1) fwd_load_lds<DH>(Kst[1], kb, rs32, ents[e0 + 1] & 0x7fffffff, p.Skv, wave, lane);
+        lk.load(KA, kt0, wave);
+        lv.load(VA, kt0, wave);
+        if (n > 1) lk.load(KB, kt1, wave);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         f32x16_t sa[2], sb[2];
-        s_tile(sa, Kst[0]);
-        for (int i = 0; i < n; i += 2) {
-            body(i, sa, sb);
-            if (i + 1 < n) body(i + 1, sb, sa);
+        s_tile(sa, KA);
+        // full tiles in pairs, unmasked; a last odd full tile joins the masked
+        // loop (its mask keeps every key)
+        const int nF2 = (m_full - e0) & ~1;
+        int i = 0;
+        for (; i < nF2; i += 2) {
+            body(i, sa, sb, KB, KA, VA, VB, std::false_type{});
+            body(i + 1, sb, sa, KA, KB, VB, VA, std::false_type{});
+        }
+        for (; i < n; i += 2) {
+            body(i, sa, sb, KB, KA, VA, VB, std::true_type{});
+            if (i + 1 < n) body(i + 1, sb, sa, KA, KB, VB, VA, std::true_type{});
         }
     }
 
@@ -322,7 +312,7 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
 
     // FWD_LAST / FWD_SOLO: final bf16 output through LDS for coalesced rows.
     __syncthreads();  // every wave is done with the K/V stages
-    unsigned char* st = smem + wave * 32 * C::OUT_STRIDE;
+    unsigned char* st = wave == 0 ? KA : wave == 1 ? KB : wave == 2 ? VA : VB;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll

@@ -57,6 +57,81 @@ __device__ __forceinline__ cint_ptr as_const(const int32_t* p) { return (cint_pt
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16-byte slot of logical chunk c in row r of an LDS tile whose rows hold NCH
+// chunks (16: 256-byte rows; 8: 128-byte rows, two rows per bank cycle).  The
+// XOR patterns keep 16 consecutive rows at one chunk, and 4 consecutive rows
+// x 2 chunks, on distinct banks; each pattern is its own inverse.
+template <int NCH>
+__device__ __forceinline__ int swz_slot(int r, int c) {
+    static_assert(NCH == 16 || NCH == 8, "row width");
+    if (NCH == 16) return c ^ (((r & 7) << 1) | ((r >> 3) & 1));
+    return c ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+}
+template <int NCH>
+__device__ __forceinline__ int swz_off(int r, int c) {
+    return r * (NCH * 16) + (swz_slot<NCH>(r, c) << 4);
+}
+
+// Tiles of ROWS rows x DH bf16 values (one head) of a row-major tensor
+// [rows, heads, DH] copied straight into LDS by buffer loads
+// (buffer_load_dwordx4 ... lds: the 16 bytes of lane l land at the
+// wave-uniform LDS base + 16*l).  Instruction c of wave w fills LDS chunks
+// NT*c + 64w + lane; the lane whose slot there is physical chunk p of row r
+// loads logical chunk swz_slot(r, p), so the tile lands XOR-swizzled.  The
+// buffer spans the tensor's `nrows` rows, so rows past the end read as zeros;
+// the per-lane part of every offset is fixed and a tile moves only the scalar
+// offset.  Byte offsets are 32-bit: nrows * row bytes must stay below 2^32.
+template <int DH, int ROWS, int NT = 256>
+struct BufTileLoader {
+    static constexpr int KCH = DH / 8;
+    static constexpr int NLD = ROWS * KCH / NT;   // instructions per thread per tile
+    static_assert(NLD >= 1 && ROWS * KCH % NT == 0, "tile shape");
+    __amdgpu_buffer_rsrc_t rsrc;
+    int voff[NLD];
+    int tile_bytes;   // bytes from one tile to the next
+    int head_off;     // bytes from the start of a row to this head
+
+    __device__ __forceinline__ void init(const uint16_t* base, int nrows, int heads, int head,
+                                         int wave, int lane) {
+        const int row_bytes = heads * DH * 2;
+        tile_bytes = ROWS * row_bytes;
+        head_off = head * DH * 2;
+        rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrows * row_bytes, 0x00020000);
+#pragma unroll
+        for (int c = 0; c < NLD; ++c) {
+            const int idx = NT * c + 64 * wave + lane;
+            const int row = idx / KCH, pc = idx % KCH;
+            voff[c] = row * row_bytes + swz_slot<KCH>(row, pc) * 16;
+        }
+    }
+    // tile `t` (rows ROWS*t ..) of head `head` (default: the head of init)
+    __device__ __forceinline__ void load(unsigned char* lds, int t, int wave, int head = -1) const {
+        const int soff = t * tile_bytes + (head < 0 ? head_off : head * DH * 2);
+#pragma unroll
+        for (int c = 0; c < NLD; ++c)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void*)(lds + (NT * c + 64 * wave) * 16), 16,
+                voff[c], soff, 0, 0);
+    }
+};
+
+// K and V tiles of one kv head (rows = keys of a [B, Skv, Hkv, DH] block).
+template <int DH, int ROWS>
+struct KvLoader {
+    BufTileLoader<DH, ROWS> lk, lv;
+    __device__ __forceinline__ void init(const uint16_t* k, const uint16_t* v, int b, int Skv,
+                                         int Hkv, int hk, int wave, int lane) {
+        const int64_t batch = (int64_t)b * Skv * Hkv * DH;
+        lk.init(k + batch, Skv, Hkv, hk, wave, lane);
+        lv.init(v + batch, Skv, Hkv, hk, wave, lane);
+    }
+    __device__ __forceinline__ void load(unsigned char* kdst, unsigned char* vdst, int t,
+                                         int wave) const {
+        lk.load(kdst, t, wave);
+        lv.load(vdst, t, wave);
+    }
+};
+
 // Blocks of a launch are dealt to the 8 XCDs round-robin; this remaps the
 // block index so that each XCD receives one contiguous range of work items
 // (neighbouring items share K/V and therefore that XCD's L2).  grid % 8 == 0.
