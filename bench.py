@@ -10,6 +10,8 @@ C ABI.  Default workload: basic causal ring, rank 7 of D = 8, global sequence
 
 Prints ONE JSON line.  Throughput counts algorithmic work only (visible
 (query, key) pairs): forward 4*d*Hq*B*pairs flops, backward 10*d*Hq*B*pairs.
+`--calibrate-copy` runs only a plain copy kernel of known size, the reference
+for scaling the FETCH_SIZE / WRITE_SIZE counters.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -123,6 +125,28 @@ def merge_bandwidth(ca, torch, rows=524288, d=128, reps=20):
             "avg_ms": ms / n, "GB/s": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS}
 
 
+# Algorithmic flops per visible (query, key) pair and query head, per kernel.
+# The backward's 10*d splits into S, dP, dV, dK (the dK/dV kernel, 8*d) and dQ
+# (2*d); the dQ kernel also recomputes S and dP, which count as issued work
+# only.
+ALGO_FLOPS_PER_PAIR = {"fwd_step": 4, "bwd_step": 8, "bwd_dq": 2}
+ISSUED_FLOPS_PER_PAIR = {"fwd_step": 4, "bwd_step": 8, "bwd_dq": 6}
+ROCPROF_NAME = {"fwd_step": "fwd_step_bf16_kernel", "bwd_step": "bwd_dkdv_bf16_kernel",
+                "bwd_dq": "bwd_dq_bf16_kernel"}
+
+
+def calibrate_copy(torch, nbytes=256 << 20, reps=5):
+    """A plain copy kernel of known size for scaling the FETCH_SIZE / WRITE_SIZE
+    counters: each dispatch reads nbytes and writes nbytes."""
+    x = torch.randn(nbytes // 4, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_kernel": "elementwise mul by 1.0", "bytes_read_per_dispatch": nbytes,
+                      "bytes_written_per_dispatch": nbytes, "dispatches": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +156,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the copy kernel used to scale the traffic counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one rank's share on ONE GPU; multi-GPU runs are not part of "
@@ -139,8 +165,11 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
     import context_attention_flash_amd as ca
-    from context_attention_flash_amd import synth
+    from context_attention_flash_amd import profsum, synth
 
     w = synth.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
@@ -193,21 +222,25 @@ def main():
     ms_step = elapsed / args.steps * 1e3
     total_flops = fwd_flops + bwd_flops
     value = total_flops / (ms_step * 1e-3) / 1e12
-    if "fwd_step" in kern:
-        kern["fwd_step"]["TFLOP/s"] = fwd_flops / (kern["fwd_step"]["ms_per_step"] * 1e-3) / 1e12
-    if "bwd_step" in kern:  # dK/dV kernel: S, dP, dV, dK = 8d flops per visible pair
-        kern["bwd_step"]["TFLOP/s"] = 0.8 * bwd_flops / (kern["bwd_step"]["ms_per_step"] * 1e-3) / 1e12
-    if "bwd_dq" in kern:    # dQ kernel: S, dP recomputed, dQ = 6d flops per visible pair
-        kern["bwd_dq"]["TFLOP/s"] = 0.6 * bwd_flops / (kern["bwd_dq"]["ms_per_step"] * 1e-3) / 1e12
+    flops_unit = w.head_dim * heads_b * pairs   # d * Hq * B * pairs
+    for name, k in kern.items():
+        if name in ALGO_FLOPS_PER_PAIR:
+            k["algorithmic_TFLOP/s"] = ALGO_FLOPS_PER_PAIR[name] * flops_unit / (k["ms_per_step"] * 1e-3) / 1e12
+            k["issued_TFLOP/s"] = ISSUED_FLOPS_PER_PAIR[name] * flops_unit / (k["ms_per_step"] * 1e-3) / 1e12
 
-    dom = "bwd_step" if w.with_grad else "fwd_step"
-    dom_flops = bwd_flops if w.with_grad else fwd_flops
+    # roofline of the dominant kernel (most time per step): algorithmic flops
+    # per launch (per-pair figure x the visible pairs of one launch, averaged
+    # over the step's launches) over its average launch duration
+    dom = max((n for n in kern if n in ALGO_FLOPS_PER_PAIR), key=lambda n: kern[n]["ms_per_step"])
     n_launch = kern[dom]["launches"]
-    achieved = (dom_flops / n_launch) / (kern[dom]["avg_launch_ms"] * 1e-3) / 1e12
-    roofline = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                "flops_per_launch": dom_flops / n_launch,
-                "avg_launch_ms": kern[dom]["avg_launch_ms"]}
+    flops_per_launch = ALGO_FLOPS_PER_PAIR[dom] * flops_unit / n_launch
+    achieved = flops_per_launch / (kern[dom]["avg_launch_ms"] * 1e-3) / 1e12
+    traffic = profsum.read_traffic(os.path.join(ROOT, "profiles", f"traffic_{ROCPROF_NAME[dom]}_{w.name}.md"),
+                                   ROCPROF_NAME[dom])
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": ROCPROF_NAME[dom],
+                "flops_per_launch": flops_per_launch, "avg_launch_ms": kern[dom]["avg_launch_ms"],
+                "launches_per_step": n_launch}
 
     res = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,

@@ -26,7 +26,7 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{os.path.join(ROOT, 'include')}", f"
           # no value in these kernels is ever NaN; without this every fmaxf
           # first quiets its operands (one extra instruction per value)
           "-fno-honor-nans",
-          "-munsafe-fp-atomics", "-Wno-unused-command-line-argument"]
+          "-Wno-unused-command-line-argument"]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -1,0 +1,150 @@
+"""Summaries of rocprofv3 CSV output for the profiles/ folder.
+
+    python -m context_attention_flash_amd.profsum stats TRACE_kernel_stats.csv \
+        --cmd "<the rocprofv3 command>" --title "..." --out profiles/NAME.md
+    python -m context_attention_flash_amd.profsum traffic \
+        --fetch F_counter_collection.csv --write W_counter_collection.csv \
+        --copy-fetch CF_counter_collection.csv --copy-write CW_counter_collection.csv \
+        --copy-bytes N --kernel bwd_dkdv_bf16_kernel --cmds "..." --out profiles/NAME.md
+
+`traffic` turns the FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch, as
+rocprofv3 reports them) of one kernel into bytes per launch.  Each counter is
+scaled by the factor that maps what it reads for a plain copy kernel of known
+size (N bytes read and N bytes written per dispatch) onto N.  The summary
+records a hash of the kernel's sources; bench.py reports the traffic only while
+that hash still matches the sources in the tree.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import re
+import statistics
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+
+# kernel (substring of the dispatched symbol) -> the sources it is built from
+KERNEL_SOURCES = {
+    "fwd_step_bf16_kernel": ["fwd_bf16.hip", "kernel_common.h", "kernel_args.h"],
+    "bwd_dkdv_bf16_kernel": ["bwd_bf16.hip", "kernel_common.h", "kernel_args.h"],
+    "bwd_dq_bf16_kernel": ["bwd_bf16.hip", "kernel_common.h", "kernel_args.h"],
+    "lse_merge_kernel": ["elementwise.hip", "kernel_common.h", "kernel_args.h"],
+}
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _short(name: str, n: int = 70) -> str:
+    name = re.sub(r"\(.*\)$", "", name.replace("void ", "", 1)) if name.startswith("void ") else name
+    return name if len(name) <= n else name[: n - 3] + "..."
+
+
+def stats_md(csv_path: str, cmd: str, title: str, top: int = 10) -> str:
+    rows = list(csv.DictReader(open(csv_path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = [f"# {title}", "", "Command (from the repository root, one MI355X):", "", "```", cmd, "```",
+           "", "| kernel | calls | total (us) | average (us) | min (us) | max (us) | % of GPU time |",
+           "|---|---|---|---|---|---|---|"]
+    for r in rows[:top]:
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+                   f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                   f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def _per_dispatch(csv_path: str, kernel: str, counter: str):
+    """Counter value (KiB) of every dispatch whose kernel name contains `kernel`."""
+    vals = {}
+    for r in csv.DictReader(open(csv_path)):
+        if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            vals[int(r["Dispatch_Id"])] = vals.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for a kernel matching {kernel!r} in {csv_path}")
+    return list(vals.values())
+
+
+def traffic_md(a) -> str:
+    fetch = _per_dispatch(a.fetch, a.kernel, "FETCH_SIZE")
+    write = _per_dispatch(a.write, a.kernel, "WRITE_SIZE")
+    cf = _per_dispatch(a.copy_fetch, a.copy_kernel, "FETCH_SIZE")
+    cw = _per_dispatch(a.copy_write, a.copy_kernel, "WRITE_SIZE")
+    # the copy kernel moves copy_bytes each way per dispatch; take the median
+    # dispatch (the first one may see cold caches)
+    f_scale = a.copy_bytes / (statistics.median(cf) * 1024.0)
+    w_scale = a.copy_bytes / (statistics.median(cw) * 1024.0)
+    fetch_b = statistics.mean(fetch) * 1024.0 * f_scale
+    write_b = statistics.mean(write) * 1024.0 * w_scale
+    total = fetch_b + write_b
+    out = [f"# HBM traffic of `{a.kernel}`: {a.title}", "",
+           "Commands (from the repository root, one MI355X; one counter per run):", "", "```",
+           *a.cmds.split(" ;; "), "```", "",
+           f"- dispatches of the kernel: {len(fetch)} (FETCH_SIZE run), {len(write)} (WRITE_SIZE run)",
+           f"- FETCH_SIZE per dispatch: mean {statistics.mean(fetch):.0f} KiB "
+           f"(min {min(fetch):.0f}, max {max(fetch):.0f})",
+           f"- WRITE_SIZE per dispatch: mean {statistics.mean(write):.0f} KiB "
+           f"(min {min(write):.0f}, max {max(write):.0f})",
+           f"- copy kernel (`{a.copy_kernel}`, {a.copy_bytes} bytes read and written per dispatch): "
+           f"FETCH_SIZE median {statistics.median(cf):.0f} KiB, WRITE_SIZE median "
+           f"{statistics.median(cw):.0f} KiB -> scale {f_scale:.4f} (fetch), {w_scale:.4f} (write)",
+           f"- scaled bytes per launch: fetch {fetch_b:.4g}, write {write_b:.4g}, total {total:.4g}",
+           "", "Machine-readable (bench.py reads these; the hash covers the kernel's sources):", "",
+           "```", f"kernel: {a.kernel}", f"kernel_source_sha256_16: {source_hash(a.kernel)}",
+           f"fetch_bytes_per_launch: {fetch_b:.6g}", f"write_bytes_per_launch: {write_b:.6g}",
+           f"traffic_bytes_per_launch: {total:.6g}", "```"]
+    return "\n".join(out) + "\n"
+
+
+def read_traffic(md_path: str, kernel: str):
+    """Traffic bytes per launch from a summary written by `traffic`, or None when
+    the file is missing, is for another kernel, or the kernel's sources changed."""
+    if not os.path.exists(md_path):
+        return None
+    kv = {}
+    for line in open(md_path):
+        m = re.match(r"^([a-z_0-9]+): (\S+)$", line.strip())
+        if m:
+            kv[m.group(1)] = m.group(2)
+    if kv.get("kernel") != kernel or kv.get("kernel_source_sha256_16") != source_hash(kernel):
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--title", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    for k in ("fetch", "write", "copy_fetch", "copy_write"):
+        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--copy-bytes", type=float, required=True)
+    t.add_argument("--copy-kernel", default="elementwise_kernel")
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--title", required=True)
+    t.add_argument("--cmds", required=True, help="the commands, separated by ' ;; '")
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    text = stats_md(a.csv, a.cmd, a.title) if a.mode == "stats" else traffic_md(a)
+    with open(a.out, "w") as fh:
+        fh.write(text)
+    print(text)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
