@@ -200,29 +200,35 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     };
 
     // S = Q K^T and dP - Delta = dO V^T - Delta for the 32-row half mt of the
-    // tile in stage `st`; the dP accumulators start from -Delta of their rows
-    // (element r is query row 32*mt + 8*(r/4) + 4*g + r%4).
-    auto s_half = [&](const unsigned char* st, int mt, f32x16_t& sacc, f32x16_t& pacc) {
+    // tile in stage `st`, in two parts: the LDS reads (the A operands and -Delta
+    // of the half's rows, element r being query row 32*mt + 8*(r/4) + 4*g +
+    // r%4), issued one scheduling region ahead, and the MFMAs; the dP
+    // accumulators start from -Delta.
+    struct SOps {
+        u32x4_t qa[C::NKS], oa[C::NKS];
+        f32x16_t nd;
+    };
+    auto s_read = [&](const unsigned char* st, int mt, SOps& o) {
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+            o.qa[ks] = *(const u32x4_t*)(st + C::OFF_Q + nat[ks] + mt * 32 * C::ROWB);
+            o.oa[ks] = *(const u32x4_t*)(st + C::OFF_DO + nat[ks] + mt * 32 * C::ROWB);
+        }
         const float* nd = (const float*)(st + C::OFF_ND);
-        sacc = (f32x16_t){};
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             const f32x4_t x = *(const f32x4_t*)(nd + 32 * mt + 8 * rg + 4 * g);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pacc[4 * rg + i] = x[i];
+            for (int i = 0; i < 4; ++i) o.nd[4 * rg + i] = x[i];
         }
-        // the operands of step ks+1 are read while step ks runs
-        u32x4_t qa[2], oa[2];
-        qa[0] = *(const u32x4_t*)(st + C::OFF_Q + nat[0] + mt * 32 * C::ROWB);
-        oa[0] = *(const u32x4_t*)(st + C::OFF_DO + nat[0] + mt * 32 * C::ROWB);
+    };
+    auto s_mfma = [&](const SOps& o, f32x16_t& sacc, f32x16_t& pacc) {
+        sacc = (f32x16_t){};
+        pacc = o.nd;
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
-            if (ks + 1 < C::NKS) {
-                qa[(ks + 1) & 1] = *(const u32x4_t*)(st + C::OFF_Q + nat[ks + 1] + mt * 32 * C::ROWB);
-                oa[(ks + 1) & 1] = *(const u32x4_t*)(st + C::OFF_DO + nat[ks + 1] + mt * 32 * C::ROWB);
-            }
-            sacc = mfma_32x32x16(qa[ks & 1], kreg[ks], sacc);
-            pacc = mfma_32x32x16(oa[ks & 1], vreg[ks], pacc);
+            sacc = mfma_32x32x16(o.qa[ks], kreg[ks], sacc);
+            pacc = mfma_32x32x16(o.oa[ks], vreg[ks], pacc);
         }
     };
 
@@ -261,13 +267,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     };
 
     // dV^T += dO^T P and dK^T += Q^T dS over the query rows of half mt; the K
-    // dimension of query block kk takes rows 16kk + 4g + 0..3 and
+    // dimension of query block kk = 2*mt + k2 takes rows 16kk + 4g + 0..3 and
     // 16kk + 8 + 4g + 0..3.
-    auto d_half = [&](const unsigned char* st, int mt, const u32x4_t (&pb)[2],
-                      const u32x4_t (&db)[2]) {
-        // the operands of head-dim block dt+1 are read while block dt runs
-        u32x4_t oa[2][2], qa[2][2];
-        auto read = [&](int dt, u32x4_t (&o)[2], u32x4_t (&q)[2]) {
+    // The transposed operands of half mt of the tile in stage st, all head-dim
+    // blocks (the dV/dK MFMAs of that half then need no LDS read).
+    auto read_half = [&](const unsigned char* st, int mt, u32x4_t (&oa)[C::NDT][2],
+                         u32x4_t (&qa)[C::NDT][2]) {
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
                 const int o16 = (2 * mt + k2) * 16 * C::ROWB;
@@ -275,54 +282,77 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                 const u32x2_t o2 = lds_tr16(st + C::OFF_DO + trq[1][dt] + o16);
                 const u32x2_t q1 = lds_tr16(st + C::OFF_Q + trq[0][dt] + o16);
                 const u32x2_t q2 = lds_tr16(st + C::OFF_Q + trq[1][dt] + o16);
-                o[k2] = (u32x4_t){o1[0], o1[1], o2[0], o2[1]};
-                q[k2] = (u32x4_t){q1[0], q1[1], q2[0], q2[1]};
+                oa[dt][k2] = (u32x4_t){o1[0], o1[1], o2[0], o2[1]};
+                qa[dt][k2] = (u32x4_t){q1[0], q1[1], q2[0], q2[1]};
             }
-        };
-        read(0, oa[0], qa[0]);
+    };
+    auto mfma_half = [&](const u32x4_t (&oa)[C::NDT][2], const u32x4_t (&qa)[C::NDT][2],
+                         const u32x4_t (&pb)[2], const u32x4_t (&db)[2]) {
 #pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt) {
-            if (dt + 1 < C::NDT) read(dt + 1, oa[(dt + 1) & 1], qa[(dt + 1) & 1]);
+        for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
-                dv_acc[dt] = mfma_32x32x16(oa[dt & 1][k2], pb[k2], dv_acc[dt]);
-                dk_acc[dt] = mfma_32x32x16(qa[dt & 1][k2], db[k2], dk_acc[dt]);
+                dv_acc[dt] = mfma_32x32x16(oa[dt][k2], pb[k2], dv_acc[dt]);
+                dk_acc[dt] = mfma_32x32x16(qa[dt][k2], db[k2], dk_acc[dt]);
             }
-        }
     };
+
+    // dV/dK of the second half of a tile run at the start of the next
+    // iteration, before its barrier: their operands (read below, at the end of
+    // the tile) and P/dS wait in registers, and the MFMAs execute while the
+    // wave waits at the barrier.  Every LDS read of a stage is complete before
+    // that barrier, so two stages still suffice.  Zero-initialised, the first
+    // iteration's carried MFMAs add nothing.
+    u32x4_t c_oa[C::NDT][2], c_qa[C::NDT][2], c_pb[2], c_db[2];
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) c_oa[dt][k2] = c_qa[dt][k2] = (u32x4_t){0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) c_pb[k2] = c_db[k2] = (u32x4_t){0u, 0u, 0u, 0u};
 
     // One query tile, pipelined in halves: S/dP of half 1 run on the matrix
     // cores while P/dS of half 0 run on the vector ALUs, then dV/dK of half 0
-    // while P/dS of half 1.
+    // while P/dS of half 1; the operands of half 1's dV/dK are read last.
+    // Scheduling fences split the tile into regions; the LDS reads of each
+    // region's MFMAs are issued in the region before, so that the MFMAs do
+    // not wait for them, and the fences bound the registers in flight.
     auto tile = [&](const unsigned char* st, auto partial_tag) {
         f32x16_t s0, p0, s1, p1;
-        u32x4_t pb0[2], db0[2], pb1[2], db1[2];
-        // the scheduling fences keep each slice's operand reads inside it,
-        // which bounds the registers in flight
-        s_half(st, 0, s0, p0);
+        u32x4_t pb0[2], db0[2];
+        SOps o0, o1;
+        u32x4_t oa[C::NDT][2], qa[C::NDT][2];
+        s_read(st, 0, o0);
         __builtin_amdgcn_sched_barrier(0);
-        s_half(st, 1, s1, p1);
+        s_mfma(o0, s0, p0);
+        s_read(st, 1, o1);
+        __builtin_amdgcn_sched_barrier(0);
+        s_mfma(o1, s1, p1);
         p_half(st, 0, partial_tag, s0, p0, pb0, db0);
+        read_half(st, 0, oa, qa);
         __builtin_amdgcn_sched_barrier(0);
-        d_half(st, 0, pb0, db0);
-        p_half(st, 1, partial_tag, s1, p1, pb1, db1);
+        mfma_half(oa, qa, pb0, db0);
+        p_half(st, 1, partial_tag, s1, p1, c_pb, c_db);
+        read_half(st, 1, c_oa, c_qa);
         __builtin_amdgcn_sched_barrier(0);
-        d_half(st, 1, pb1, db1);
     };
 
-    // Two LDS stages: the barrier at the top of iteration `it` makes tile it
-    // visible and frees the stage of tile it-1, which then receives tile it+1.
-    // Even iterations use stage A, odd ones stage B.
+    // Iteration it: the carried dV/dK MFMAs of tile it-1, then the barrier
+    // that makes tile it visible and frees the other stage, which receives
+    // tile it+1.  Even iterations use stage A, odd ones stage B.
     int ent_nx = n_iter > 1 ? entry_of(1) : 0;   // entry of tile it+1
     auto step = [&](int it, unsigned char* cur, unsigned char* nxt, auto partial_tag) {
+        mfma_half(c_oa, c_qa, c_pb, c_db);
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt) asm volatile("" : "+a"(dk_acc[dt]), "+a"(dv_acc[dt]));
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile it have landed
         __syncthreads();
-        const int ent = ent_nx;
-        if (it + 1 < n_iter) load(it + 1, ent, nxt);
-        if (it + 2 < n_iter) ent_nx = entry_of(it + 2);
+        if (it + 1 < n_iter) load(it + 1, ent_nx, nxt);
         tile(cur, partial_tag);
+        // the scalar load goes out after the tile's LDS reads: while it is in
+        // flight every LDS wait must be a full one (scalar loads return out of
+        // order)
+        if (it + 2 < n_iter) ent_nx = entry_of(it + 2);
     };
     // The unmasked loop covers an even number of iterations; a last full tile
     // left over goes through the masked loop, where the mask keeps every key.
@@ -337,6 +367,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         step(it, stA, stB, std::true_type{});
         if (it + 1 < n_iter) step(it + 1, stB, stA, std::true_type{});
     }
+    mfma_half(c_oa, c_qa, c_pb, c_db);   // the last tile's second half
 
     // dK_j += scale * dK^T acc, dV_j += dV^T acc (this lane's key, 64 head-dim values)
     if (key < p.Skv) {
