@@ -90,24 +90,37 @@ template <int DH>
 struct DkdvLoader {
     using C = BwdCfg<DH>;
     BufTileLoader<DH, C::BQ> lq, lo;
+    // row values: lse2 and -Delta of batch entry b ([Hq][S_pad] each), the
+    // intervals ([S_pad][2]); lanes 0-15, 16-31 and 32-63 of wave 0 each load
+    // one of them with its own buffer (a direct-to-LDS global load instead
+    // would make the compiler drain every later LDS wait completely)
+    __amdgpu_buffer_rsrc_t rl, rd, rr;
 
     __device__ __forceinline__ void init(const BwdArgs& p, int b, int wave, int lane) {
         const int64_t batch = (int64_t)b * p.S * p.Hq * DH;
         lq.init(p.q + batch, p.S, p.Hq, 0, wave, lane);
         lo.init(p.dout + batch, p.S, p.Hq, 0, wave, lane);
+        const int rows = p.Hq * p.S_pad * 4;
+        rl = __builtin_amdgcn_make_buffer_rsrc((void*)(p.lse2 + (int64_t)b * p.Hq * p.S_pad), (short)0,
+                                               rows, 0x00020000);
+        rd = __builtin_amdgcn_make_buffer_rsrc((void*)(p.ndelta + (int64_t)b * p.Hq * p.S_pad), (short)0,
+                                               rows, 0x00020000);
+        rr = __builtin_amdgcn_make_buffer_rsrc((void*)p.rng, (short)0, p.S_pad * 8, 0x00020000);
     }
 
-    __device__ __forceinline__ void load(unsigned char* stage, const BwdArgs& p, int b, int h,
-                                         int qt, int wave, int lane) const {
+    __device__ __forceinline__ void load(unsigned char* stage, const BwdArgs& p, int h, int qt,
+                                         int wave, int lane) const {
         lq.load(stage + C::OFF_Q, qt, wave, h);
         lo.load(stage + C::OFF_DO, qt, wave, h);
         if (wave == 0) {
-            const int64_t r0 = ((int64_t)b * p.Hq + h) * p.S_pad + qt * C::BQ;
-            const void* src = lane < 16   ? (const void*)(p.lse2 + r0 + 4 * lane)
-                              : lane < 32 ? (const void*)(p.ndelta + r0 + 4 * (lane - 16))
-                                          : (const void*)(p.rng + 2 * qt * C::BQ + 4 * (lane - 32));
-            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(stage + C::OFF_L),
-                                             16, 0, 0);
+            auto* dst = (__attribute__((address_space(3))) void*)(stage + C::OFF_L);
+            const int row_off = (h * p.S_pad + qt * C::BQ) * 4;
+            if (lane < 16)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, dst, 16, lane * 16, row_off, 0, 0);
+            else if (lane < 32)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, dst, 16, (lane - 16) * 16, row_off, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, dst, 16, (lane - 32) * 16, qt * C::BQ * 8, 0, 0);
         }
     }
 };
@@ -196,7 +209,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         return hk * group + (full ? it : it - nF) / n;
     };
     auto load = [&](int it, int ent, unsigned char* st) {
-        ld.load(st, p, b, head_of(it), ent & 0x7fffffff, wave, lane);
+        ld.load(st, p, head_of(it), ent & 0x7fffffff, wave, lane);
     };
 
     // S = Q K^T and dP - Delta = dO V^T - Delta for the 32-row half mt of the
