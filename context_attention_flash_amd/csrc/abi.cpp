@@ -39,6 +39,10 @@ struct DevStep {
     const int32_t* b_mid = nullptr;
     const int32_t* b_ent = nullptr;
     const int32_t* b_order = nullptr;
+    const int32_t* q_off = nullptr;   // dQ lists: 256-row query tiles over 64-key tiles
+    const int32_t* q_mid = nullptr;
+    const int32_t* q_ent = nullptr;
+    const int32_t* q_order = nullptr;
 };
 
 struct Plan {
@@ -46,6 +50,7 @@ struct Plan {
     int64_t S_pad = 0;
     int32_t nqt = 0;    // forward query tiles
     int32_t nkt_b = 0;  // backward key tiles
+    int32_t nqt_dq = 0; // dQ query tiles
     void* dbuf = nullptr;
     std::vector<DevStep> steps;
     ~Plan() {
@@ -104,14 +109,15 @@ void build_lists(const std::vector<int8_t>& kinds, int64_t nrows, int64_t ncols,
 int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
     auto plan = std::make_unique<Plan>();
     plan->device = device;
-    plan->S_pad = round_up(g.S, FWD_BQ);
+    plan->S_pad = round_up(g.S, S_ALIGN);
     plan->nqt = (int32_t)((g.S + FWD_BQ - 1) / FWD_BQ);
     plan->nkt_b = (int32_t)((g.Skv + BWD_BK - 1) / BWD_BK);
+    plan->nqt_dq = (int32_t)((g.S + DQ_BQ - 1) / DQ_BQ);
     const int64_t nkt_f = (g.Skv + FWD_BK - 1) / FWD_BK;
     const int64_t nqt_b = (g.S + BWD_BQ - 1) / BWD_BQ;
 
     HostArrays H;
-    struct Idx { size_t rng, foff, fmid, fent, ford, boff, bmid, bent, bord; };
+    struct Idx { size_t rng, foff, fmid, fent, ford, boff, bmid, bent, bord, qoff, qmid, qent, qord; };
     std::vector<Idx> idx;
     std::vector<StepRanges> all(g.nb);
     int64_t total_pairs = 0;
@@ -150,6 +156,12 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
         ix.bmid = H.add(std::move(mid));
         ix.bent = H.add(std::move(ent));
         ix.bord = H.add(std::move(order));
+        classify(sr, g.S, g.Skv, DQ_BQ, DQ_BK, kinds);
+        build_lists(kinds, plan->nqt_dq, (g.Skv + DQ_BK - 1) / DQ_BK, true, off, mid, ent, order);
+        ix.qoff = H.add(std::move(off));
+        ix.qmid = H.add(std::move(mid));
+        ix.qent = H.add(std::move(ent));
+        ix.qord = H.add(std::move(order));
         plan->steps.push_back(ds);
         idx.push_back(ix);
     }
@@ -182,6 +194,10 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
         d.b_mid = P(idx[k].bmid);
         d.b_ent = P(idx[k].bent);
         d.b_order = P(idx[k].bord);
+        d.q_off = P(idx[k].qoff);
+        d.q_mid = P(idx[k].qmid);
+        d.q_ent = P(idx[k].qent);
+        d.q_order = P(idx[k].qord);
     }
     out = std::move(plan);
     return RA_OK;
@@ -276,7 +292,7 @@ int collect_timing() {
 int64_t elem_bytes(const Geometry& g) { return g.dtype == RA_BF16 ? 2 : 4; }
 
 int64_t fwd_workspace(const Geometry& g) {
-    const int64_t S_pad = round_up(g.S, FWD_BQ);
+    const int64_t S_pad = round_up(g.S, S_ALIGN);
     if (g.merge_mode == RA_MERGE_FUSED) return round_up((int64_t)g.B * g.Hq * S_pad * g.d * 4, 256);
     const int64_t o = round_up((int64_t)g.B * g.S * g.Hq * g.d * 4, 256);
     return 2 * o + round_up((int64_t)g.B * g.Hq * g.S * 4, 256);
@@ -285,10 +301,10 @@ int64_t fwd_workspace(const Geometry& g) {
 // Backward workspace: the per-row arrays lse2 and -Delta, [B, Hq, S_pad] fp32
 // each, then the dQ accumulator [B, Hq, S_pad, d] fp32.
 int64_t bwd_row_bytes(const Geometry& g) {
-    return round_up((int64_t)g.B * g.Hq * round_up(g.S, FWD_BQ) * 4, 256);
+    return round_up((int64_t)g.B * g.Hq * round_up(g.S, S_ALIGN) * 4, 256);
 }
 int64_t bwd_workspace(const Geometry& g) {
-    const int64_t S_pad = round_up(g.S, FWD_BQ);
+    const int64_t S_pad = round_up(g.S, S_ALIGN);
     return 2 * bwd_row_bytes(g) + round_up((int64_t)g.B * g.Hq * S_pad * g.d * 4, 256);
 }
 
@@ -537,9 +553,9 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
         qa.q = (const uint16_t*)q; qa.dout = (const uint16_t*)dout; qa.lse2 = lse2;
         qa.ndelta = ndelta; qa.dq_acc = dq_acc;
         qa.B = g.B; qa.S = (int32_t)g.S; qa.Skv = (int32_t)g.Skv; qa.Hq = g.Hq; qa.Hkv = g.Hkv;
-        qa.nqt = plan->nqt;
+        qa.nqt = plan->nqt_dq;
         qa.S_pad = (int32_t)plan->S_pad;
-        qa.total_work = g.B * g.Hq * plan->nqt;
+        qa.total_work = g.B * g.Hq * plan->nqt_dq;
         qa.scale = g.scale;
         qa.scale_log2 = a.scale_log2;
         bool first = true;
@@ -556,7 +572,7 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
             // the dQ kernel writes the accumulator on the first step (also when a
             // step has no visible pair, in which case it writes zeros)
             qa.k = a.k; qa.v = a.v;
-            qa.rng = st.rng; qa.t_off = st.f_off; qa.t_mid = st.f_mid; qa.t_ent = st.f_ent; qa.t_order = st.f_order;
+            qa.rng = st.rng; qa.t_off = st.q_off; qa.t_mid = st.q_mid; qa.t_ent = st.q_ent; qa.t_order = st.q_order;
             qa.first = first ? 1 : 0;
             if (st.pairs > 0 || first) {
                 rc = hip_rc(timed(KC_BWD_DQ, s, [&] { return launch_bwd_dq_bf16(qa, g.d, s); }));

@@ -19,13 +19,14 @@
 // 32-63); the transpose reads pick their rows in that same order.  dK/dV are
 // added to the caller's buffers once at the end (one owner per key tile).
 //
-// K4b bwd_dq: one work-group = one (batch, q head, 128-row query tile), as in
-// the forward: lane = query column, Q and dO in registers, 64-key tiles of K
-// and V streamed through LDS.  It recomputes S^T = K Q^T and dP^T = V dO^T and
-// accumulates dQ^T += K^T dS^T (K^T from transpose reads).  Each (head, query
-// tile) has one owner per launch, so dQ needs no atomics: fp32 atomics on the
-// L2 run about ten times slower than plain stores, and the dQ of a key-tile
-// decomposition would be bound by them.
+// K4b bwd_dq: one work-group = one (batch, q head, 256-row query tile); wave w
+// owns 64 query rows as two 32-row blocks, lane = query column, Q and dO in
+// registers, 64-key tiles of K and V streamed through LDS.  It recomputes
+// S^T = K Q^T and dP^T = V dO^T and accumulates dQ^T += K^T dS^T (K^T from
+// transpose reads); every LDS operand feeds the MFMAs of both query blocks.
+// Each (head, query tile) has one owner per launch, so dQ needs no atomics:
+// fp32 atomics on the L2 run about ten times slower than plain stores, and
+// the dQ of a key-tile decomposition would be bound by them.
 #include <type_traits>
 
 #include "kernel_args.h"
@@ -423,7 +424,7 @@ hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int head_dim, hipStream_t s) {
 template <int DH>
 struct DqCfg {
     static constexpr int NT = 256;
-    static constexpr int BQ = FWD_BQ, BK = FWD_BK;   // 4 waves x 32 queries, 64 keys
+    static constexpr int BQ = DQ_BQ, BK = DQ_BK;     // 4 waves x 64 queries, 64 keys
     static constexpr int NKS = DH / 16;
     static constexpr int NDT = DH / 32;
     static constexpr int ROWB = DH * 2;
@@ -452,25 +453,35 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int e0 = as_const(p.t_off)[qt], e1 = as_const(p.t_off)[qt + 1];
     const int m = as_const(p.t_mid)[qt];   // FULL tiles in [e0, m), PARTIAL in [m, e1)
 
-    const int iq = qt * C::BQ + wave * 32 + l32;  // this lane's query row
-    const int iqc = min(iq, p.S - 1);
+    // Wave w owns query rows qt*256 + 64w + 32qb + l32 for qb = 0, 1: every K
+    // or V operand read from LDS feeds the MFMAs of both query blocks.
     const int q_stride = p.Hq * DH;
-    const uint16_t* qrow = p.q + ((int64_t)b * p.S + iqc) * q_stride + h * DH;
-    const uint16_t* orow = p.dout + ((int64_t)b * p.S + iqc) * q_stride + h * DH;
-    u32x4_t qreg[C::NKS], oreg[C::NKS];
+    u32x4_t qreg[2][C::NKS], oreg[2][C::NKS];
+    float L2[2], nD[2];
+    int ra[2], rb[2];
 #pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-        qreg[ks] = *(const u32x4_t*)(qrow + 16 * ks + 8 * g);
-        oreg[ks] = *(const u32x4_t*)(orow + 16 * ks + 8 * g);
+    for (int qb = 0; qb < 2; ++qb) {
+        const int iq = qt * C::BQ + wave * 64 + qb * 32 + l32;   // < S_pad
+        const int iqc = min(iq, p.S - 1);
+        const uint16_t* qrow = p.q + ((int64_t)b * p.S + iqc) * q_stride + h * DH;
+        const uint16_t* orow = p.dout + ((int64_t)b * p.S + iqc) * q_stride + h * DH;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+            qreg[qb][ks] = *(const u32x4_t*)(qrow + 16 * ks + 8 * g);
+            oreg[qb][ks] = *(const u32x4_t*)(orow + 16 * ks + 8 * g);
+        }
+        L2[qb] = p.lse2[((int64_t)b * p.Hq + h) * p.S_pad + iq];   // +inf on padding rows
+        nD[qb] = p.ndelta[((int64_t)b * p.Hq + h) * p.S_pad + iq];
+        ra[qb] = p.rng[2 * iq];
+        rb[qb] = p.rng[2 * iq + 1];
     }
-    const float L2 = p.lse2[((int64_t)b * p.Hq + h) * p.S_pad + iq];   // +inf on padding rows
-    const float nD = p.ndelta[((int64_t)b * p.Hq + h) * p.S_pad + iq];
-    const int ra = p.rng[2 * iq], rb = p.rng[2 * iq + 1];
 
     KvLoader<DH, C::BK> ld;   // K and V tiles of 64 keys
     ld.init(p.k, p.v, b, p.Skv, p.Hkv, hk, wave, lane);
 
-    // per-lane LDS offsets (see the dK/dV kernel)
+    // per-lane LDS offsets (see the dK/dV kernel): natural reads of key row
+    // l32 (+32 per key half), chunk 2ks+g; transpose reads of key rows
+    // {4g, 8+4g} + j/4 (+16 per key step), head-dim block dt
     const int j = lane & 15, gsel = (lane >> 4) & 1;
     int nat[C::NKS];
 #pragma unroll
@@ -484,101 +495,141 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             trk[r][dt] = row_off<C::KCH>(8 * r + 4 * g + (j >> 2), col >> 3) + (col & 7) * 2;
         }
 
-    f32x16_t acc[C::NDT];
+    f32x16_t acc[2][C::NDT];
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt) acc[dt] = (f32x16_t){};
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) acc[qb][dt] = (f32x16_t){};
     const float c2 = p.scale_log2;
 
-    // One key tile: S^T = K Q^T and dP^T = V dO^T (two 32-key halves), then
-    // P = exp(scale*S - lse), dS = P (dP - Delta) (element (mt, r) is key
-    // 32*mt + 8*(r/4) + 4*g + r%4 of the tile), then dQ^T += K^T dS^T.
-    auto tile = [&](const unsigned char* Ks, int kt, auto partial_tag) {
-        constexpr bool PARTIAL = decltype(partial_tag)::value;
-        const unsigned char* Vs = Ks + C::K_BYTES;
-        f32x16_t sacc[2], pacc[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            sacc[mt] = (f32x16_t){};
-            pacc[mt] = (f32x16_t){};
-        }
-        // the operands of step ks+1 are read while step ks runs
-        u32x4_t ka[2][2], va[2][2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            ka[0][mt] = *(const u32x4_t*)(Ks + nat[0] + mt * 32 * C::ROWB);
-            va[0][mt] = *(const u32x4_t*)(Vs + nat[0] + mt * 32 * C::ROWB);
-        }
+    // Key half kh (keys 32kh .. 32kh+31 of the tile) of stage `st`:
+    // S^T = K Q^T and dP^T = V dO^T for both query blocks (element r of a
+    // block is key 32kh + 8*(r/4) + 4*g + r%4), the A operands read one
+    // scheduling region ahead.
+    struct SOps {
+        u32x4_t ka[C::NKS], va[C::NKS];
+    };
+    auto s_read = [&](const unsigned char* st, int kh, SOps& o) {
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
-            if (ks + 1 < C::NKS)
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    ka[(ks + 1) & 1][mt] = *(const u32x4_t*)(Ks + nat[ks + 1] + mt * 32 * C::ROWB);
-                    va[(ks + 1) & 1][mt] = *(const u32x4_t*)(Vs + nat[ks + 1] + mt * 32 * C::ROWB);
-                }
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                sacc[mt] = mfma_32x32x16(ka[ks & 1][mt], qreg[ks], sacc[mt]);
-                pacc[mt] = mfma_32x32x16(va[ks & 1][mt], oreg[ks], pacc[mt]);
-            }
+            o.ka[ks] = *(const u32x4_t*)(st + nat[ks] + kh * 32 * C::ROWB);
+            o.va[ks] = *(const u32x4_t*)(st + C::K_BYTES + nat[ks] + kh * 32 * C::ROWB);
         }
-        u32x4_t db[4];
+    };
+    auto s_mfma = [&](const SOps& o, f32x16_t (&sacc)[2], f32x16_t (&pacc)[2]) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int qb = 0; qb < 2; ++qb) {
+            sacc[qb] = (f32x16_t){};
+            pacc[qb] = (f32x16_t){};
+        }
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                sacc[qb] = mfma_32x32x16(o.ka[ks], qreg[qb][ks], sacc[qb]);
+                pacc[qb] = mfma_32x32x16(o.va[ks], oreg[qb][ks], pacc[qb]);
+            }
+    };
+    // P = exp(scale*S - lse), dS = P (dP - Delta), packed to bf16 as the B
+    // operands of dQ^T for the two 16-key steps of the half
+    auto p_half = [&](int kt, int kh, auto partial_tag, const f32x16_t (&sacc)[2],
+                      const f32x16_t (&pacc)[2], u32x4_t (&db)[2][2]) {
+        constexpr bool PARTIAL = decltype(partial_tag)::value;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
                 float pv[2];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    float pr = fast_exp2(fmaf(sacc[mt][r + u], c2, -L2));
+                    float pr = fast_exp2(fmaf(sacc[qb][r + u], c2, -L2[qb]));
                     if (PARTIAL) {  // keys outside [ra, rb) are invisible
-                        const int key = kt * C::BK + 32 * mt + 8 * ((r + u) >> 2) + 4 * g + ((r + u) & 3);
-                        pr = ((key >= ra) & (key < rb)) ? pr : 0.f;
+                        const int key = kt * C::BK + 32 * kh + 8 * ((r + u) >> 2) + 4 * g + ((r + u) & 3);
+                        pr = ((key >= ra[qb]) & (key < rb[qb])) ? pr : 0.f;
                     }
-                    pv[u] = pr * (pacc[mt][r + u] + nD);
+                    pv[u] = pr * (pacc[qb][r + u] + nD[qb]);
                 }
-                db[2 * mt + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(pv[0], pv[1]);
+                db[qb][r >> 3][(r & 7) >> 1] = pack_bf16x2(pv[0], pv[1]);
             }
-        // dQ^T += K^T dS^T; the K dimension (keys) of step kk takes rows
-        // 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3, as dS is held.  The K^T
-        // operands of step kk+1 are read while step kk runs.
-        u32x4_t kt4[2][C::NDT];
-        auto read_kt = [&](u32x4_t (&dst)[C::NDT], int kk) {
+    };
+    // K^T operands of half kh: the K dimension (keys) of step kk takes rows
+    // 32kh + 16kk + 4g + 0..3 and 32kh + 16kk + 8 + 4g + 0..3, as dS is held
+    auto t_read = [&](const unsigned char* st, int kh, u32x4_t (&kt4)[2][C::NDT]) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int dt = 0; dt < C::NDT; ++dt) {
-                const u32x2_t a1 = lds_tr16(Ks + trk[0][dt] + kk * 16 * C::ROWB);
-                const u32x2_t a2 = lds_tr16(Ks + trk[1][dt] + kk * 16 * C::ROWB);
-                dst[dt] = (u32x4_t){a1[0], a1[1], a2[0], a2[1]};
+                const int o = (2 * kh + kk) * 16 * C::ROWB;
+                const u32x2_t a1 = lds_tr16(st + trk[0][dt] + o);
+                const u32x2_t a2 = lds_tr16(st + trk[1][dt] + o);
+                kt4[kk][dt] = (u32x4_t){a1[0], a1[1], a2[0], a2[1]};
             }
-        };
-        read_kt(kt4[0], 0);
+    };
+    auto q_mfma = [&](const u32x4_t (&kt4)[2][C::NDT], const u32x4_t (&db)[2][2]) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            if (kk + 1 < 4) read_kt(kt4[(kk + 1) & 1], kk + 1);
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int dt = 0; dt < C::NDT; ++dt)
-                acc[dt] = mfma_32x32x16(kt4[kk & 1][dt], db[kk], acc[dt]);
-        }
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+                    acc[qb][dt] = mfma_32x32x16(kt4[kk][dt], db[qb][kk], acc[qb][dt]);
+    };
+
+    // dQ of the second key half runs at the start of the next iteration,
+    // before its barrier (as in the dK/dV kernel); zero operands at first.
+    u32x4_t c_kt[2][C::NDT], c_db[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) c_kt[kk][dt] = (u32x4_t){0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) c_db[qb][kk] = (u32x4_t){0u, 0u, 0u, 0u};
+    }
+
+    // One key tile in four scheduling regions: S/dP of half 0; S/dP of half
+    // 1 with P/dS of half 0; dQ of half 0 with P/dS of half 1 (and the K^T
+    // reads of half 1, for the carried dQ).  Each region's LDS reads are
+    // issued in the region before.
+    auto tile = [&](const unsigned char* st, int kt, auto partial_tag) {
+        f32x16_t s0[2], p0[2], s1[2], p1[2];
+        u32x4_t db0[2][2];
+        SOps o0, o1;
+        u32x4_t kt0[2][C::NDT];
+        s_read(st, 0, o0);
+        __builtin_amdgcn_sched_barrier(0);
+        s_mfma(o0, s0, p0);
+        s_read(st, 1, o1);
+        __builtin_amdgcn_sched_barrier(0);
+        s_mfma(o1, s1, p1);
+        p_half(kt, 0, partial_tag, s0, p0, db0);
+        t_read(st, 0, kt0);
+        __builtin_amdgcn_sched_barrier(0);
+        q_mfma(kt0, db0);
+        p_half(kt, 1, partial_tag, s1, p1, c_db);
+        t_read(st, 1, c_kt);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     // Two LDS stages, even list positions in stage A: the barrier at the top
-    // of position e makes tile e visible and frees the other stage, which
-    // then receives tile e+1.  The entry of tile e+1 is fetched a position
+    // of position i makes tile i visible and frees the other stage, which
+    // then receives tile i+1.  The entry of tile i+1 is fetched a position
     // ahead.  Full tiles run unmasked in pairs; a last odd full tile joins the
     // masked loop (its mask keeps every key).
     const int n = e1 - e0;
     const int nF2 = (m - e0) & ~1;
     int ent_nx = n > 1 ? ents[e0 + 1] : 0;
     auto step = [&](int i, const unsigned char* cur, unsigned char* nxt, auto partial_tag) {
+        q_mfma(c_kt, c_db);
 #pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt) asm volatile("" : "+a"(acc[dt]));
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) asm volatile("" : "+a"(acc[qb][dt]));
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile i have landed
         __syncthreads();
-        const int ent = ents[e0 + i];
-        const int enx = ent_nx;
+        if (i + 1 < n) ld.load(nxt, nxt + C::K_BYTES, ent_nx & 0x7fffffff, wave);
+        const int kt = ents[e0 + i] & 0x7fffffff;
+        tile(cur, kt, partial_tag);
         if (i + 2 < n) ent_nx = ents[e0 + i + 2];
-        if (i + 1 < n) ld.load(nxt, nxt + C::K_BYTES, enx & 0x7fffffff, wave);
-        tile(cur, ent & 0x7fffffff, partial_tag);
     };
     if (n > 0) ld.load(stA, stA + C::K_BYTES, ents[e0] & 0x7fffffff, wave);
     int i = 0;
@@ -590,21 +641,26 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         step(i, stA, stB, std::true_type{});
         if (i + 1 < n) step(i + 1, stB, stA, std::true_type{});
     }
+    q_mfma(c_kt, c_db);   // the last tile's second half
 
-    // dq_acc (+)= scale * acc in the accumulator layout: element (dt, r) of this
-    // lane is head-dim index 32*dt + 8*(r/4) + 4*g + r%4 of query row iq.
-    f32x4_t* dst = (f32x4_t*)p.dq_acc +
-                   (((int64_t)b * p.Hq + h) * (p.S_pad / 32) + (qt * 4 + wave)) * (8 * DH) + lane;
+    // dq_acc (+)= scale * acc in the accumulator layout: element (dt, r) of
+    // query block qb is head-dim index 32*dt + 8*(r/4) + 4*g + r%4 of query
+    // row qt*256 + 64*wave + 32*qb + l32.
 #pragma unroll
-    for (int dt = 0; dt < C::NDT; ++dt)
+    for (int qb = 0; qb < 2; ++qb) {
+        f32x4_t* dst = (f32x4_t*)p.dq_acc +
+                       (((int64_t)b * p.Hq + h) * (p.S_pad / 32) + (qt * 8 + wave * 2 + qb)) * (8 * DH) + lane;
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            f32x4_t o = {acc[dt][4 * rg] * p.scale, acc[dt][4 * rg + 1] * p.scale,
-                         acc[dt][4 * rg + 2] * p.scale, acc[dt][4 * rg + 3] * p.scale};
-            f32x4_t* ptr = dst + (dt * 4 + rg) * 64;
-            if (!p.first) o += *ptr;
-            *ptr = o;
-        }
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                f32x4_t o = {acc[qb][dt][4 * rg] * p.scale, acc[qb][dt][4 * rg + 1] * p.scale,
+                             acc[qb][dt][4 * rg + 2] * p.scale, acc[qb][dt][4 * rg + 3] * p.scale};
+                f32x4_t* ptr = dst + (dt * 4 + rg) * 64;
+                if (!p.first) o += *ptr;
+                *ptr = o;
+            }
+    }
 }
 
 hipError_t launch_bwd_dq_bf16(const DqArgs& a, int head_dim, hipStream_t s) {

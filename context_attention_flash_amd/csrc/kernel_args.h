@@ -21,6 +21,9 @@ constexpr int FWD_BQ = 128;   // query rows per forward work-group (4 waves x 32
 constexpr int FWD_BK = 64;    // keys per forward tile
 constexpr int BWD_BQ = 64;    // query rows per backward tile
 constexpr int BWD_BK = 128;   // keys per backward work-group (4 waves x 32)
+constexpr int DQ_BQ = 256;    // query rows per dQ work-group (4 waves x 64)
+constexpr int DQ_BK = 64;     // keys per dQ tile
+constexpr int S_ALIGN = 256;  // the padded row count S_pad is a multiple of this
 
 struct FwdArgs {
     const void* q;          // [B, S, Hq, d]
@@ -71,13 +74,13 @@ struct DqArgs {
     const float* lse2;      // [B, Hq, S_pad] as in BwdArgs
     const float* ndelta;    // [B, Hq, S_pad]
     const int32_t* rng;     // [S_pad][2]
-    const int32_t* t_off;   // [nqt + 1] key-tile lists per query tile
+    const int32_t* t_off;   // [nqt + 1] key-tile lists per 256-row query tile
     const int32_t* t_mid;   // [nqt] first PARTIAL entry of each list
     const int32_t* t_ent;   // key tile index | (partial << 31)
     const int32_t* t_order; // [nqt] query tiles, heaviest first
     float* dq_acc;          // fp32 accumulator in the forward's running-output layout
     int32_t B, S, Skv, Hq, Hkv, nqt, S_pad;
-    int32_t total_work;     // B * Hq * nqt
+    int32_t total_work;     // B * Hq * nqt (nqt: 256-row query tiles)
     int32_t first;          // first active step: write instead of add
     float scale;
     float scale_log2;

@@ -128,7 +128,7 @@ typedef struct ring_attn_desc {
  * (plus one partial in RA_MERGE_SEPARATE mode).  Backward: two per-row fp32
  * arrays of B * Hq * S_pad floats (the lse in base 2 and -Delta, Delta =
  * rowsum(dout * out)) and an fp32 dQ accumulator of B * Hq * S_pad * d floats
- * (S_pad = S rounded up to 128; each part starts on a 256-byte boundary). */
+ * (S_pad = S rounded up to 256; each part starts on a 256-byte boundary). */
 int64_t ring_attn_workspace_bytes(const ring_attn_desc* desc, int is_bwd);
 
 /* Forward of the rank share ("Forward Pass Implementation"): for s = 0..D-1
