@@ -208,6 +208,22 @@ def test_bwd_small(layout, head_dim, causal):
         _check_bwd(w, glob, rank, dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
 
 
+@pytest.mark.parametrize("layout,head_dim,causal", [
+    (ca.BASIC, 128, True), (ca.BASIC, 64, False), (ca.ZIGZAG, 128, True), (ca.STRIPE, 128, True),
+    (ca.VARLEN_RING, 128, True)])
+def test_bwd_several_tiles(layout, head_dim, causal):
+    """Shards of 600 rows: three 256-row dQ tiles (the last ragged), five
+    128-row forward tiles, ten 64-row dK/dV query tiles over 128-key tiles with
+    a ragged last block, GQA 4/2."""
+    w = _small_workload(layout, causal, head_dim, D=3, S=600, B=1, seed=40 + layout,
+                        with_grad=True)
+    glob = synth.draw_global(w)
+    for rank in (0, w.world - 1):
+        say(f"bwd several tiles layout={layout} d={head_dim} causal={causal} rank={rank}")
+        dq, dk, dv = _run_bwd(w, glob, rank)
+        _check_bwd(w, glob, rank, dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
+
+
 def test_bwd_ranks_sum_to_full_gradient():
     """dk/dv accumulated over every rank's backward on the same buffers equal
     the full-sequence gradient; the ranks' dq tile the full dq."""
