@@ -58,14 +58,17 @@ __device__ __forceinline__ cint_ptr as_const(const int32_t* p) { return (cint_pt
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // 16-byte slot of logical chunk c in row r of an LDS tile whose rows hold NCH
-// chunks (16: 256-byte rows; 8: 128-byte rows, two rows per bank cycle).  The
-// XOR patterns keep 16 consecutive rows at one chunk, and 4 consecutive rows
-// x 2 chunks, on distinct banks; each pattern is its own inverse.
+// chunks (16: 256-byte rows; 8: 128-byte rows, two rows per 256 bytes).  LDS
+// serves 256 bytes (sixteen 16-byte bank groups) per cycle; the XOR patterns
+// put on distinct bank groups both 16 consecutive rows at one chunk (the
+// 16-lane phases of a ds_read_b128 operand read) and every aligned block of 4
+// rows x 4 chunks (the half-wave phases of a ds_read_b64_tr_b16 transpose
+// read).  Each pattern is its own inverse within a row.
 template <int NCH>
 __device__ __forceinline__ int swz_slot(int r, int c) {
     static_assert(NCH == 16 || NCH == 8, "row width");
-    if (NCH == 16) return c ^ (((r & 7) << 1) | ((r >> 3) & 1));
-    return c ^ ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+    if (NCH == 16) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+    return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 template <int NCH>
 __device__ __forceinline__ int swz_off(int r, int c) {
