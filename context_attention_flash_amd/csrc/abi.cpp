@@ -461,10 +461,19 @@ int ring_attn_fwd(const ring_attn_desc* desc, const void* q, const void* k, cons
         a.lse = lse;
         a.out = out;
         a.B = g.B; a.S = (int32_t)g.S; a.Skv = (int32_t)g.Skv; a.Hq = g.Hq; a.Hkv = g.Hkv;
-        a.nqt = plan->nqt;
+        // the bf16 kernel walks 256-row query tiles, the fp32 one 128-row tiles
+        const bool bf16 = g.dtype == RA_BF16;
+        a.nqt = bf16 ? plan->nqt_dq : plan->nqt;
         a.S_pad = (int32_t)plan->S_pad;
-        a.total_work = g.B * g.Hq * plan->nqt;
+        a.total_work = g.B * g.Hq * a.nqt;
         a.scale_log2 = g.scale * 1.4426950408889634f;
+        auto set_lists = [&](const DevStep& st) {
+            a.rng = st.rng;
+            a.t_off = bf16 ? st.q_off : st.f_off;
+            a.t_mid = bf16 ? st.q_mid : st.f_mid;
+            a.t_ent = bf16 ? st.q_ent : st.f_ent;
+            a.t_order = bf16 ? st.q_order : st.f_order;
+        };
         auto launch_step = [&](const FwdArgs& args) {
             return timed(KC_FWD, s, [&] {
                 return g.dtype == RA_BF16 ? launch_fwd_bf16(args, g.d, s)
@@ -478,7 +487,7 @@ int ring_attn_fwd(const ring_attn_desc* desc, const void* q, const void* k, cons
                 const DevStep& st = plan->steps[i];
                 a.k = (const unsigned char*)k + st.j * block_elems * eb;
                 a.v = (const unsigned char*)v + st.j * block_elems * eb;
-                a.rng = st.rng; a.t_off = st.f_off; a.t_mid = st.f_mid; a.t_ent = st.f_ent; a.t_order = st.f_order;
+                set_lists(st);
                 a.mode = n == 1 ? FWD_SOLO : (i == 0 ? FWD_FIRST : (i + 1 == n ? FWD_LAST : FWD_MERGE));
                 if ((rc = hip_rc(launch_step(a))) != RA_OK) return rc;
             }
@@ -491,7 +500,7 @@ int ring_attn_fwd(const ring_attn_desc* desc, const void* q, const void* k, cons
                 const DevStep& st = plan->steps[i];
                 a.k = (const unsigned char*)k + st.j * block_elems * eb;
                 a.v = (const unsigned char*)v + st.j * block_elems * eb;
-                a.rng = st.rng; a.t_off = st.f_off; a.t_mid = st.f_mid; a.t_ent = st.f_ent; a.t_order = st.f_order;
+                set_lists(st);
                 a.mode = FWD_PARTIAL;
                 a.o_part = i == 0 ? o_run : o_j;
                 a.lse_part = i == 0 ? lse : l_j;

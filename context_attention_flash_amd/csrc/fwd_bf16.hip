@@ -1,6 +1,8 @@
 // K1: one ring step of the flash forward, bf16 inputs, fp32 accumulation.
 //
-// One work-group = one (batch, q head, 128-row query tile); it walks the
+// One work-group = one (batch, q head, 256-row query tile), eight waves of 32
+// rows (two per SIMD, so that one wave's softmax overlaps the other's MFMAs,
+// and each K/V tile in LDS serves eight waves); it walks the
 // step's list of 64-key tiles of block j (instagit/nanotron page, "Forward
 // Pass Implementation": one flash call per ring step) with an online softmax
 // (ai360xpert "Ring Attention", "Online softmax across ring steps") and ends
@@ -35,15 +37,16 @@ namespace ra {
 
 template <int DH>
 struct FwdCfg {
-    static constexpr int NT = 256;
-    static constexpr int BQ = FWD_BQ, BK = FWD_BK;
+    static constexpr int NT = 512;
+    static constexpr int BQ = DQ_BQ, BK = FWD_BK;      // 8 waves x 32 query rows, 64 keys
     static constexpr int NKS = DH / 16;        // MFMA steps over the head dim
     static constexpr int NDT = DH / 32;        // 32-row tiles of O^T
     static constexpr int ROWB = DH * 2;        // bytes of one K row
     static constexpr int KCH = DH / 8;         // 16-byte chunks per K row
     static constexpr int K_BYTES = BK * ROWB;
     static constexpr int OUT_STRIDE = ROWB + 16;          // epilogue staging row
-    static_assert(32 * OUT_STRIDE <= K_BYTES, "a wave stages its output rows in one stage");
+    // a stage array also holds the output rows of two waves in the epilogue
+    static constexpr int STAGE_BYTES = 64 * OUT_STRIDE > K_BYTES ? 64 * OUT_STRIDE : K_BYTES;
 };
 
 typedef short fi16x4_t __attribute__((ext_vector_type(4)));
@@ -56,16 +59,16 @@ __device__ __forceinline__ u32x2_t fwd_tr16(const unsigned char* p) {
 }
 
 template <int DH>
-__global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
+__global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
     using C = FwdCfg<DH>;
     // K and V stages as separate objects, each access naming its stage
     // statically: the compiler can then see that the transpose reads of V
     // never overlap the loads in flight into the other stages (it would
     // otherwise wait for those loads before every transpose read).
-    __shared__ __attribute__((aligned(16))) unsigned char KA[C::K_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char KB[C::K_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char VA[C::K_BYTES];
-    __shared__ __attribute__((aligned(16))) unsigned char VB[C::K_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char KA[C::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char KB[C::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char VA[C::STAGE_BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char VB[C::STAGE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
     for (int ks = 0; ks < C::NKS; ++ks) qreg[ks] = *(const u32x4_t*)(qrow + 16 * ks + 8 * g);
     const int ra = p.rng[2 * iq], rb = p.rng[2 * iq + 1];
 
-    BufTileLoader<DH, C::BK> lk, lv;   // K and V tiles of 64 keys
+    BufTileLoader<DH, C::BK, C::NT> lk, lv;   // K and V tiles of 64 keys
     {
         const int64_t batch = (int64_t)b * p.Skv * p.Hkv * DH;
         lk.init((const uint16_t*)p.k + batch, p.Skv, p.Hkv, hk, wave, lane);
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
     // 32*dt + 8*(r/4) + 4*g + r%4 of query row iq.
     float w_old = 0.f, w_new = inv, L_out = Lj;
     f32x4_t* orun = (f32x4_t*)p.o_run +
-                    (((int64_t)b * p.Hq + h) * (p.S_pad / 32) + (qt * 4 + wave)) * (8 * DH) + lane;
+                    (((int64_t)b * p.Hq + h) * (p.S_pad / 32) + (qt * (C::BQ / 32) + wave)) * (8 * DH) + lane;
     const int mode = p.mode;
     if (mode == FWD_MERGE || mode == FWD_LAST) {
         const float Lr = valid ? p.lse[lse_idx] : -INFINITY;
@@ -312,7 +315,8 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
 
     // FWD_LAST / FWD_SOLO: final bf16 output through LDS for coalesced rows.
     __syncthreads();  // every wave is done with the K/V stages
-    unsigned char* st = wave == 0 ? KA : wave == 1 ? KB : wave == 2 ? VA : VB;
+    unsigned char* st = ((wave & 3) == 0 ? KA : (wave & 3) == 1 ? KB : (wave & 3) == 2 ? VA : VB) +
+                        (wave >> 2) * 32 * C::OUT_STRIDE;
 #pragma unroll
     for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
@@ -341,9 +345,9 @@ __global__ __launch_bounds__(256, 2) void fwd_step_bf16_kernel(FwdArgs p) {
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, hipStream_t s) {
     const int grid = (a.total_work + 7) / 8 * 8;
     if (head_dim == 128)
-        hipLaunchKernelGGL(fwd_step_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(fwd_step_bf16_kernel<128>, dim3(grid), dim3(512), 0, s, a);
     else if (head_dim == 64)
-        hipLaunchKernelGGL(fwd_step_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(fwd_step_bf16_kernel<64>, dim3(grid), dim3(512), 0, s, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

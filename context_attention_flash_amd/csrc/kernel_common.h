@@ -118,10 +118,11 @@ struct BufTileLoader {
     }
 };
 
-// K and V tiles of one kv head (rows = keys of a [B, Skv, Hkv, DH] block).
-template <int DH, int ROWS>
+// K and V tiles of one kv head (rows = keys of a [B, Skv, Hkv, DH] block),
+// loaded by a work-group of NT threads.
+template <int DH, int ROWS, int NT = 256>
 struct KvLoader {
-    BufTileLoader<DH, ROWS> lk, lv;
+    BufTileLoader<DH, ROWS, NT> lk, lv;
     __device__ __forceinline__ void init(const uint16_t* k, const uint16_t* v, int b, int Skv,
                                          int Hkv, int hk, int wave, int lane) {
         const int64_t batch = (int64_t)b * Skv * Hkv * DH;
