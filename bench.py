@@ -86,7 +86,7 @@ def cpu_baseline(w, g, budget_s: float):
         oracle.rank_share_forward(g["q"], g["k"], g["v"], w.layout, w.world, w.rank, w.causal, cu,
                                   rows=rows, heads=[0])
         m = oracle.allowed(pos_q[rows], np.arange(w.seqlen), w.causal,
-                           cu if w.layout in (3, 4) else None)
+                           cu if w.layout in oracle.PACKED else None)
         pairs = float(m.sum())
         flops += 4.0 * w.head_dim * pairs
         if w.with_grad:
@@ -247,7 +247,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic (seeded N(0,1), bf16-rounded)",
-        "config": {"workload": f"{w.name}: {'basic' if w.layout == 0 else w.layout} "
+        "config": {"workload": f"{w.name}: {synth.LAYOUT_NAMES[w.layout]} "
                                f"{'causal' if w.causal else 'non-causal'} "
                                f"{'fwd+bwd' if w.with_grad else 'fwd'} rank share",
                    "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,

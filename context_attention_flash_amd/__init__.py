@@ -15,7 +15,7 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-from .synth import BASIC, ZIGZAG, STRIPE, VARLEN_RING, LLAMA3  # noqa: F401
+from .synth import BASIC, ZIGZAG, STRIPE, VARLEN_RING, LLAMA3, VARLEN_ZIGZAG, VARLEN_STRIPE  # noqa: F401
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn.so")
 

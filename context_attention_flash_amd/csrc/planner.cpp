@@ -23,14 +23,16 @@ int validate(const ring_attn_desc* desc, const int32_t* cu, Geometry* g, bool ch
     if (d.seqlen > (int64_t)(INT_MAX / 2)) return RA_E_SHAPE;
     if (d.heads_q % d.heads_kv != 0) return RA_E_HEADS;
     if (d.world < 1 || d.rank < 0 || d.rank >= d.world) return RA_E_WORLD;
-    if (d.layout < RA_BASIC || d.layout > RA_LLAMA3) return RA_E_LAYOUT;
+    if (d.layout < RA_BASIC || d.layout > RA_VARLEN_STRIPE) return RA_E_LAYOUT;
     if (d.causal != 0 && d.causal != 1) return RA_E_ARG;
     if (d.dtype != RA_F32 && d.dtype != RA_BF16) return RA_E_UNSUPPORTED;
     if (d.merge_mode != RA_MERGE_FUSED && d.merge_mode != RA_MERGE_SEPARATE) return RA_E_ARG;
     if (!(d.softmax_scale == d.softmax_scale)) return RA_E_ARG;  // NaN
-    const bool varlen = d.layout == RA_VARLEN_RING || d.layout == RA_LLAMA3;
+    const bool varlen = d.layout == RA_VARLEN_RING || d.layout == RA_LLAMA3 ||
+                        d.layout == RA_VARLEN_ZIGZAG || d.layout == RA_VARLEN_STRIPE;
     if (varlen && d.batch != 1) return RA_E_LAYOUT;
-    const int64_t div = d.layout == RA_ZIGZAG ? 2LL * d.world : (int64_t)d.world;
+    const bool zz = d.layout == RA_ZIGZAG || d.layout == RA_VARLEN_ZIGZAG;
+    const int64_t div = zz ? 2LL * d.world : (int64_t)d.world;
     if (d.seqlen % div != 0) return RA_E_DIVISIBILITY;
 
     Geometry G;
@@ -51,9 +53,10 @@ int validate(const ring_attn_desc* desc, const int32_t* cu, Geometry* g, bool ch
             if (i > 0 && cu[i] < cu[i - 1]) return RA_E_CU_SEQLENS;
             G.cu[i] = cu[i];
         }
-        if (d.layout == RA_VARLEN_RING)
+        // every document must split evenly into the layout's parts
+        if (d.layout != RA_LLAMA3)
             for (int i = 0; i < d.n_seqs; ++i)
-                if ((G.cu[i + 1] - G.cu[i]) % d.world != 0) return RA_E_CU_SEQLENS;
+                if ((G.cu[i + 1] - G.cu[i]) % div != 0) return RA_E_CU_SEQLENS;
     }
     *g = std::move(G);
     return RA_OK;
@@ -83,6 +86,21 @@ void rank_positions(const Geometry& g, int32_t rank, std::vector<int64_t>& out) 
                 const int64_t part = (g.cu[k + 1] - g.cu[k]) / g.D;
                 for (int64_t i = 0; i < part; ++i) out[o++] = g.cu[k] + rank * part + i;
             }
+            break;
+        }
+        case RA_VARLEN_ZIGZAG: {
+            int64_t o = 0;
+            for (size_t k = 0; k + 1 < g.cu.size(); ++k) {
+                const int64_t c = (g.cu[k + 1] - g.cu[k]) / (2 * g.D);
+                for (int64_t i = 0; i < c; ++i) out[o++] = g.cu[k] + rank * c + i;
+                for (int64_t i = 0; i < c; ++i) out[o++] = g.cu[k] + (2 * g.D - 1 - rank) * c + i;
+            }
+            break;
+        }
+        case RA_VARLEN_STRIPE: {
+            int64_t o = 0;
+            for (size_t k = 0; k + 1 < g.cu.size(); ++k)
+                for (int64_t t = g.cu[k] + rank; t < g.cu[k + 1]; t += g.D) out[o++] = t;
             break;
         }
     }

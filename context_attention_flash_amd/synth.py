@@ -28,9 +28,17 @@ from typing import Optional
 import numpy as np
 
 # Layout codes; the same integers are used by the C ABI.
-BASIC, ZIGZAG, STRIPE, VARLEN_RING, LLAMA3 = 0, 1, 2, 3, 4
+BASIC, ZIGZAG, STRIPE, VARLEN_RING, LLAMA3, VARLEN_ZIGZAG, VARLEN_STRIPE = 0, 1, 2, 3, 4, 5, 6
 LAYOUT_NAMES = {BASIC: "basic", ZIGZAG: "zigzag", STRIPE: "stripe",
-                VARLEN_RING: "varlen_ring", LLAMA3: "llama3"}
+                VARLEN_RING: "varlen_ring", LLAMA3: "llama3",
+                VARLEN_ZIGZAG: "varlen_zigzag", VARLEN_STRIPE: "varlen_stripe"}
+# layouts over packed documents (batch 1, cu_seqlens required)
+VARLEN_LAYOUTS = (VARLEN_RING, LLAMA3, VARLEN_ZIGZAG, VARLEN_STRIPE)
+
+
+def doc_multiple(layout: int, world: int) -> int:
+    """Document lengths a packed layout accepts must be multiples of this."""
+    return {VARLEN_RING: world, VARLEN_STRIPE: world, VARLEN_ZIGZAG: 2 * world}.get(layout, 1)
 
 # Document boundaries of the packed llama3 workload.  They were produced once by
 # ``lognormal_cu_seqlens(65536, 2048, 1.0, 64, 16384, np.random.default_rng(2004))``

@@ -60,13 +60,23 @@ extern "C" {
  *   RA_LLAMA3      query shard as RA_BASIC over the packed stream; the KV is
  *                  the gathered stream (all N tokens, global order), attended
  *                  in a single step with per-document causal masking.
+ *   RA_VARLEN_ZIGZAG packed documents, RA_ZIGZAG applied inside each one:
+ *                  every document (length a multiple of 2D) is cut into 2D
+ *                  chunks and rank r holds chunks r and 2D-1-r of each, in
+ *                  document order ("ring-flash-attn": every variant in batch
+ *                  and varlen form).
+ *   RA_VARLEN_STRIPE packed documents, RA_STRIPE applied inside each one:
+ *                  token a+i of a document starting at a (length a multiple
+ *                  of D) belongs to rank i mod D.
  * KV block j of the ring layouts is exactly what rank j holds. */
 typedef enum {
     RA_BASIC = 0,
     RA_ZIGZAG = 1,
     RA_STRIPE = 2,
     RA_VARLEN_RING = 3,
-    RA_LLAMA3 = 4
+    RA_LLAMA3 = 4,
+    RA_VARLEN_ZIGZAG = 5,
+    RA_VARLEN_STRIPE = 6
 } ra_layout;
 
 /* Element type of q, k, v, out and dout.  Accumulation is always fp32. */
@@ -81,7 +91,7 @@ typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
 typedef enum { RA_MERGE_FUSED = 0, RA_MERGE_SEPARATE = 1 } ra_merge_mode;
 
 typedef struct ring_attn_desc {
-    int32_t batch;         /* B (must be 1 for RA_VARLEN_RING and RA_LLAMA3)   */
+    int32_t batch;         /* B (must be 1 for the packed layouts)   */
     int32_t heads_q;       /* Hq                                               */
     int32_t heads_kv;      /* Hkv; Hq % Hkv == 0; q head h uses kv head h*Hkv/Hq */
     int32_t head_dim;      /* d: 64 or 128                                     */
@@ -101,9 +111,11 @@ typedef struct ring_attn_desc {
 #define RA_E_NULL            -1  /* a required pointer is NULL                 */
 #define RA_E_SHAPE           -2  /* batch/heads/seqlen out of range            */
 #define RA_E_WORLD           -3  /* world < 1 or rank not in [0, world)        */
-#define RA_E_DIVISIBILITY    -4  /* N % D != 0 (N % 2D for zigzag)             */
+#define RA_E_DIVISIBILITY    -4  /* N % D != 0 (N % 2D for both zigzags)       */
 #define RA_E_CU_SEQLENS      -5  /* cu_seqlens not 0 .. N non-decreasing, or a
-                                    varlen-ring document length % D != 0       */
+                                    document length not a multiple of D
+                                    (varlen ring, varlen stripe) or of 2D
+                                    (varlen zigzag)                            */
 #define RA_E_HEADS           -6  /* heads_q % heads_kv != 0                    */
 #define RA_E_UNSUPPORTED     -7  /* no kernel for this head_dim/dtype/mode     */
 #define RA_E_WORKSPACE       -8  /* workspace NULL or smaller than required    */
@@ -120,7 +132,8 @@ typedef struct ring_attn_desc {
  *   dq           : fp32 [B, S, Hq, d]
  *   dk, dv       : fp32, shaped like k and v
  *   cu_seqlens   : host int32 [n_seqs + 1] in global packed coordinates
- *                  (RA_VARLEN_RING and RA_LLAMA3 only; NULL otherwise). */
+ *                  (packed layouts RA_VARLEN_RING, RA_LLAMA3, RA_VARLEN_ZIGZAG
+ *                  and RA_VARLEN_STRIPE only; NULL otherwise). */
 
 /* Bytes of device workspace ring_attn_fwd (is_bwd = 0) or ring_attn_bwd
  * (is_bwd = 1) needs for this descriptor; negative RA_E_* if the descriptor is

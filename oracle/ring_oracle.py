@@ -38,7 +38,9 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-BASIC, ZIGZAG, STRIPE, VARLEN_RING, LLAMA3 = 0, 1, 2, 3, 4
+BASIC, ZIGZAG, STRIPE, VARLEN_RING, LLAMA3, VARLEN_ZIGZAG, VARLEN_STRIPE = 0, 1, 2, 3, 4, 5, 6
+# layouts over packed documents: masks also require the same document
+PACKED = (VARLEN_RING, LLAMA3, VARLEN_ZIGZAG, VARLEN_STRIPE)
 
 
 # ---------------------------------------------------------------------------
@@ -62,6 +64,10 @@ def positions(layout: int, n: int, world: int, rank: int,
                and rank r holds part r of every document, in document order.
     LLAMA3  -- the query shard is the BASIC block r of the packed stream; its
                KV is the gathered stream (see ``kv_positions``).
+    VARLEN_ZIGZAG, VARLEN_STRIPE -- [PF] lists every variant in a packed
+               form as well; read here as the ZIGZAG / STRIPE rule applied to
+               the document-local token index inside every packed document,
+               documents in order.
     """
     if layout in (BASIC, LLAMA3):
         s = n // world
@@ -78,6 +84,12 @@ def positions(layout: int, n: int, world: int, rank: int,
         for a, b in zip(cu_seqlens[:-1], cu_seqlens[1:]):
             part = (b - a) // world
             parts.append(a + rank * part + np.arange(part, dtype=np.int64))
+        return np.concatenate(parts) if parts else np.zeros(0, np.int64)
+    if layout in (VARLEN_ZIGZAG, VARLEN_STRIPE):
+        parts = []
+        for a, b in zip(cu_seqlens[:-1], cu_seqlens[1:]):
+            doc = positions(ZIGZAG if layout == VARLEN_ZIGZAG else STRIPE, b - a, world, rank)
+            parts.append(a + doc)
         return np.concatenate(parts) if parts else np.zeros(0, np.int64)
     raise ValueError(f"unknown layout {layout}")
 
@@ -192,7 +204,7 @@ def rank_share_forward(q_glob, k_glob, v_glob, layout: int, world: int, rank: in
     Hkv = k_glob.shape[2]
     if scale is None:
         scale = default_scale(d)
-    cu = cu_seqlens if layout in (VARLEN_RING, LLAMA3) else None
+    cu = cu_seqlens if layout in PACKED else None
     pos_q = positions(layout, N, world, rank, cu)
     if rows is not None:
         pos_q = pos_q[np.asarray(rows)]
@@ -271,7 +283,7 @@ def ring_forward(q_glob, k_glob, v_glob, layout: int, world: int, rank: int,
     Hkv = k_glob.shape[2]
     if scale is None:
         scale = default_scale(d)
-    cu = cu_seqlens if layout in (VARLEN_RING, LLAMA3) else None
+    cu = cu_seqlens if layout in PACKED else None
     pos_q = positions(layout, N, world, rank, cu)
     S = len(pos_q)
     run_out = None
@@ -329,7 +341,7 @@ def rank_share_backward(q_glob, k_glob, v_glob, dout_local, layout: int, world: 
     Hkv = k_glob.shape[2]
     if scale is None:
         scale = default_scale(d)
-    cu = cu_seqlens if layout in (VARLEN_RING, LLAMA3) else None
+    cu = cu_seqlens if layout in PACKED else None
     pos_q = positions(layout, N, world, rank, cu)
     local = np.arange(len(pos_q)) if rows is None else np.asarray(rows)
     pos_q = pos_q[local]
@@ -378,7 +390,7 @@ def step_pair_counts(layout: int, n: int, world: int, rank: int, causal: bool,
                      cu_seqlens=None):
     """Visible (query row, key) pairs of every ring step, per (batch, q-head):
     a list of (step, block, pairs) in ring order."""
-    cu = cu_seqlens if layout in (VARLEN_RING, LLAMA3) else None
+    cu = cu_seqlens if layout in PACKED else None
     pos_q = positions(layout, n, world, rank, cu)
     steps = [(0, 0)] if layout == LLAMA3 else ring_schedule(world, rank)
     res = []

@@ -18,7 +18,8 @@ import oracle
 from context_attention_flash_amd import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-LAYOUTS = [ca.BASIC, ca.ZIGZAG, ca.STRIPE, ca.VARLEN_RING, ca.LLAMA3]
+LAYOUTS = [ca.BASIC, ca.ZIGZAG, ca.STRIPE, ca.VARLEN_RING, ca.LLAMA3, ca.VARLEN_ZIGZAG,
+           ca.VARLEN_STRIPE]
 
 
 def test_exports_every_declared_symbol():
@@ -32,11 +33,10 @@ def test_exports_every_declared_symbol():
 
 
 def _cu(layout, N, D, rng, n_docs=5):
-    if layout == ca.VARLEN_RING:
-        return synth.random_cu_seqlens(N, n_docs, rng, multiple=D)
-    if layout == ca.LLAMA3:
-        return synth.random_cu_seqlens(N, n_docs, rng)
-    return None
+    if layout not in synth.VARLEN_LAYOUTS:
+        return None
+    m = synth.doc_multiple(layout, D)
+    return synth.random_cu_seqlens(N, min(n_docs, N // m), rng, multiple=m)
 
 
 @pytest.mark.parametrize("layout", LAYOUTS)
@@ -47,7 +47,7 @@ def test_positions_bit_exact(layout, D):
         cu = _cu(layout, N, D, rng)
         for r in range(D):
             desc = ca.make_desc(1, 2, 1, 128, N, D, r, True, layout, cu_seqlens=cu)
-            cu_l = cu if layout in (ca.VARLEN_RING, ca.LLAMA3) else None
+            cu_l = cu if layout in synth.VARLEN_LAYOUTS else None
             got = ca.ring_attn_positions(desc, cu)
             assert got.dtype == np.int64
             assert np.array_equal(got, oracle.positions(layout, N, D, r, cu_l))
@@ -98,7 +98,7 @@ def test_tile_kinds_against_brute_force(layout, causal):
     rng = np.random.default_rng(50 + layout)
     for D, N, tq, tk in ((2, 2 * 2 * 45, 16, 8), (4, 4 * 2 * 40, 32, 16), (3, 3 * 2 * 30, 8, 32)):
         cu = _cu(layout, N, D, rng, n_docs=4)
-        cu_l = cu if layout in (ca.VARLEN_RING, ca.LLAMA3) else None
+        cu_l = cu if layout in synth.VARLEN_LAYOUTS else None
         for r in range(D):
             desc = ca.make_desc(1, 1, 1, 64, N, D, r, causal, layout, cu_seqlens=cu)
             pos_q = oracle.positions(layout, N, D, r, cu_l)
@@ -145,6 +145,10 @@ def test_validation_errors_before_device_work():
         (dict(layout=ca.LLAMA3, cu=[0, 10, 63]), -5), (dict(layout=ca.LLAMA3, cu=[1, 64]), -5),
         (dict(layout=ca.LLAMA3, cu=[0, 40, 30, 64]), -5),
         (dict(layout=ca.VARLEN_RING, cu=[0, 10, 64]), -5),
+        (dict(layout=ca.VARLEN_ZIGZAG, cu=[0, 12, 64]), -5),
+        (dict(layout=ca.VARLEN_ZIGZAG, cu=[0, 16, 64], seqlen=68), -4),
+        (dict(layout=ca.VARLEN_STRIPE, cu=[0, 6, 64]), -5),
+        (dict(layout=ca.VARLEN_STRIPE, batch=2, cu=[0, 64]), -9),
         (dict(head_dim=96), -7), (dict(dtype=5), -7),
     ]
     for kw, code in cases:

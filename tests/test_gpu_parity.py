@@ -16,15 +16,17 @@ from _helpers import max_err_lse, say, shard, to_dev, tol
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-LAYOUTS = [ca.BASIC, ca.ZIGZAG, ca.STRIPE, ca.VARLEN_RING, ca.LLAMA3]
+LAYOUTS = [ca.BASIC, ca.ZIGZAG, ca.STRIPE, ca.VARLEN_RING, ca.LLAMA3, ca.VARLEN_ZIGZAG,
+           ca.VARLEN_STRIPE]
 
 
 def _small_workload(layout, causal, head_dim, dtype="bf16", D=4, S=200, B=2, Hq=4, Hkv=2,
                     seed=0, with_grad=False):
     N = D * S
     cu = None
-    if layout == ca.VARLEN_RING:
-        cu = tuple(synth.random_cu_seqlens(N, 3, np.random.default_rng(seed + 7), multiple=D))
+    if layout in (ca.VARLEN_RING, ca.VARLEN_ZIGZAG, ca.VARLEN_STRIPE):
+        cu = tuple(synth.random_cu_seqlens(N, 3, np.random.default_rng(seed + 7),
+                                           multiple=synth.doc_multiple(layout, D)))
         B = 1
     elif layout == ca.LLAMA3:
         cu = tuple(synth.random_cu_seqlens(N, 4, np.random.default_rng(seed + 7)))
@@ -210,7 +212,7 @@ def test_bwd_small(layout, head_dim, causal):
 
 @pytest.mark.parametrize("layout,head_dim,causal", [
     (ca.BASIC, 128, True), (ca.BASIC, 64, False), (ca.ZIGZAG, 128, True), (ca.STRIPE, 128, True),
-    (ca.VARLEN_RING, 128, True)])
+    (ca.VARLEN_RING, 128, True), (ca.VARLEN_ZIGZAG, 128, True), (ca.VARLEN_STRIPE, 64, True)])
 def test_bwd_several_tiles(layout, head_dim, causal):
     """Shards of 600 rows: three 256-row dQ tiles (the last ragged), five
     128-row forward tiles, ten 64-row dK/dV query tiles over 128-key tiles with

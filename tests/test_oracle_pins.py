@@ -24,18 +24,19 @@ import pytest
 import torch
 
 import oracle
-from oracle import BASIC, ZIGZAG, STRIPE, VARLEN_RING, LLAMA3
+from oracle import BASIC, ZIGZAG, STRIPE, VARLEN_RING, LLAMA3, VARLEN_ZIGZAG, VARLEN_STRIPE, PACKED
 from context_attention_flash_amd import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
-LAYOUTS = [BASIC, ZIGZAG, STRIPE, VARLEN_RING, LLAMA3]
+LAYOUTS = [BASIC, ZIGZAG, STRIPE, VARLEN_RING, LLAMA3, VARLEN_ZIGZAG, VARLEN_STRIPE]
 
 
 def _cu_for(layout, n, world, rng):
-    if layout == VARLEN_RING:
-        return synth.random_cu_seqlens(n, 3, rng, multiple=world)
     if layout == LLAMA3:
         return synth.random_cu_seqlens(n, 4, rng)
+    if layout in PACKED:
+        m = synth.doc_multiple(layout, world)
+        return synth.random_cu_seqlens(n, min(3, n // m), rng, multiple=m)
     return None
 
 
@@ -110,7 +111,7 @@ def _sdpa_reference(q, k, v, dout_local, layout, world, rank, causal, cu):
     restricted to the rank's rows; gradients by autograd."""
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
-    cu_l = cu if layout in (VARLEN_RING, LLAMA3) else None
+    cu_l = cu if layout in PACKED else None
     pos_q = oracle.positions(layout, N, world, rank, cu_l)
     # mask from the definition on global positions, written out here directly
     t = np.arange(N)
@@ -150,7 +151,7 @@ def test_forward_and_grads_match_torch_sdpa(layout, causal):
     rng = np.random.default_rng(100 + layout * 2 + causal)
     world, B, Hq, Hkv, d = 4, 2, 4, 2, 8
     N = 48
-    if layout in (VARLEN_RING, LLAMA3):
+    if layout in PACKED:
         B = 1
     cu = _cu_for(layout, N, world, rng)
     q, k, v = _inputs(rng, B, N, Hq, Hkv, d)
@@ -185,7 +186,7 @@ def test_d1_reduces_to_plain_attention():
 def test_ring_equals_unblocked(layout, world, causal):
     rng = np.random.default_rng(1000 + 10 * layout + world + 100 * causal)
     N = 2 * world * 5
-    B = 1 if layout in (VARLEN_RING, LLAMA3) else 2
+    B = 1 if layout in PACKED else 2
     if layout == VARLEN_RING and N // world < 3:
         N = world * 6
     cu = _cu_for(layout, N, world, rng)
@@ -267,7 +268,7 @@ def test_brute_force_tiny(layout):
     q, k, v = _inputs(rng, B, N, 2, 1, 4)
     for causal in (True, False):
         for r in range(D):
-            cu_l = cu if layout in (VARLEN_RING, LLAMA3) else None
+            cu_l = cu if layout in PACKED else None
             pos_q = oracle.positions(layout, N, D, r, cu_l)
             bo, bl = _brute(q, k, v, pos_q, causal, cu_l, 0.5)
             o, l = oracle.rank_share_forward(q, k, v, layout, D, r, causal, cu, scale=0.5)
@@ -289,9 +290,9 @@ def test_zero_query_gives_mean_and_log_count(layout, causal):
     (varlen) without the causal mask."""
     rng = np.random.default_rng(77 + layout)
     N, D = 32, 4
-    B = 1 if layout in (VARLEN_RING, LLAMA3) else 2
+    B = 1 if layout in PACKED else 2
     cu = _cu_for(layout, N, D, rng)
-    cu_l = cu if layout in (VARLEN_RING, LLAMA3) else None
+    cu_l = cu if layout in PACKED else None
     q, k, v = _inputs(rng, B, N, 2, 2, 8)
     q[:] = 0.0
     for r in range(D):
@@ -332,7 +333,7 @@ def test_identity_v_gives_probability_matrix(layout):
     rng = np.random.default_rng(21 + layout)
     N, D = 16, 2
     cu = _cu_for(layout, N, D, rng)
-    cu_l = cu if layout in (VARLEN_RING, LLAMA3) else None
+    cu_l = cu if layout in PACKED else None
     q = rng.standard_normal((1, N, 1, N))
     k = rng.standard_normal((1, N, 1, N))
     v = np.eye(N)[None, :, None, :]
@@ -383,13 +384,13 @@ def test_gradients_by_central_differences(layout):
     B = 1
     cu = _cu_for(layout, N, D, rng)
     q, k, v = _inputs(rng, B, N, 2, 1, 4)
-    S = len(oracle.positions(layout, N, D, r, cu if layout in (VARLEN_RING, LLAMA3) else None))
+    S = len(oracle.positions(layout, N, D, r, cu if layout in PACKED else None))
     dout = rng.standard_normal((B, S, 2, 4))
     dq, dk, dv = oracle.rank_share_backward(q, k, v, dout, layout, D, r, True, cu)
     nb = oracle.num_blocks(layout, D)
-    blocks = [oracle.kv_positions(layout, N, D, j, cu if layout in (VARLEN_RING, LLAMA3) else None)
+    blocks = [oracle.kv_positions(layout, N, D, j, cu if layout in PACKED else None)
               for j in range(nb)]
-    cu_l = cu if layout in (VARLEN_RING, LLAMA3) else None
+    cu_l = cu if layout in PACKED else None
     pos_q = oracle.positions(layout, N, D, r, cu_l)
 
     def loss(q_, k_, v_):
@@ -428,7 +429,7 @@ def test_rank_gradients_sum_to_full_gradient(layout):
     N, D = 24, 3 if layout != ZIGZAG else 2
     N = 24
     cu = _cu_for(layout, N, D, rng)
-    cu_l = cu if layout in (VARLEN_RING, LLAMA3) else None
+    cu_l = cu if layout in PACKED else None
     q, k, v = _inputs(rng, 1, N, 4, 2, 8)
     dout_g = rng.standard_normal((1, N, 4, 8))
     full = _sdpa_reference(q, k, v, dout_g, BASIC if cu_l is None else LLAMA3, 1, 0, True, cu)
@@ -460,7 +461,7 @@ def test_layout_is_a_bijection(layout, world):
     rng = np.random.default_rng(5)
     N = 2 * world * 6
     cu = _cu_for(layout, N, world, rng)
-    cu_l = cu if layout in (VARLEN_RING, LLAMA3) else None
+    cu_l = cu if layout in PACKED else None
     allpos = np.concatenate([oracle.positions(layout, N, world, r, cu_l) for r in range(world)])
     assert np.array_equal(np.sort(allpos), np.arange(N))
     for r in range(world):
@@ -483,6 +484,33 @@ def test_zigzag_and_stripe_pair_counts():
         counts = oracle.step_pair_counts(BASIC, N, D, r, True)
         for s, j, pairs in counts:
             assert pairs == (S * (S + 1) // 2 if s == 0 else (S * S if s <= r else 0))
+
+
+def test_varlen_zigzag_and_stripe_pair_counts():
+    """Documents never see each other, so the packed forms' causal pair counts
+    are the per-document closed forms of ZIGZAG / STRIPE summed over the
+    documents; every rank also holds exactly L/D tokens of each document."""
+    D = 4
+    cu = [0, 8, 40, 64, 128]  # document lengths 8, 32, 24, 64: multiples of 2D
+    N = cu[-1]
+    lens = np.diff(cu)
+    for r in range(D):
+        for layout in (VARLEN_ZIGZAG, VARLEN_STRIPE):
+            p = oracle.positions(layout, N, D, r, cu)
+            per_doc = np.histogram(p, bins=cu)[0]
+            assert np.array_equal(per_doc, lens // D)
+        for s, j, pairs in oracle.step_pair_counts(VARLEN_ZIGZAG, N, D, r, True, cu):
+            c = lens // (2 * D)
+            assert pairs == int((2 * c * c + (c if s == 0 else 0)).sum())
+        for s, j, pairs in oracle.step_pair_counts(VARLEN_STRIPE, N, D, r, True, cu):
+            Sk = lens // D
+            assert pairs == int((Sk * (Sk + 1) // 2 if j <= r else Sk * (Sk - 1) // 2).sum())
+    # a single document is the batch form
+    for r in range(D):
+        assert np.array_equal(oracle.positions(VARLEN_ZIGZAG, N, D, r, [0, N]),
+                              oracle.positions(ZIGZAG, N, D, r))
+        assert np.array_equal(oracle.positions(VARLEN_STRIPE, N, D, r, [0, N]),
+                              oracle.positions(STRIPE, N, D, r))
 
 
 def test_workload_pair_totals():
