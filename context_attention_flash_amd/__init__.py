@@ -35,7 +35,8 @@ class RingAttnDesc(ctypes.Structure):
         ("head_dim", ctypes.c_int32), ("seqlen", ctypes.c_int64), ("world", ctypes.c_int32),
         ("rank", ctypes.c_int32), ("causal", ctypes.c_int32), ("layout", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("n_seqs", ctypes.c_int32),
-        ("merge_mode", ctypes.c_int32),
+        ("merge_mode", ctypes.c_int32), ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
     ]
 
 
@@ -100,7 +101,7 @@ def ring_attn_version() -> int:
 
 def make_desc(batch, heads_q, heads_kv, head_dim, seqlen, world, rank, causal, layout,
               dtype="bf16", softmax_scale=0.0, cu_seqlens: Optional[Sequence[int]] = None,
-              merge_mode=RA_MERGE_FUSED) -> RingAttnDesc:
+              merge_mode=RA_MERGE_FUSED, window=(-1, -1)) -> RingAttnDesc:
     d = RingAttnDesc()
     d.batch, d.heads_q, d.heads_kv, d.head_dim = batch, heads_q, heads_kv, head_dim
     d.seqlen, d.world, d.rank, d.causal, d.layout = seqlen, world, rank, int(causal), layout
@@ -108,13 +109,14 @@ def make_desc(batch, heads_q, heads_kv, head_dim, seqlen, world, rank, causal, l
     d.softmax_scale = float(softmax_scale)
     d.n_seqs = 0 if cu_seqlens is None else len(cu_seqlens) - 1
     d.merge_mode = merge_mode
+    d.window_left, d.window_right = int(window[0]), int(window[1])
     return d
 
 
 def desc_from_workload(w, rank=None, merge_mode=RA_MERGE_FUSED) -> RingAttnDesc:
     return make_desc(w.batch, w.heads_q, w.heads_kv, w.head_dim, w.seqlen, w.world,
                      w.rank if rank is None else rank, w.causal, w.layout, w.dtype,
-                     cu_seqlens=w.cu_seqlens, merge_mode=merge_mode)
+                     cu_seqlens=w.cu_seqlens, merge_mode=merge_mode, window=w.window)
 
 
 def _cu_arg(cu):

@@ -28,6 +28,7 @@ int validate(const ring_attn_desc* desc, const int32_t* cu, Geometry* g, bool ch
     if (d.dtype != RA_F32 && d.dtype != RA_BF16) return RA_E_UNSUPPORTED;
     if (d.merge_mode != RA_MERGE_FUSED && d.merge_mode != RA_MERGE_SEPARATE) return RA_E_ARG;
     if (!(d.softmax_scale == d.softmax_scale)) return RA_E_ARG;  // NaN
+    if (d.window_left < -1 || d.window_right < -1) return RA_E_ARG;
     const bool varlen = d.layout == RA_VARLEN_RING || d.layout == RA_LLAMA3 ||
                         d.layout == RA_VARLEN_ZIGZAG || d.layout == RA_VARLEN_STRIPE;
     if (varlen && d.batch != 1) return RA_E_LAYOUT;
@@ -44,6 +45,8 @@ int validate(const ring_attn_desc* desc, const int32_t* cu, Geometry* g, bool ch
     G.Skv = d.layout == RA_LLAMA3 ? d.seqlen : G.S;
     G.nb = d.layout == RA_LLAMA3 ? 1 : d.world;
     G.varlen = varlen;
+    G.win_left = d.window_left;
+    G.win_right = d.window_right;
     if (varlen && check_cu) {
         if (!cu) return RA_E_NULL;
         if (d.n_seqs < 1) return RA_E_CU_SEQLENS;
@@ -132,7 +135,9 @@ void step_ranges(const Geometry& g, int32_t s, StepRanges& out) {
             lo = *(it - 1);
             hi = *it - 1;
         }
-        if (g.causal) hi = t;
+        if (g.causal) hi = std::min(hi, t);
+        if (g.win_left >= 0) lo = std::max(lo, t - g.win_left);
+        if (g.win_right >= 0) hi = std::min(hi, t + g.win_right);
         const int64_t a = std::lower_bound(pk.begin(), pk.end(), lo) - pk.begin();
         const int64_t b = std::upper_bound(pk.begin(), pk.end(), hi) - pk.begin();
         out.a[i] = (int32_t)a;
@@ -174,7 +179,8 @@ void classify(const StepRanges& sr, int64_t S, int64_t Skv, int32_t bq, int32_t 
 std::string plan_key(const Geometry& g) {
     // The schedule and tile lists depend only on the token geometry.
     std::ostringstream o;
-    o << g.N << ',' << g.D << ',' << g.r << ',' << g.causal << ',' << g.layout;
+    o << g.N << ',' << g.D << ',' << g.r << ',' << g.causal << ',' << g.layout << ','
+      << g.win_left << ',' << g.win_right;
     if (g.varlen) {
         o << '|';
         for (int64_t c : g.cu) o << c << ',';

@@ -26,6 +26,8 @@ struct Geometry {
     int32_t nb = 1;             // number of KV blocks (ring steps)
     bool varlen = false;
     std::vector<int64_t> cu;    // cu_seqlens (varlen layouts only)
+    int64_t win_left = -1;      // sliding window sides, -1 = unbounded
+    int64_t win_right = -1;
 };
 
 // Validates the descriptor (and cu_seqlens when the layout is varlen).

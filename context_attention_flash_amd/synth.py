@@ -40,6 +40,7 @@ def doc_multiple(layout: int, world: int) -> int:
     """Document lengths a packed layout accepts must be multiples of this."""
     return {VARLEN_RING: world, VARLEN_STRIPE: world, VARLEN_ZIGZAG: 2 * world}.get(layout, 1)
 
+
 # Document boundaries of the packed llama3 workload.  They were produced once by
 # ``lognormal_cu_seqlens(65536, 2048, 1.0, 64, 16384, np.random.default_rng(2004))``
 # with numpy 2.2 and are kept literally so that the workload does not depend on
@@ -65,6 +66,7 @@ class Workload:
     value_scale: float = 1.0
     cu_seqlens: Optional[tuple] = None
     with_grad: bool = False
+    window: tuple = (-1, -1)   # sliding window (left, right); -1 = unbounded side
 
     @property
     def shard(self) -> int:

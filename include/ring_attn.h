@@ -104,6 +104,14 @@ typedef struct ring_attn_desc {
     float softmax_scale;   /* <= 0 selects 1/sqrt(head_dim)                    */
     int32_t n_seqs;        /* number of packed documents (varlen layouts), else 0 */
     int32_t merge_mode;    /* ra_merge_mode                                    */
+    int32_t window_left;   /* sliding window: key u visible to query t only if */
+    int32_t window_right;  /* t-left <= u <= t+right (global positions); -1 on
+                            * a side leaves that side unbounded, so (-1, -1) is
+                            * plain attention.  Values below -1 are RA_E_ARG.
+                            * ("Ring Attention for Long Sequences in Nanotron":
+                            * the window_size argument of the call interface,
+                            * (-1, -1) = unbounded.)  Combined with the causal
+                            * and document rules by AND.                       */
 } ring_attn_desc;
 
 /* Error codes. */

@@ -34,7 +34,7 @@ with autograd.
 from __future__ import annotations
 
 import math
-from typing import Optional, Sequence
+from typing import Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -119,18 +119,31 @@ def doc_index(pos: np.ndarray, cu_seqlens: Optional[Sequence[int]]) -> np.ndarra
 
 
 def allowed(pos_q: np.ndarray, pos_k: np.ndarray, causal: bool,
-            cu_seqlens: Optional[Sequence[int]] = None) -> np.ndarray:
+            cu_seqlens: Optional[Sequence[int]] = None,
+            window: Tuple[int, int] = (-1, -1)) -> np.ndarray:
     """Boolean [len(pos_q), len(pos_k)] mask on *global* positions.
 
     A key is visible to a query when it is not in the query's future (causal)
     and lies in the same packed document (varlen).  The mask is decided by
     global positions, not by positions inside a block ([RA] "Watch Out For").
+
+    ``window`` = (left, right) is the sliding window of the call interface
+    ([NT] "Calling the Ring Attention Function Directly" shows the argument,
+    with (-1, -1) meaning an unbounded window).  Reading: a key at global
+    position u is visible to the query at t only if t - left <= u (when
+    left >= 0) and u <= t + right (when right >= 0), on top of the causal and
+    document rules.
     """
     m = np.ones((len(pos_q), len(pos_k)), dtype=bool)
     if causal:
         m &= pos_k[None, :] <= pos_q[:, None]
     if cu_seqlens is not None:
         m &= doc_index(pos_k, cu_seqlens)[None, :] == doc_index(pos_q, cu_seqlens)[:, None]
+    left, right = window
+    if left >= 0:
+        m &= pos_k[None, :] >= pos_q[:, None] - left
+    if right >= 0:
+        m &= pos_k[None, :] <= pos_q[:, None] + right
     return m
 
 
@@ -190,7 +203,8 @@ def _row_chunks(n_rows: int, n_keys: int, budget: int = 1 << 24):
 
 def rank_share_forward(q_glob, k_glob, v_glob, layout: int, world: int, rank: int,
                        causal: bool, cu_seqlens=None, scale: Optional[float] = None,
-                       rows: Optional[np.ndarray] = None, heads: Optional[Sequence[int]] = None):
+                       rows: Optional[np.ndarray] = None, heads: Optional[Sequence[int]] = None,
+                       window: Tuple[int, int] = (-1, -1)):
     """Expected (out, lse) of rank ``rank``: plain attention of the rank's query
     rows over every key of the global sequence, with the global-position mask.
 
@@ -213,7 +227,7 @@ def rank_share_forward(q_glob, k_glob, v_glob, layout: int, world: int, rank: in
     out = np.zeros((B, S, Hq, d), np.float64)
     lse = np.zeros((B, Hq, S), np.float64)
     for a, b in _row_chunks(S, N):
-        mask = allowed(pos_q[a:b], pos_k, causal, cu)
+        mask = allowed(pos_q[a:b], pos_k, causal, cu, window)
         for bi in range(B):
             for h in (range(Hq) if heads is None else heads):
                 hk = kv_head_of(h, Hq, Hkv)
@@ -269,7 +283,7 @@ def ring_schedule(world: int, rank: int):
 
 def ring_forward(q_glob, k_glob, v_glob, layout: int, world: int, rank: int,
                  causal: bool, cu_seqlens=None, scale: Optional[float] = None,
-                 partial_out: Optional[list] = None):
+                 partial_out: Optional[list] = None, window: Tuple[int, int] = (-1, -1)):
     """Ring-decomposed (out, lse) of rank ``rank``: one partial attention per
     ring step against the block held at that step, folded in ring order with
     ``lse_merge`` ([NT] "Forward Pass Implementation").
@@ -293,7 +307,7 @@ def ring_forward(q_glob, k_glob, v_glob, layout: int, world: int, rank: int,
         if layout == BASIC and causal and s > rank:
             continue
         pos_k = kv_positions(layout, N, world, j, cu)
-        mask = allowed(pos_q, pos_k, causal, cu)
+        mask = allowed(pos_q, pos_k, causal, cu, window)
         o = np.zeros((B, Hq, S, d))
         l = np.zeros((B, Hq, S))
         for bi in range(B):
@@ -317,7 +331,8 @@ def ring_forward(q_glob, k_glob, v_glob, layout: int, world: int, rank: int,
 def rank_share_backward(q_glob, k_glob, v_glob, dout_local, layout: int, world: int,
                         rank: int, causal: bool, cu_seqlens=None,
                         scale: Optional[float] = None, rows: Optional[np.ndarray] = None,
-                        heads: Optional[Sequence[int]] = None):
+                        heads: Optional[Sequence[int]] = None,
+                        window: Tuple[int, int] = (-1, -1)):
     """Gradients of  sum(dout * out)  over the rank's rows.
 
     With P_tu = exp(scale <q_t,k_u> - lse_t) on visible pairs (0 elsewhere) and
@@ -347,7 +362,7 @@ def rank_share_backward(q_glob, k_glob, v_glob, dout_local, layout: int, world: 
     pos_q = pos_q[local]
     S = len(pos_q)
     pos_k = np.arange(N, dtype=np.int64)
-    mask = allowed(pos_q, pos_k, causal, cu)
+    mask = allowed(pos_q, pos_k, causal, cu, window)
     nb = num_blocks(layout, world)
     blocks = [kv_positions(layout, N, world, j, cu) for j in range(nb)]
     dq = np.zeros((B, S, Hq, d))
@@ -387,7 +402,7 @@ def rank_share_backward(q_glob, k_glob, v_glob, dout_local, layout: int, world: 
 # ---------------------------------------------------------------------------
 
 def step_pair_counts(layout: int, n: int, world: int, rank: int, causal: bool,
-                     cu_seqlens=None):
+                     cu_seqlens=None, window: Tuple[int, int] = (-1, -1)):
     """Visible (query row, key) pairs of every ring step, per (batch, q-head):
     a list of (step, block, pairs) in ring order."""
     cu = cu_seqlens if layout in PACKED else None
@@ -398,6 +413,6 @@ def step_pair_counts(layout: int, n: int, world: int, rank: int, causal: bool,
         pos_k = kv_positions(layout, n, world, j, cu)
         total = 0
         for a, b in _row_chunks(len(pos_q), len(pos_k)):
-            total += int(allowed(pos_q[a:b], pos_k, causal, cu).sum())
+            total += int(allowed(pos_q[a:b], pos_k, causal, cu, window).sum())
         res.append((s, j, total))
     return res

@@ -58,18 +58,19 @@ def test_positions_bit_exact(layout, D):
 
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("causal", [True, False])
-def test_schedule_matches_oracle_pair_counts(layout, causal):
+@pytest.mark.parametrize("window", [(-1, -1), (17, -1), (9, 30), (-1, 5), (0, 0)])
+def test_schedule_matches_oracle_pair_counts(layout, causal, window):
     rng = np.random.default_rng(3 + layout)
     for D in (1, 2, 4, 8):
         N = 2 * D * 24
         cu = _cu(layout, N, D, rng)
         for r in range(D):
-            desc = ca.make_desc(2, 4, 2, 64, N, D, r, causal, layout if cu is None else layout,
-                                cu_seqlens=cu)
+            desc = ca.make_desc(2, 4, 2, 64, N, D, r, causal, layout, cu_seqlens=cu,
+                                window=window)
             if cu is not None:
                 desc.batch = 1
             got = ca.ring_attn_schedule(desc, cu)
-            ref = oracle.step_pair_counts(layout, N, D, r, causal, cu)
+            ref = oracle.step_pair_counts(layout, N, D, r, causal, cu, window)
             assert got == ref
 
 
@@ -94,17 +95,19 @@ def test_workload_pair_totals_from_library():
 
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("causal", [True, False])
-def test_tile_kinds_against_brute_force(layout, causal):
+@pytest.mark.parametrize("window", [(-1, -1), (21, 13)])
+def test_tile_kinds_against_brute_force(layout, causal, window):
     rng = np.random.default_rng(50 + layout)
     for D, N, tq, tk in ((2, 2 * 2 * 45, 16, 8), (4, 4 * 2 * 40, 32, 16), (3, 3 * 2 * 30, 8, 32)):
         cu = _cu(layout, N, D, rng, n_docs=4)
         cu_l = cu if layout in synth.VARLEN_LAYOUTS else None
         for r in range(D):
-            desc = ca.make_desc(1, 1, 1, 64, N, D, r, causal, layout, cu_seqlens=cu)
+            desc = ca.make_desc(1, 1, 1, 64, N, D, r, causal, layout, cu_seqlens=cu,
+                                window=window)
             pos_q = oracle.positions(layout, N, D, r, cu_l)
             for s, j, _ in ca.ring_attn_schedule(desc, cu):
                 pos_k = oracle.kv_positions(layout, N, D, j, cu_l)
-                m = oracle.allowed(pos_q, pos_k, causal, cu_l)
+                m = oracle.allowed(pos_q, pos_k, causal, cu_l, window)
                 kinds = ca.ring_attn_tile_kinds(desc, cu, s, tq, tk)
                 for qt in range(kinds.shape[0]):
                     for kt in range(kinds.shape[1]):
@@ -150,6 +153,7 @@ def test_validation_errors_before_device_work():
         (dict(layout=ca.VARLEN_STRIPE, cu=[0, 6, 64]), -5),
         (dict(layout=ca.VARLEN_STRIPE, batch=2, cu=[0, 64]), -9),
         (dict(head_dim=96), -7), (dict(dtype=5), -7),
+        (dict(window=(-2, -1)), -11), (dict(window=(3, -5)), -11),
     ]
     for kw, code in cases:
         desc, cu = d(**kw)

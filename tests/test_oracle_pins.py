@@ -106,7 +106,7 @@ def test_planted_sign_error_in_merge_fails_example(monkeypatch):
 # torch fp64 SDPA + autograd (independent library routine)
 # ---------------------------------------------------------------------------
 
-def _sdpa_reference(q, k, v, dout_local, layout, world, rank, causal, cu):
+def _sdpa_reference(q, k, v, dout_local, layout, world, rank, causal, cu, window=(-1, -1)):
     """Full-sequence attention by torch SDPA in fp64 with an explicit mask,
     restricted to the rank's rows; gradients by autograd."""
     B, N, Hq, d = q.shape
@@ -123,6 +123,11 @@ def _sdpa_reference(q, k, v, dout_local, layout, world, rank, causal, cu):
         for i, (a, b) in enumerate(zip(cu_l[:-1], cu_l[1:])):
             doc[a:b] = i
         mask &= doc[None, :] == doc[:, None]
+    for i in range(N):  # sliding window, row by row
+        if window[0] >= 0:
+            mask[i, :max(0, i - window[0])] = False
+        if window[1] >= 0:
+            mask[i, i + window[1] + 1:] = False
     qt = torch.tensor(q, dtype=torch.float64, requires_grad=True)
     kt = torch.tensor(k, dtype=torch.float64, requires_grad=True)
     vt = torch.tensor(v, dtype=torch.float64, requires_grad=True)
@@ -283,11 +288,13 @@ def test_brute_force_tiny(layout):
 
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("causal", [True, False])
-def test_zero_query_gives_mean_and_log_count(layout, causal):
+@pytest.mark.parametrize("window", [(-1, -1), (5, -1), (3, 2), (-1, 4)])
+def test_zero_query_gives_mean_and_log_count(layout, causal, window):
     """Q = 0: every visible score is 0, so out_t = mean of the visible v_u and
-    lse_t = ln(#visible_t).  #visible_t = t + 1 for causal batch mode,
-    t - doc_start + 1 for causal varlen, N (batch) or the document length
-    (varlen) without the causal mask."""
+    lse_t = ln(#visible_t).  The visible keys are the interval from
+    max(doc_start, t - left) to min(t, doc_end - 1, t + right) (the causal and
+    window bounds only where they apply); doc_start = 0, doc_end = N in batch
+    mode."""
     rng = np.random.default_rng(77 + layout)
     N, D = 32, 4
     B = 1 if layout in PACKED else 2
@@ -297,7 +304,7 @@ def test_zero_query_gives_mean_and_log_count(layout, causal):
     q[:] = 0.0
     for r in range(D):
         pos_q = oracle.positions(layout, N, D, r, cu_l)
-        o, l = oracle.ring_forward(q, k, v, layout, D, r, causal, cu)
+        o, l = oracle.ring_forward(q, k, v, layout, D, r, causal, cu, window=window)
         for i, t in enumerate(pos_q):
             if cu_l is None:
                 start, end = 0, N
@@ -305,10 +312,68 @@ def test_zero_query_gives_mean_and_log_count(layout, causal):
                 di = int(np.searchsorted(cu_l, t, side="right") - 1)
                 start, end = cu_l[di], cu_l[di + 1]
             hi = t + 1 if causal else end
+            if window[0] >= 0:
+                start = max(start, t - window[0])
+            if window[1] >= 0:
+                hi = min(hi, t + window[1] + 1)
             cnt = hi - start
             assert np.allclose(l[:, :, i], math.log(cnt), atol=1e-13, rtol=0)
             for h in range(2):
                 assert np.allclose(o[:, i, h], v[:, start:hi, h].mean(axis=1), atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_window_of_one_token_is_the_token_itself(layout):
+    """A window (0, 0) (or left 0 under the causal mask) leaves each query only
+    its own key: out_t = v_t and lse_t = scale <q_t, k_t>, for every rank."""
+    rng = np.random.default_rng(91 + layout)
+    N, D, d = 48, 4, 8
+    B = 1 if layout in PACKED else 2
+    cu = _cu_for(layout, N, D, rng)
+    cu_l = cu if layout in PACKED else None
+    q, k, v = _inputs(rng, B, N, 4, 2, d)
+    for causal, window in ((True, (0, -1)), (False, (0, 0)), (True, (0, 7))):
+        for r in range(D):
+            pos_q = oracle.positions(layout, N, D, r, cu_l)
+            o, l = oracle.ring_forward(q, k, v, layout, D, r, causal, cu, window=window)
+            o2, l2 = oracle.rank_share_forward(q, k, v, layout, D, r, causal, cu, window=window)
+            for h in range(4):
+                hk = h // 2
+                assert np.abs(o[:, :, h] - v[:, pos_q, hk]).max() < 1e-14
+                assert np.abs(o2[:, :, h] - v[:, pos_q, hk]).max() < 1e-14
+                dots = (q[:, pos_q, h] * k[:, pos_q, hk]).sum(-1) / math.sqrt(d)
+                assert np.abs(l[:, h] - dots).max() < 1e-13
+                assert np.abs(l2[:, h] - dots).max() < 1e-13
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("causal,window", [(True, (6, -1)), (False, (5, 3)), (False, (-1, 2))])
+def test_window_matches_torch_sdpa_and_ring(layout, causal, window):
+    """Windowed rank shares against torch fp64 SDPA with the window mask built
+    row by row in the test, forward and gradients; the ring decomposition
+    matches as well; a window wider than the sequence is plain attention."""
+    rng = np.random.default_rng(300 + layout * 3 + causal)
+    world, N, d = 4, 48, 8
+    B = 1 if layout in PACKED else 2
+    cu = _cu_for(layout, N, world, rng)
+    q, k, v = _inputs(rng, B, N, 4, 2, d)
+    for rank in range(world):
+        S = len(oracle.positions(layout, N, world, rank, cu if layout in PACKED else None))
+        dout = rng.standard_normal((B, S, 4, d))
+        ref = _sdpa_reference(q, k, v, dout, layout, world, rank, causal, cu, window)
+        out, lse = oracle.rank_share_forward(q, k, v, layout, world, rank, causal, cu, window=window)
+        assert np.abs(out - ref["out"]).max() < 1e-12
+        ring, lr = oracle.ring_forward(q, k, v, layout, world, rank, causal, cu, window=window)
+        assert np.abs(ring - out).max() < 1e-12 and np.abs(lr - lse).max() < 1e-12
+        dq, dk, dv = oracle.rank_share_backward(q, k, v, dout, layout, world, rank, causal, cu,
+                                                window=window)
+        assert np.abs(dq - ref["dq"]).max() < 1e-11
+        assert np.abs(dk - ref["dk"]).max() < 1e-11
+        assert np.abs(dv - ref["dv"]).max() < 1e-11
+        wide, _ = oracle.rank_share_forward(q, k, v, layout, world, rank, causal, cu,
+                                            window=(N, N))
+        plain, _ = oracle.rank_share_forward(q, k, v, layout, world, rank, causal, cu)
+        assert np.array_equal(wide, plain)
 
 
 def test_constant_v_and_rows_sum_to_one():
