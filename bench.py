@@ -129,10 +129,10 @@ def merge_bandwidth(ca, torch, rows=524288, d=128, reps=20):
 # The backward's 10*d splits into S, dP, dV, dK (the dK/dV kernel, 8*d) and dQ
 # (2*d); the dQ kernel also recomputes S and dP, which count as issued work
 # only.
-ALGO_FLOPS_PER_PAIR = {"fwd_step": 4, "bwd_step": 8, "bwd_dq": 2}
-ISSUED_FLOPS_PER_PAIR = {"fwd_step": 4, "bwd_step": 8, "bwd_dq": 6}
+ALGO_FLOPS_PER_PAIR = {"fwd_step": 4, "bwd_step": 8, "bwd_dq": 2, "bwd_dq_ds": 2}
+ISSUED_FLOPS_PER_PAIR = {"fwd_step": 4, "bwd_step": 8, "bwd_dq": 6, "bwd_dq_ds": 2}
 ROCPROF_NAME = {"fwd_step": "fwd_step_bf16_kernel", "bwd_step": "bwd_dkdv_bf16_kernel",
-                "bwd_dq": "bwd_dq_bf16_kernel"}
+                "bwd_dq": "bwd_dq_bf16_kernel", "bwd_dq_ds": "bwd_dq_ds_bf16_kernel"}
 
 
 def calibrate_copy(torch, nbytes=256 << 20, reps=5):
@@ -156,6 +156,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true")
+    ap.add_argument("--no-ds-store", action="store_true",
+                    help="give the backward no room for the dS tile store (dQ recomputes S, dP)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the copy kernel used to scale the traffic counters")
     args = ap.parse_args()
@@ -184,7 +186,7 @@ def main():
     out = torch.empty_like(t["q"])
     lse = torch.empty(w.batch, w.heads_q, w.seqlen // w.world, device="cuda")
     if w.with_grad:
-        ws_b = ca.alloc_workspace(desc, True)
+        ws_b = ca.alloc_workspace(desc, True, cu_seqlens=w.cu_seqlens, ds_store=not args.no_ds_store)
         dq = torch.empty(t["q"].shape, dtype=torch.float32, device="cuda")
         dk = torch.zeros(t["k"].shape, dtype=torch.float32, device="cuda")
         dv = torch.zeros(t["v"].shape, dtype=torch.float32, device="cuda")
@@ -210,7 +212,8 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     kern = {}
-    for name in ("fwd_step", "bwd_pre", "bwd_step", "bwd_dq", "bwd_post", "lse_merge", "finalize"):
+    for name in ("fwd_step", "bwd_pre", "bwd_step", "bwd_dq", "bwd_dq_ds", "bwd_post", "lse_merge",
+                 "finalize"):
         n, ms = ca.ring_attn_timing_read(name)
         if n:
             kern[name] = {"launches": n // args.steps, "ms_per_step": ms / args.steps,

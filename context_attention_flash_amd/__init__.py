@@ -52,6 +52,7 @@ _P = ctypes.c_void_p
 _DP = ctypes.POINTER(RingAttnDesc)
 _SIGS = {
     "ring_attn_workspace_bytes": (ctypes.c_int64, [_DP, ctypes.c_int]),
+    "ring_attn_bwd_ds_bytes": (ctypes.c_int64, [_DP, _P]),
     "ring_attn_fwd": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "ring_attn_bwd": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                      ctypes.c_size_t, _P]),
@@ -141,6 +142,19 @@ def ring_attn_workspace_bytes(desc: RingAttnDesc, is_bwd: bool) -> int:
     return int(n)
 
 
+def ring_attn_bwd_ds_bytes(desc: RingAttnDesc, cu_seqlens=None) -> int:
+    keep, cu = _cu_arg(cu_seqlens)
+    n = lib().ring_attn_bwd_ds_bytes(ctypes.byref(desc), cu)
+    if n < 0:
+        raise RingAttnError(int(n), "ring_attn_bwd_ds_bytes")
+    return int(n)
+
+
+# The binding gives the backward the dS tile store when it needs at most this
+# many bytes (callers who pass their own workspace decide for themselves).
+DS_STORE_LIMIT = 16 << 30
+
+
 def ring_attn_positions(desc: RingAttnDesc, cu_seqlens=None, rank: Optional[int] = None) -> np.ndarray:
     S, _, _ = shard_sizes(desc)
     out = np.empty(S, np.int64)
@@ -226,9 +240,16 @@ def _elem_dtype(desc):
     return torch.bfloat16 if desc.dtype == RA_BF16 else torch.float32
 
 
-def alloc_workspace(desc: RingAttnDesc, is_bwd: bool, device="cuda"):
+def alloc_workspace(desc: RingAttnDesc, is_bwd: bool, device="cuda", cu_seqlens=None,
+                    ds_store: bool = True):
+    """Workspace for the forward or the backward; the backward one includes
+    the dS tile store when ``ds_store`` and it fits DS_STORE_LIMIT."""
     torch = _torch()
     n = ring_attn_workspace_bytes(desc, is_bwd)
+    if is_bwd and ds_store:
+        extra = ring_attn_bwd_ds_bytes(desc, cu_seqlens)
+        if extra <= DS_STORE_LIMIT:
+            n += extra
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
@@ -270,7 +291,7 @@ def ring_attn_bwd(desc: RingAttnDesc, dout, q, k, v, out, lse, cu_seqlens=None, 
     if dv is None:
         dv = torch.zeros(sh["kv"], dtype=f32, device=q.device)
     if workspace is None:
-        workspace = alloc_workspace(desc, True, q.device)
+        workspace = alloc_workspace(desc, True, q.device, cu_seqlens)
     keep, cu = _cu_arg(cu_seqlens)
     rc = lib().ring_attn_bwd(ctypes.byref(desc), _expect(dout, sh["q"], dt, "dout"),
                              _expect(q, sh["q"], dt, "q"), _expect(k, sh["kv"], dt, "k"),

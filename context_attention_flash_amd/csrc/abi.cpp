@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cstring>
 #include <map>
 #include <memory>
@@ -43,6 +44,10 @@ struct DevStep {
     const int32_t* q_mid = nullptr;
     const int32_t* q_ent = nullptr;
     const int32_t* q_order = nullptr;
+    int32_t b_ne = 0;                 // entries of the b lists (dS tiles per batch, q head)
+    const int32_t* d_off = nullptr;   // K4c lists: 256-row query tiles over 128-key tiles
+    const int32_t* d_ent = nullptr;
+    const int32_t* d_order = nullptr;
 };
 
 struct Plan {
@@ -51,6 +56,7 @@ struct Plan {
     int32_t nqt = 0;    // forward query tiles
     int32_t nkt_b = 0;  // backward key tiles
     int32_t nqt_dq = 0; // dQ query tiles
+    int32_t max_ne = 0; // largest b_ne over the steps
     void* dbuf = nullptr;
     std::vector<DevStep> steps;
     ~Plan() {
@@ -106,6 +112,34 @@ void build_lists(const std::vector<int8_t>& kinds, int64_t nrows, int64_t ncols,
     });
 }
 
+// Lists of the dQ-from-dS kernel, derived from the backward lists (per key
+// tile over 64-row query tiles, entry index = dS tile): for each 256-row query
+// tile, the 128-key tiles it meets in increasing order, each with the dS tile
+// entry of the four 64-row quarters (-1 where a quarter sees none of the keys).
+void build_ds_lists(const std::vector<int32_t>& boff, const std::vector<int32_t>& bent,
+                    int64_t nkt, int64_t nqt256, std::vector<int32_t>& off,
+                    std::vector<int32_t>& ent, std::vector<int32_t>& order) {
+    std::vector<std::vector<std::array<int32_t, 5>>> per(nqt256);
+    for (int64_t kt = 0; kt < nkt; ++kt)
+        for (int32_t e = boff[kt]; e < boff[kt + 1]; ++e) {
+            const int32_t qs = bent[e] & 0x7fffffff;
+            auto& L = per[qs >> 2];
+            if (L.empty() || L.back()[0] != kt) L.push_back({(int32_t)kt, -1, -1, -1, -1});
+            L.back()[1 + (qs & 3)] = e;
+        }
+    off.assign(nqt256 + 1, 0);
+    ent.clear();
+    for (int64_t q = 0; q < nqt256; ++q) {
+        for (const auto& x : per[q]) ent.insert(ent.end(), x.begin(), x.end());
+        off[q + 1] = (int32_t)(ent.size() / 5);
+    }
+    order.resize(nqt256);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+        return off[x + 1] - off[x] > off[y + 1] - off[y];
+    });
+}
+
 int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
     auto plan = std::make_unique<Plan>();
     plan->device = device;
@@ -117,7 +151,8 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
     const int64_t nqt_b = (g.S + BWD_BQ - 1) / BWD_BQ;
 
     HostArrays H;
-    struct Idx { size_t rng, foff, fmid, fent, ford, boff, bmid, bent, bord, qoff, qmid, qent, qord; };
+    struct Idx { size_t rng, foff, fmid, fent, ford, boff, bmid, bent, bord, qoff, qmid, qent, qord,
+                 doff, dent, dord; };
     std::vector<Idx> idx;
     std::vector<StepRanges> all(g.nb);
     int64_t total_pairs = 0;
@@ -152,6 +187,15 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
         ix.ford = H.add(std::move(order));
         classify(sr, g.S, g.Skv, BWD_BQ, BWD_BK, kinds);
         build_lists(kinds, nqt_b, plan->nkt_b, false, off, mid, ent, order);
+        {
+            std::vector<int32_t> doff, dent, dord;
+            build_ds_lists(off, ent, plan->nkt_b, plan->nqt_dq, doff, dent, dord);
+            ix.doff = H.add(std::move(doff));
+            ix.dent = H.add(std::move(dent));
+            ix.dord = H.add(std::move(dord));
+        }
+        ds.b_ne = (int32_t)ent.size();
+        plan->max_ne = std::max(plan->max_ne, ds.b_ne);
         ix.boff = H.add(std::move(off));
         ix.bmid = H.add(std::move(mid));
         ix.bent = H.add(std::move(ent));
@@ -198,6 +242,9 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
         d.q_mid = P(idx[k].qmid);
         d.q_ent = P(idx[k].qent);
         d.q_order = P(idx[k].qord);
+        d.d_off = P(idx[k].doff);
+        d.d_ent = P(idx[k].dent);
+        d.d_order = P(idx[k].dord);
     }
     out = std::move(plan);
     return RA_OK;
@@ -224,10 +271,11 @@ int get_plan(const Geometry& g, const Plan** out) {
 // ---------------------------------------------------------------------------
 
 enum KernelClass {
-    KC_FWD = 0, KC_MERGE, KC_FINALIZE, KC_BWD_PRE, KC_BWD, KC_BWD_DQ, KC_BWD_POST, KC_COUNT
+    KC_FWD = 0, KC_MERGE, KC_FINALIZE, KC_BWD_PRE, KC_BWD, KC_BWD_DQ, KC_BWD_DQ_DS, KC_BWD_POST,
+    KC_COUNT
 };
-const char* kClassNames[KC_COUNT] = {"fwd_step", "lse_merge", "finalize", "bwd_pre",
-                                     "bwd_step",  "bwd_dq",    "bwd_post"};
+const char* kClassNames[KC_COUNT] = {"fwd_step", "lse_merge", "finalize", "bwd_pre",  "bwd_step",
+                                     "bwd_dq",   "bwd_dq_ds", "bwd_post"};
 
 struct Timing {
     std::mutex mu;
@@ -308,6 +356,40 @@ int64_t bwd_workspace(const Geometry& g) {
     return 2 * bwd_row_bytes(g) + round_up((int64_t)g.B * g.Hq * S_pad * g.d * 4, 256);
 }
 
+// The dS tile store (optional part of the backward workspace, after the
+// parts above): one tile of DS_TILE_ELEMS bf16 per (batch, q head, entry of a
+// step's backward lists), sized for the step with the most entries.
+int64_t ds_store_bytes(const Geometry& g, int64_t max_ne) {
+    return round_up((int64_t)g.B * g.Hq * max_ne * DS_TILE_ELEMS * 2, 256);
+}
+
+// Largest entry count of the backward lists over the active steps, computed
+// on the host exactly as the plan does (memoised per geometry).
+int64_t host_max_ne(const Geometry& g) {
+    static std::mutex mu;
+    static std::map<std::string, int64_t> memo;
+    const std::string key = plan_key(g);
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = memo.find(key);
+        if (it != memo.end()) return it->second;
+    }
+    int64_t best = 0;
+    StepRanges sr;
+    std::vector<int8_t> kinds;
+    for (int32_t s = 0; s < g.nb; ++s) {
+        step_ranges(g, s, sr);
+        if (sr.pairs == 0) continue;
+        classify(sr, g.S, g.Skv, BWD_BQ, BWD_BK, kinds);
+        const int64_t ne = std::count_if(kinds.begin(), kinds.end(),
+                                         [](int8_t k) { return k != TILE_EMPTY; });
+        best = std::max(best, ne);
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    memo[key] = best;
+    return best;
+}
+
 int check_support(const Geometry& g, bool bwd) {
     if (g.d != 64 && g.d != 128) return RA_E_UNSUPPORTED;
     // kernels address one batch entry of a block, and of q, with 32-bit offsets
@@ -353,6 +435,17 @@ int64_t ring_attn_workspace_bytes(const ring_attn_desc* desc, int is_bwd) {
     const int rc = validate(desc, nullptr, &g, false);
     if (rc != RA_OK) return rc;
     return is_bwd ? bwd_workspace(g) : fwd_workspace(g);
+}
+
+int64_t ring_attn_bwd_ds_bytes(const ring_attn_desc* desc, const int32_t* cu) {
+    try {
+        Geometry g;
+        const int rc = validate(desc, cu, &g, true);
+        if (rc != RA_OK) return rc;
+        return ds_store_bytes(g, host_max_ne(g));
+    } catch (...) {
+        return RA_E_ARG;
+    }
 }
 
 int ring_attn_positions(const ring_attn_desc* desc, const int32_t* cu, int32_t rank,
@@ -542,6 +635,12 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
         float* lse2 = (float*)workspace;
         float* ndelta = (float*)((unsigned char*)workspace + bwd_row_bytes(g));
         float* dq_acc = (float*)((unsigned char*)workspace + 2 * bwd_row_bytes(g));
+        // with room for the dS tile store, K4a keeps dS and K4c builds dQ from
+        // it; otherwise K4b recomputes S and dP
+        const int64_t ds_bytes = ds_store_bytes(g, plan->max_ne);
+        uint16_t* ds_buf = plan->max_ne > 0 && (int64_t)workspace_bytes >= need + ds_bytes
+                               ? (uint16_t*)((unsigned char*)workspace + need)
+                               : nullptr;
 
         BwdPreArgs pa{};
         pa.dout = dout; pa.out = out; pa.lse = lse; pa.lse2 = lse2; pa.ndelta = ndelta;
@@ -558,6 +657,14 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
         a.total_work = g.B * g.Hkv * plan->nkt_b;
         a.scale = g.scale;
         a.scale_log2 = g.scale * 1.4426950408889634f;
+        a.ds = ds_buf;
+        DqDsArgs da{};
+        da.ds = ds_buf; da.dq_acc = dq_acc;
+        da.B = g.B; da.S = (int32_t)g.S; da.Skv = (int32_t)g.Skv; da.Hq = g.Hq; da.Hkv = g.Hkv;
+        da.nqt = plan->nqt_dq;
+        da.S_pad = (int32_t)plan->S_pad;
+        da.total_work = g.B * g.Hq * plan->nqt_dq;
+        da.scale = g.scale;
         DqArgs qa{};
         qa.q = (const uint16_t*)q; qa.dout = (const uint16_t*)dout; qa.lse2 = lse2;
         qa.ndelta = ndelta; qa.dq_acc = dq_acc;
@@ -574,6 +681,7 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
             a.dk = dk + st.j * block_elems;
             a.dv = dv + st.j * block_elems;
             a.rng = st.rng; a.t_off = st.b_off; a.t_mid = st.b_mid; a.t_ent = st.b_ent; a.t_order = st.b_order;
+            a.ds_ne = st.b_ne;
             if (st.pairs > 0) {
                 rc = hip_rc(timed(KC_BWD, s, [&] { return launch_bwd_dkdv_bf16(a, g.d, s); }));
                 if (rc != RA_OK) return rc;
@@ -583,7 +691,15 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
             qa.k = a.k; qa.v = a.v;
             qa.rng = st.rng; qa.t_off = st.q_off; qa.t_mid = st.q_mid; qa.t_ent = st.q_ent; qa.t_order = st.q_order;
             qa.first = first ? 1 : 0;
-            if (st.pairs > 0 || first) {
+            if (ds_buf && (st.pairs > 0 || first)) {
+                da.k = a.k;
+                da.t_off = st.d_off; da.t_ent = st.d_ent; da.t_order = st.d_order;
+                da.ds_ne = st.b_ne;
+                da.first = qa.first;
+                rc = hip_rc(timed(KC_BWD_DQ_DS, s, [&] { return launch_bwd_dq_ds_bf16(da, g.d, s); }));
+                if (rc != RA_OK) return rc;
+                first = false;
+            } else if (st.pairs > 0 || first) {
                 rc = hip_rc(timed(KC_BWD_DQ, s, [&] { return launch_bwd_dq_bf16(qa, g.d, s); }));
                 if (rc != RA_OK) return rc;
                 first = false;

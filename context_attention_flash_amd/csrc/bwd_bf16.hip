@@ -27,6 +27,16 @@
 // Each (head, query tile) has one owner per launch, so dQ needs no atomics:
 // fp32 atomics on the L2 run about ten times slower than plain stores, and
 // the dQ of a key-tile decomposition would be bound by them.
+//
+// K4c bwd_dq_ds (used when the workspace holds the dS tile store): K4a also
+// writes every dS tile it computes (bf16, 16 KB per 64-row x 128-key tile, in
+// its register order, four 1 KB stores per wave and tile), and K4c computes
+// dQ^T += K^T dS^T from those tiles: one work-group per (batch, q head,
+// 256-row query tile), wave w owning the 64-row quarter w, 32-key stages of
+// K and of the four quarters' dS streamed through LDS, the dS^T operands taken
+// by transpose reads.  This replaces the recomputation of S and dP (4 of
+// K4b's 6 flops per pair) by a read of 2 bytes per tile element, written once
+// by K4a.
 #include <type_traits>
 
 #include "kernel_args.h"
@@ -126,7 +136,7 @@ struct DkdvLoader {
     }
 };
 
-template <int DH>
+template <int DH, bool STORE_DS>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_bf16_kernel(BwdArgs p) {
     using C = BwdCfg<DH>;
     // Two stages as separate objects: every access below names its stage
@@ -198,12 +208,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // is fetched one iteration ahead so that its scalar load is off the path.
     DkdvLoader<DH> ld;
     ld.init(p, b, wave, lane);
-    auto entry_of = [&](int it) {
+    auto index_of = [&](int it) {   // position of iteration it's tile in the list
         const bool full = it < nF;
         const int n = full ? m - e0 : e1 - m;
         const int jt = full ? it : it - nF;
-        return ents[(full ? e0 : m) + jt % n];
+        return (full ? e0 : m) + jt % n;
     };
+    auto entry_of = [&](int it) { return ents[index_of(it)]; };
     auto head_of = [&](int it) {
         const bool full = it < nF;
         const int n = full ? m - e0 : e1 - m;
@@ -250,7 +261,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // packed to bf16 as the B operands of dV^T and dK^T for the query blocks
     // kk = 2*mt and 2*mt + 1.
     auto p_half = [&](const unsigned char* st, int mt, auto partial_tag, const f32x16_t& sacc,
-                      const f32x16_t& pacc, u32x4_t (&pb)[2], u32x4_t (&db)[2]) {
+                      const f32x16_t& pacc, u32x4_t (&pb)[2], u32x4_t (&db)[2], uint16_t* ds_tile) {
         constexpr bool PARTIAL = decltype(partial_tag)::value;
         const float* L2 = (const float*)(st + C::OFF_L);
         const int32_t* R = (const int32_t*)(st + C::OFF_RNG);
@@ -277,6 +288,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             pb[kk][w + 1] = pack_bf16x2(pr[2], pr[3]);
             db[kk][w] = pack_bf16x2(ds[0], ds[1]);
             db[kk][w + 1] = pack_bf16x2(ds[2], ds[3]);
+        }
+        if constexpr (STORE_DS) {   // the dS tile store, in this register order
+            // non-temporal: the tile is read once, by the dQ kernel, after
+            // the whole launch; streaming it out keeps the caches for Q and dO
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)ds_tile, (short)0, DS_TILE_ELEMS * 2, 0x00020000);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                __builtin_amdgcn_raw_buffer_store_b128(db[kk], r, (wave * 256 + lane) * 16,
+                                                       (2 * mt + kk) * 1024, 2);
         }
     };
 
@@ -331,7 +352,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Scheduling fences split the tile into regions; the LDS reads of each
     // region's MFMAs are issued in the region before, so that the MFMAs do
     // not wait for them, and the fences bound the registers in flight.
-    auto tile = [&](const unsigned char* st, auto partial_tag) {
+    auto tile = [&](const unsigned char* st, auto partial_tag, uint16_t* ds_tile) {
         f32x16_t s0, p0, s1, p1;
         u32x4_t pb0[2], db0[2];
         SOps o0, o1;
@@ -342,11 +363,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         s_read(st, 1, o1);
         __builtin_amdgcn_sched_barrier(0);
         s_mfma(o1, s1, p1);
-        p_half(st, 0, partial_tag, s0, p0, pb0, db0);
+        p_half(st, 0, partial_tag, s0, p0, pb0, db0, ds_tile);
         read_half(st, 0, oa, qa);
         __builtin_amdgcn_sched_barrier(0);
         mfma_half(oa, qa, pb0, db0);
-        p_half(st, 1, partial_tag, s1, p1, c_pb, c_db);
+        p_half(st, 1, partial_tag, s1, p1, c_pb, c_db, ds_tile);
         read_half(st, 1, c_oa, c_qa);
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -359,10 +380,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         mfma_half(c_oa, c_qa, c_pb, c_db);
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt) asm volatile("" : "+a"(dk_acc[dt]), "+a"(dv_acc[dt]));
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile it have landed
+        // this wave's loads of tile it have landed; with the dS store, the
+        // four dS stores of tile it-1, issued after those loads, may still be
+        // in flight (vmcnt <= 4: vector memory operations complete in order)
+        __builtin_amdgcn_s_waitcnt(STORE_DS ? 0x0004 : 0);
         __syncthreads();
         if (it + 1 < n_iter) load(it + 1, ent_nx, nxt);
-        tile(cur, partial_tag);
+        uint16_t* ds_tile = nullptr;   // this tile's place in the dS tile store
+        if constexpr (STORE_DS)
+            ds_tile = p.ds + ((int64_t)(b * p.Hq + head_of(it)) * p.ds_ne + index_of(it)) * DS_TILE_ELEMS;
+        tile(cur, partial_tag, ds_tile);
         // the scalar load goes out after the tile's LDS reads: while it is in
         // flight every LDS wait must be a full one (scalar loads return out of
         // order)
@@ -372,6 +399,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // left over goes through the masked loop, where the mask keeps every key.
     const int nF2 = nF & ~1;
     if (n_iter > 0) load(0, entry_of(0), stA);
+    if constexpr (STORE_DS) __builtin_amdgcn_s_waitcnt(0);   // the first wait counts on none in flight
     int it = 0;
     for (; it < nF2; it += 2) {
         step(it, stA, stB, std::false_type{});
@@ -405,13 +433,26 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     }
 }
 
+// Explicit instantiations: with several specialisations of one kernel
+// template launched from one function, the host pass emitted the launch stub
+// of the first one only (the build checks the library for missing stubs).
+template __global__ void bwd_dkdv_bf16_kernel<128, true>(BwdArgs);
+template __global__ void bwd_dkdv_bf16_kernel<128, false>(BwdArgs);
+template __global__ void bwd_dkdv_bf16_kernel<64, true>(BwdArgs);
+template __global__ void bwd_dkdv_bf16_kernel<64, false>(BwdArgs);
+
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int head_dim, hipStream_t s) {
     const int grid = (a.total_work + 7) / 8 * 8;
     if (grid == 0) return hipSuccess;
-    if (head_dim == 128)
-        hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a);
+    const bool st = a.ds != nullptr;
+    if (head_dim == 128 && st)
+        hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<128, true>), dim3(grid), dim3(256), 0, s, a);
+    else if (head_dim == 128)
+        hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<128, false>), dim3(grid), dim3(256), 0, s, a);
+    else if (head_dim == 64 && st)
+        hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<64, true>), dim3(grid), dim3(256), 0, s, a);
     else if (head_dim == 64)
-        hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<64, false>), dim3(grid), dim3(256), 0, s, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -670,6 +711,217 @@ hipError_t launch_bwd_dq_bf16(const DqArgs& a, int head_dim, hipStream_t s) {
         hipLaunchKernelGGL(bwd_dq_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a);
     else if (head_dim == 64)
         hipLaunchKernelGGL(bwd_dq_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// K4c: dQ of one ring step from the dS tiles stored by K4a (no recompute)
+// ---------------------------------------------------------------------------
+
+template <int DH>
+struct DsCfg {
+    static constexpr int KH = 32;                       // keys per stage (a quarter of a dS tile)
+    static constexpr int NDT = DH / 32;
+    static constexpr int ROWB = DH * 2;
+    static constexpr int KCH = DH / 8;
+    static constexpr int DS_BYTES = BWD_BQ * KH * 2;    // one quarter's dS over KH keys: 4 KB
+    static constexpr int NDS = DS_BYTES / 1024;         // 1 KB loads per wave
+    static constexpr int SPT = BWD_BK / KH;             // stages per dS tile
+    static constexpr int OFF_K = 4 * DS_BYTES;
+    static constexpr int STAGE = OFF_K + KH * ROWB;     // + the K rows of those keys
+};
+
+// LDS place of 16-byte chunk f of a quarter's dS over one 32-key group
+// (f = kk*64 + lane in the stored register order): bits 2 and 3 of f are
+// flipped by bits 6 and 5, which makes the transpose reads below touch every
+// bank once per half-wave.  The map is its own inverse.
+__device__ __forceinline__ int ds_pos(int f) {
+    return f ^ ((((f >> 6) & 1) << 2) | (((f >> 5) & 1) << 3));
+}
+
+// One wave's quarter of a dS tile over KH keys (NDS KB, starting at byte
+// `soff` of the 16 KB tile) into LDS, each chunk f at ds_pos(f).  dS is read
+// once, so the loads are non-temporal; a quarter without a tile (present ==
+// false) reads zeros through an empty buffer range.
+template <int NDS>
+struct DsQuarterLoader {
+    int dvo[NDS];
+    __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+        for (int i = 0; i < NDS; ++i) dvo[i] = 16 * ds_pos(64 * i + lane);
+    }
+    __device__ __forceinline__ void load(unsigned char* lds, const uint16_t* tile, bool present,
+                                         int soff) const {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)tile, (short)0, present ? DS_TILE_ELEMS * 2 : 0, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < NDS; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (__attribute__((address_space(3))) void*)(lds + 1024 * i), 16, dvo[i], soff, 0, 2);
+    }
+};
+
+template <int DH>
+__global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(DqDsArgs p) {
+    using C = DsCfg<DH>;
+    __shared__ __attribute__((aligned(16))) unsigned char stA[C::STAGE];
+    __shared__ __attribute__((aligned(16))) unsigned char stB[C::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int work = xcd_work_index(blockIdx.x, gridDim.x);
+    if (work >= p.total_work) return;
+    const int t = work % p.nqt, bh = work / p.nqt;
+    const int h = bh % p.Hq, b = bh / p.Hq;
+    const int qt = as_const(p.t_order)[t];
+    const int hk = (h * p.Hkv) / p.Hq;
+    const cint_ptr ents = as_const(p.t_ent);
+    const int e0 = as_const(p.t_off)[qt], e1 = as_const(p.t_off)[qt + 1];
+    const int n_iter = C::SPT * (e1 - e0);   // SPT stages per 128-key tile
+
+    // K rows of the stage (64 keys of head hk) and this wave's quarter of dS
+    BufTileLoader<DH, C::KH> lk;
+    lk.init(p.k + (int64_t)b * p.Skv * p.Hkv * DH, p.Skv, p.Hkv, hk, wave, lane);
+    DsQuarterLoader<C::NDS> lds_ds;
+    lds_ds.init(lane);
+    const uint16_t* ds_head = p.ds + (int64_t)(b * p.Hq + h) * p.ds_ne * DS_TILE_ELEMS;
+    // iteration it: key tile kt = entry (it/SPT), keys KH*(it%SPT).. of it
+    auto load = [&](int it, int kt, int e, unsigned char* st) {
+        lk.load(st + C::OFF_K, C::SPT * kt + it % C::SPT, wave);
+        lds_ds.load(st + wave * C::DS_BYTES, e >= 0 ? ds_head + (int64_t)e * DS_TILE_ELEMS : p.ds,
+                    e >= 0, (it % C::SPT) * C::DS_BYTES);
+    };
+
+    // Transpose-read offsets.  dS^T operand (B) of query block qb, key step
+    // ks: lane L takes query 32qb + L%32 and keys 16ks + 8(L/32) + 0..7; the
+    // reading lane s of each 16-lane group G points at query rows
+    // 32qb + 16(G%2) + 4(s%4) .. +3 of key 16ks + 8(G/2) + 4r + s/4.
+    const int G = lane >> 4, sl = lane & 15, c = sl & 3, kq = sl >> 2;
+    int dsr[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int f = (G & 1) * 64 + 32 * (c & 1) + 8 * (G >> 1) + 4 * r + kq;
+        dsr[r] = wave * C::DS_BYTES + 16 * ds_pos(f) + 8 * (c >> 1);
+    }
+    // K^T operand (A) of head-dim block dt, key step ks: rows (keys)
+    // 16ks + 8(L/32) + 4r + j/4, columns 32dt + 16((L/16)%2) + 4(j%4)
+    const int j = lane & 15, gsel = (lane >> 4) & 1, hsel = lane >> 5;
+    int trk[2][C::NDT];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) {
+            const int col = 32 * dt + 16 * gsel + 4 * (j & 3);
+            trk[r][dt] = C::OFF_K + row_off<C::KCH>(8 * hsel + 4 * r + (j >> 2), col >> 3) + (col & 7) * 2;
+        }
+
+    f32x16_t acc[2][C::NDT];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) acc[qb][dt] = (f32x16_t){};
+
+    // Operands of key step ks (16 keys) of stage st.
+    static_assert(C::KH == 32, "two key steps per stage");
+    struct Ops {
+        u32x4_t ka[C::NDT], da[2];
+    };
+    auto read_ks = [&](const unsigned char* st, int ks, Ops& o) {
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) {
+            const u32x2_t a1 = lds_tr16(st + trk[0][dt] + ks * 16 * C::ROWB);
+            const u32x2_t a2 = lds_tr16(st + trk[1][dt] + ks * 16 * C::ROWB);
+            o.ka[dt] = (u32x4_t){a1[0], a1[1], a2[0], a2[1]};
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const int off = 2048 * qb + 256 * ks;
+            const u32x2_t d1 = lds_tr16(st + dsr[0] + off);
+            const u32x2_t d2 = lds_tr16(st + dsr[1] + off);
+            o.da[qb] = (u32x4_t){d1[0], d1[1], d2[0], d2[1]};
+        }
+    };
+    auto mfma_ks = [&](const Ops& o) {
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+                acc[qb][dt] = mfma_32x32x16(o.ka[dt], o.da[qb], acc[qb][dt]);
+    };
+
+    // The second key step of a stage runs at the start of the next iteration,
+    // before its barrier (zero operands at first, adding nothing).
+    Ops c_ops;
+#pragma unroll
+    for (int dt = 0; dt < C::NDT; ++dt) c_ops.ka[dt] = (u32x4_t){0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) c_ops.da[qb] = (u32x4_t){0u, 0u, 0u, 0u};
+    auto tile = [&](const unsigned char* st) {
+        Ops o0;
+        read_ks(st, 0, o0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_ks(o0);
+        read_ks(st, 1, c_ops);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // the list entry (key tile, this quarter's dS entry) of iteration it + 1
+    auto kt_of = [&](int it) { return ents[5 * (e0 + it / C::SPT)]; };
+    auto e_of = [&](int it) { return ents[5 * (e0 + it / C::SPT) + 1 + wave]; };
+    int kt_nx = n_iter > 1 ? kt_of(1) : 0, e_nx = n_iter > 1 ? e_of(1) : -1;
+    auto step = [&](int it, const unsigned char* cur, unsigned char* nxt) {
+        mfma_ks(c_ops);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) asm volatile("" : "+a"(acc[qb][dt]));
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of stage it have landed
+        __syncthreads();
+        if (it + 1 < n_iter) load(it + 1, kt_nx, e_nx, nxt);
+        tile(cur);
+        if (it + 2 < n_iter) {
+            kt_nx = kt_of(it + 2);
+            e_nx = e_of(it + 2);
+        }
+    };
+    if (n_iter > 0) load(0, kt_of(0), e_of(0), stA);
+    for (int it = 0; it < n_iter; it += 2) {   // n_iter is even
+        step(it, stA, stB);
+        step(it + 1, stB, stA);
+    }
+    mfma_ks(c_ops);
+
+    // dq_acc (+)= scale * acc, in the layout of the recomputing dQ kernel
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        f32x4_t* dst = (f32x4_t*)p.dq_acc +
+                       (((int64_t)b * p.Hq + h) * (p.S_pad / 32) + (qt * 8 + wave * 2 + qb)) * (8 * DH) + lane;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                f32x4_t o = {acc[qb][dt][4 * rg] * p.scale, acc[qb][dt][4 * rg + 1] * p.scale,
+                             acc[qb][dt][4 * rg + 2] * p.scale, acc[qb][dt][4 * rg + 3] * p.scale};
+                f32x4_t* ptr = dst + (dt * 4 + rg) * 64;
+                if (!p.first) o += *ptr;
+                *ptr = o;
+            }
+    }
+}
+
+template __global__ void bwd_dq_ds_bf16_kernel<128>(DqDsArgs);
+template __global__ void bwd_dq_ds_bf16_kernel<64>(DqDsArgs);
+
+hipError_t launch_bwd_dq_ds_bf16(const DqDsArgs& a, int head_dim, hipStream_t s) {
+    const int grid = (a.total_work + 7) / 8 * 8;
+    if (grid == 0) return hipSuccess;
+    if (head_dim == 128)
+        hipLaunchKernelGGL(bwd_dq_ds_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a);
+    else if (head_dim == 64)
+        hipLaunchKernelGGL(bwd_dq_ds_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -59,10 +59,36 @@ struct BwdArgs {
     const int32_t* t_order; // [nkt] key tiles, heaviest first
     float* dk;              // block j: [B, Skv, Hkv, d] fp32, +=
     float* dv;
+    uint16_t* ds;           // NULL, or the dS tile store of the step (see DqDsArgs)
+    int32_t ds_ne;          // entries of the step's lists (tiles per (batch, q head))
     int32_t B, S, Skv, Hq, Hkv, nkt, S_pad;
     int32_t total_work;     // B * Hkv * nkt
     float scale;            // softmax scale
     float scale_log2;       // softmax scale * log2(e)
+};
+
+// dS tile store: one 16 KB tile of bf16 dS = P (dP - Delta) per (batch, q head,
+// entry of the dK/dV kernel's lists), i.e. 64 query rows x 128 keys, at tile
+// index (b * Hq + h) * ds_ne + entry.  Inside a tile the values sit in the
+// register order of the dK/dV kernel: u32x4 number (w * 4 + kk) * 64 + lane
+// holds, for key 32w + lane%32, the query rows 16kk + 4(lane/32) + {0..3} and
+// 16kk + 8 + 4(lane/32) + {0..3} (8 bf16, in that order).
+constexpr int DS_TILE_ELEMS = BWD_BQ * BWD_BK;
+
+// K4c: dQ of one ring step from the stored dS tiles (no recomputation).
+struct DqDsArgs {
+    const uint16_t* k;      // block j: [B, Skv, Hkv, d]
+    const uint16_t* ds;     // dS tile store of the step
+    const int32_t* t_off;   // [nqt + 1] lists per 256-row query tile
+    const int32_t* t_ent;   // 5 ints per entry: 128-key tile, then the dS tile entry
+                            // of each 64-row quarter of the query tile (-1: none)
+    const int32_t* t_order; // [nqt] query tiles, heaviest first
+    float* dq_acc;          // as in DqArgs
+    int32_t B, S, Skv, Hq, Hkv, nqt, S_pad;
+    int32_t ds_ne;
+    int32_t total_work;     // B * Hq * nqt
+    int32_t first;
+    float scale;
 };
 
 // K4b: dQ of one ring step.  Uses the forward's per-query-tile lists.
@@ -105,6 +131,7 @@ hipError_t launch_finalize(const float* o, void* out, int is_bf16, int64_t n, hi
 hipError_t launch_bwd_pre(const BwdPreArgs& a, int is_bf16, hipStream_t s);
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const DqArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_bwd_dq_ds_bf16(const DqDsArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_dq_finalize(const float* dq_acc, float* dq, int32_t B, int32_t S, int32_t Hq,
                               int32_t S_pad, int32_t d, hipStream_t s);
 

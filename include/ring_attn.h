@@ -152,6 +152,17 @@ typedef struct ring_attn_desc {
  * (S_pad = S rounded up to 256; each part starts on a 256-byte boundary). */
 int64_t ring_attn_workspace_bytes(const ring_attn_desc* desc, int is_bwd);
 
+/* Extra backward workspace, in bytes, that lets ring_attn_bwd keep dS (the
+ * softmax gradient P (dP - Delta), bf16) from the dK/dV pass and build dQ
+ * from it instead of recomputing S and dP ("Backward Pass and Gradient
+ * Accumulation": dQ, dK and dV all follow from dS; keeping it trades 2 bytes
+ * per visible tile element of HBM traffic for two of the three dQ
+ * products).  It is B * Hq * (tiles of the busiest step) * 16 KiB, where a
+ * tile is 64 query rows x 128 keys with at least one visible pair; exact for
+ * the given cu_seqlens (NULL unless the layout is packed).  Host only.
+ * Returns a negative RA_E_* for an invalid descriptor. */
+int64_t ring_attn_bwd_ds_bytes(const ring_attn_desc* desc, const int32_t* cu_seqlens);
+
 /* Forward of the rank share ("Forward Pass Implementation"): for s = 0..D-1
  * the block j = (rank - s) mod D is attended if at least one (query, key) pair
  * of the step is visible (under a causal basic layout exactly the steps with
@@ -170,7 +181,10 @@ int ring_attn_fwd(const ring_attn_desc* desc, const void* q, const void* k,
  * (+=): this rank's contribution to every block is added, so calling the
  * backward for every rank on zeroed dk/dv yields the full gradient, as the
  * gradient accumulators travelling around the ring would.  Requires
- * dtype == RA_BF16. */
+ * dtype == RA_BF16.  Workspace: at least ring_attn_workspace_bytes(desc, 1)
+ * bytes; with ring_attn_bwd_ds_bytes(desc, cu_seqlens) bytes more, dQ is
+ * built from the stored dS (same results up to summation order, less
+ * work).  The contents need no initialisation and are garbage afterwards. */
 int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q,
                   const void* k, const void* v, const void* out, const float* lse,
                   const int32_t* cu_seqlens, float* dq, float* dk, float* dv,
@@ -213,7 +227,8 @@ int ring_attn_tile_kinds(const ring_attn_desc* desc, const int32_t* cu_seqlens,
  * every kernel the library enqueues (off by default).  ring_attn_timing_read
  * synchronises on the recorded events and reports, for the kernel class
  * `name` ("fwd_step", "lse_merge", "finalize", "bwd_pre", "bwd_step" (dK/dV),
- * "bwd_dq", "bwd_post"), the
+ * "bwd_dq" (dQ recomputing S and dP), "bwd_dq_ds" (dQ from stored dS),
+ * "bwd_post"), the
  * number of launches and their summed duration in milliseconds since the
  * last reset.  ring_attn_timing_enable(0) disables and resets. */
 int ring_attn_timing_enable(int enable);

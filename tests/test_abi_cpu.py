@@ -188,6 +188,29 @@ def test_workspace_sizes():
         ca.ring_attn_workspace_bytes(desc, False)
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_ds_store_bytes_count_the_busiest_step(layout):
+    """The dS tile store holds B * Hq * 16 KiB per non-empty 64 x 128 tile of
+    the step with the most of them."""
+    rng = np.random.default_rng(70 + layout)
+    D, N = 4, 4 * 2 * 96
+    cu = _cu(layout, N, D, rng)
+    for causal in (True, False):
+        for r in (0, D - 1):
+            desc = ca.make_desc(1 if cu else 2, 4, 2, 128, N, D, r, causal, layout,
+                                cu_seqlens=cu)
+            most = 0
+            for s, j, pairs in ca.ring_attn_schedule(desc, cu):
+                if pairs:
+                    most = max(most, int((ca.ring_attn_tile_kinds(desc, cu, s, 64, 128) > 0).sum()))
+            assert ca.ring_attn_bwd_ds_bytes(desc, cu) == desc.batch * 4 * most * 64 * 128 * 2
+
+
+def test_ds_store_bytes_basic_s4096():
+    desc = ca.make_desc(1, 32, 32, 128, 32768, 8, 7, True, ca.BASIC)
+    assert ca.ring_attn_bwd_ds_bytes(desc) == 32 * (4096 // 64) * (4096 // 128) * 16384
+
+
 def test_python_binding_refuses_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ca, "_lib", None)
     monkeypatch.setattr(ca, "LIB_PATH", str(tmp_path / "nope.so"))

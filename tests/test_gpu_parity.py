@@ -194,13 +194,17 @@ def _check_bwd(w, glob, rank, dq, dk, dv):
     return errs
 
 
-def _run_bwd(w, glob, rank, dk=None, dv=None):
+def _run_bwd(w, glob, rank, dk=None, dv=None, ds_store=True):
+    """Backward through the C ABI; ds_store=False gives it the minimum
+    workspace, so that dQ recomputes S and dP instead of reading stored dS."""
     sh = shard(glob, w, rank)
     desc = ca.desc_from_workload(w, rank=rank)
     q, k, v = (to_dev(sh[n], w.dtype) for n in ("q", "k", "v"))
     out, lse = ca.ring_attn_fwd(desc, q, k, v, w.cu_seqlens)
     dout = to_dev(sh["dout"], w.dtype)
-    dq, dk, dv = ca.ring_attn_bwd(desc, dout, q, k, v, out, lse, w.cu_seqlens, dk=dk, dv=dv)
+    ws = ca.alloc_workspace(desc, True, cu_seqlens=w.cu_seqlens, ds_store=ds_store)
+    dq, dk, dv = ca.ring_attn_bwd(desc, dout, q, k, v, out, lse, w.cu_seqlens, dk=dk, dv=dv,
+                                  workspace=ws)
     torch.cuda.synchronize()
     return dq, dk, dv
 
@@ -272,6 +276,24 @@ def test_bwd_window(layout, head_dim, causal, window):
         say(f"bwd window layout={layout} d={head_dim} causal={causal} window={window} rank={rank}")
         dq, dk, dv = _run_bwd(w, glob, rank)
         _check_bwd(w, glob, rank, dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
+
+
+@pytest.mark.parametrize("layout,head_dim,causal,window", [
+    (ca.BASIC, 128, True, (-1, -1)), (ca.ZIGZAG, 64, True, (-1, -1)),
+    (ca.LLAMA3, 128, True, (-1, -1)), (ca.STRIPE, 128, False, (80, 40))])
+def test_bwd_recompute_path(layout, head_dim, causal, window):
+    """With only the minimum workspace the dQ kernel recomputes S and dP; both
+    backward paths meet the oracle on the same 600-row shards."""
+    w = _small_workload(layout, causal, head_dim, D=3, S=600, B=1, seed=80 + layout,
+                        with_grad=True, window=window)
+    glob = synth.draw_global(w)
+    for rank in (0, w.world - 1):
+        say(f"bwd recompute path layout={layout} d={head_dim} causal={causal} rank={rank}")
+        dq, dk, dv = _run_bwd(w, glob, rank, ds_store=False)
+        _check_bwd(w, glob, rank, dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
+        say(f"bwd stored-dS path layout={layout} d={head_dim} causal={causal} rank={rank}")
+        dq2, dk2, dv2 = _run_bwd(w, glob, rank, ds_store=True)
+        _check_bwd(w, glob, rank, dq2.cpu().numpy(), dk2.cpu().numpy(), dv2.cpu().numpy())
 
 
 def test_bwd_ranks_sum_to_full_gradient():
