@@ -32,6 +32,7 @@ KERNEL_SOURCES = {
     "fwd_step_bf16_kernel": ["fwd_bf16.hip", "kernel_common.h", "kernel_args.h"],
     "bwd_dkdv_bf16_kernel": ["bwd_bf16.hip", "kernel_common.h", "kernel_args.h"],
     "bwd_dq_bf16_kernel": ["bwd_bf16.hip", "kernel_common.h", "kernel_args.h"],
+    "bwd_dq_ds_bf16_kernel": ["bwd_bf16.hip", "kernel_common.h", "kernel_args.h"],
     "lse_merge_kernel": ["elementwise.hip", "kernel_common.h", "kernel_args.h"],
 }
 
