@@ -99,3 +99,29 @@ def test_workload_backward_basic_s8192():
     assert np.abs(got_dv - rdv).max() <= 5e-2 * np.abs(rdv).max()
     # blocks this rank never sees stay untouched (causal basic: none here, rank 7)
     assert torch.isfinite(dk).all().item() and torch.isfinite(dv).all().item()
+
+
+@pytest.mark.parametrize("name", ["zigzag", "llama3"])
+def test_workload_backward_dq_sampled(name):
+    """The backward at the zigzag (GQA 32/8, 16384-row shard) and llama3
+    (packed, one step over the gathered 65536 keys) sizes, through the stored-dS
+    path the bench uses: dq on sampled rows x heads (each row's dq depends on
+    that row alone); dk, dv finite."""
+    w = synth.WORKLOADS[name].replace(with_grad=True)
+    say(f"workload bwd {name}")
+    g, desc, cu, pos_q, dev = _inputs(w)
+    ws = ca.alloc_workspace(desc, True, cu_seqlens=cu)
+    assert ws.numel() >= ca.ring_attn_workspace_bytes(desc, True) + ca.ring_attn_bwd_ds_bytes(desc, cu)
+    out, lse = ca.ring_attn_fwd(desc, dev["q"], dev["k"], dev["v"], cu)
+    dq, dk, dv = ca.ring_attn_bwd(desc, dev["dout"], dev["q"], dev["k"], dev["v"], out, lse, cu,
+                                  workspace=ws)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w.shard, np.random.default_rng(8))
+    heads = [0, 13, 31]
+    rdq, _, _ = oracle.rank_share_backward(g["q"], g["k"], g["v"], g["dout"][:, pos_q], w.layout,
+                                           w.world, w.rank, w.causal, cu, rows=rows, heads=heads)
+    got = dq[:, torch.tensor(rows)].cpu().numpy()
+    for h in heads:
+        ref = rdq[:, :, h]
+        assert np.abs(got[:, :, h] - ref).max() <= 5e-2 * np.abs(ref).max(), h
+    assert torch.isfinite(dk).all().item() and torch.isfinite(dv).all().item()
