@@ -156,6 +156,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true")
+    ap.add_argument("--with-grad", action="store_true",
+                    help="also time the backward on a workload defined forward-only")
     ap.add_argument("--no-ds-store", action="store_true",
                     help="give the backward no room for the dS tile store (dQ recomputes S, dP)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -174,6 +176,8 @@ def main():
     from context_attention_flash_amd import profsum, synth
 
     w = synth.WORKLOADS[args.workload]
+    if args.with_grad:
+        w = w.replace(with_grad=True)
     torch.cuda.set_device(0)
     g, desc, t = build_inputs(ca, w, torch)
     sched = ca.ring_attn_schedule(desc, w.cu_seqlens)
