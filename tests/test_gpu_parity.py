@@ -296,6 +296,24 @@ def test_bwd_recompute_path(layout, head_dim, causal, window):
         _check_bwd(w, glob, rank, dq2.cpu().numpy(), dk2.cpu().numpy(), dv2.cpu().numpy())
 
 
+@pytest.mark.parametrize("S", [1, 63, 64, 65, 257])
+def test_bwd_edge_shapes(S):
+    """Backward on one-row shards and at exact and ragged tile boundaries
+    (64-row dK/dV query tiles, 128-key tiles, 256-row dQ tiles), both dQ
+    paths."""
+    for layout in (ca.BASIC, ca.ZIGZAG, ca.STRIPE):
+        if layout == ca.ZIGZAG and S % 2:
+            continue
+        w = _small_workload(layout, True, 128, D=3, S=S, B=1, Hq=2, Hkv=1, seed=S + 3,
+                            with_grad=True)
+        glob = synth.draw_global(w)
+        for rank in range(w.world):
+            for ds_store in (True, False):
+                say(f"bwd edge S={S} layout={layout} rank={rank} ds_store={ds_store}")
+                dq, dk, dv = _run_bwd(w, glob, rank, ds_store=ds_store)
+                _check_bwd(w, glob, rank, dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
+
+
 def test_bwd_ranks_sum_to_full_gradient():
     """dk/dv accumulated over every rank's backward on the same buffers equal
     the full-sequence gradient; the ranks' dq tile the full dq."""
