@@ -135,6 +135,24 @@ ROCPROF_NAME = {"fwd_step": "fwd_step_bf16_kernel", "bwd_step": "bwd_dkdv_bf16_k
                 "bwd_dq": "bwd_dq_bf16_kernel", "bwd_dq_ds": "bwd_dq_ds_bf16_kernel"}
 
 
+def dkdv_bytes_per_launch(ca, desc, w, sched, ds_store: bool) -> float:
+    """HBM bytes one dK/dV launch must move, averaged over the step's launches:
+    Q and dO read (bf16), K_j and V_j read (bf16), dK_j and dV_j read and
+    written (fp32), and with the dS store its 16 KiB bf16 tiles (one per
+    non-empty 64-row x 128-key tile and q head)."""
+    S, Skv = w.seqlen // w.world, ca.shard_sizes(desc)[1]
+    active = [(s, p) for s, _, p in sched if p > 0]
+    per = (2 * 2 * w.batch * S * w.heads_q * w.head_dim
+           + 2 * 2 * w.batch * Skv * w.heads_kv * w.head_dim
+           + 2 * 2 * 4 * w.batch * Skv * w.heads_kv * w.head_dim)
+    ds = 0.0
+    if ds_store:
+        for s, _ in active:
+            tiles = int((ca.ring_attn_tile_kinds(desc, w.cu_seqlens, s, 64, 128) > 0).sum())
+            ds += w.batch * w.heads_q * tiles * 64 * 128 * 2
+    return per + ds / max(1, len(active))
+
+
 def calibrate_copy(torch, nbytes=256 << 20, reps=5):
     """A plain copy kernel of known size for scaling the FETCH_SIZE / WRITE_SIZE
     counters: each dispatch reads nbytes and writes nbytes."""
@@ -248,6 +266,9 @@ def main():
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic, "kernel": ROCPROF_NAME[dom],
                 "flops_per_launch": flops_per_launch, "avg_launch_ms": kern[dom]["avg_launch_ms"],
                 "launches_per_step": n_launch}
+    if dom == "bwd_step":
+        roofline["algorithmic_bytes_per_launch"] = dkdv_bytes_per_launch(ca, desc, w, sched,
+                                                                         "bwd_dq_ds" in kern)
 
     res = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1,
