@@ -182,8 +182,8 @@ def main():
                     help="only run the copy kernel used to scale the traffic counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one rank's share on ONE GPU; multi-GPU runs are not part of "
-              "this build (use --gpus 1).", file=sys.stderr)
+        print("bench.py measures one rank's share on ONE GPU; runs on several GPUs are not "
+              "supported (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
