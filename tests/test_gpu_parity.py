@@ -333,3 +333,46 @@ def test_bwd_ranks_sum_to_full_gradient():
     got_dv = np.concatenate(list(dv.cpu().numpy()), axis=1)
     for got, ref in ((got_dk, rdk[0][:, order]), (got_dv, rdv[0][:, order]), (dq_full, rdq)):
         assert np.abs(got - ref).max() <= 5e-2 * np.abs(ref).max()
+
+
+def _random_config(seed):
+    rng = np.random.default_rng(1000 + seed)
+    layout = int(rng.choice(LAYOUTS))
+    D = int(rng.choice([1, 2, 3, 4, 5, 8]))
+    S = int(rng.integers(1, 700))
+    if layout in (ca.ZIGZAG, ca.VARLEN_ZIGZAG) and S % 2:
+        S += 1
+    Hkv = int(rng.choice([1, 2, 3]))
+    Hq = Hkv * int(rng.choice([1, 2, 4]))
+    d = int(rng.choice([64, 128]))
+    causal = bool(rng.integers(0, 2))
+    window = [(-1, -1), (int(rng.integers(0, 300)), -1), (int(rng.integers(0, 200)), int(rng.integers(0, 200)))][
+        int(rng.integers(0, 3))]
+    N = D * S
+    cu = None
+    B = int(rng.choice([1, 2]))
+    if layout in synth.VARLEN_LAYOUTS:
+        m = synth.doc_multiple(layout, D)
+        n_docs = int(rng.integers(1, max(2, min(6, N // m))))
+        cu = tuple(synth.random_cu_seqlens(N, n_docs, rng, multiple=m))
+        B = 1
+    return synth.Workload(f"rand{seed}", B, Hq, Hkv, d, N, D, 0, causal, layout, "bf16",
+                          seed=2000 + seed, cu_seqlens=cu, with_grad=True, window=window)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_configs_fwd_bwd(seed):
+    """Seeded random shapes: layout, world, shard length, GQA ratio, head dim,
+    causal flag, window, batch and document split; forward and both backward
+    paths against the oracle for the first and last rank."""
+    w = _random_config(seed)
+    glob = synth.draw_global(w)
+    for rank in sorted({0, w.world - 1}):
+        say(f"random seed={seed} layout={w.layout} D={w.world} S={w.shard} B={w.batch} "
+            f"Hq={w.heads_q} Hkv={w.heads_kv} d={w.head_dim} causal={w.causal} window={w.window} "
+            f"rank={rank}")
+        _, _, _, out, lse = _run_fwd(w, glob, rank)
+        _check_fwd(w, glob, rank, out, lse)
+        for ds_store in (True, False):
+            dq, dk, dv = _run_bwd(w, glob, rank, ds_store=ds_store)
+            _check_bwd(w, glob, rank, dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
