@@ -32,11 +32,13 @@
  *     argument validation happens before any device work is enqueued, so a
  *     failing call leaves every buffer untouched.  Nothing is printed and no
  *     C++ exception crosses the ABI.  ring_attn_strerror() names each code.
- *   - Thread safety: calls may come from several threads.  The library keeps
- *     one mutable global: a mutex-guarded cache of per-shape plans (step
- *     schedule and tile lists uploaded to device memory it owns), released by
- *     ring_attn_clear_cache().  Calls that use the same workspace or output
- *     buffers on different streams at the same time race, as any kernels do.
+ *   - Thread safety: calls may come from several threads.  The library's
+ *     mutable globals are each mutex-guarded: the cache of per-shape plans
+ *     (step schedule and tile lists uploaded to device memory it owns),
+ *     released by ring_attn_clear_cache(); a host-side memo of dS store
+ *     sizes; and the optional per-kernel timing state.  Calls that use the
+ *     same workspace or output buffers on different streams at the same time
+ *     race, as any kernels do.
  */
 #ifndef RING_ATTN_H
 #define RING_ATTN_H
