@@ -242,14 +242,18 @@ def _elem_dtype(desc):
 
 def alloc_workspace(desc: RingAttnDesc, is_bwd: bool, device="cuda", cu_seqlens=None,
                     ds_store: bool = True):
-    """Workspace for the forward or the backward; the backward one includes
-    the dS tile store when ``ds_store`` and it fits DS_STORE_LIMIT."""
+    """Workspace for the forward or the backward; with ``ds_store`` the
+    backward one includes the dS tile store, whole or (beyond DS_STORE_LIMIT)
+    for as many kv heads at a time as fit the limit."""
     torch = _torch()
     n = ring_attn_workspace_bytes(desc, is_bwd)
     if is_bwd and ds_store:
-        extra = ring_attn_bwd_ds_bytes(desc, cu_seqlens)
-        if extra <= DS_STORE_LIMIT:
-            n += extra
+        full = ring_attn_bwd_ds_bytes(desc, cu_seqlens)
+        per_kv_head = -(-full // desc.heads_kv)
+        if full <= DS_STORE_LIMIT:
+            n += full
+        elif per_kv_head <= DS_STORE_LIMIT:   # kv heads in several passes
+            n += DS_STORE_LIMIT // per_kv_head * per_kv_head
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 

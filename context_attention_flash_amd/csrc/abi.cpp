@@ -637,10 +637,15 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
         float* dq_acc = (float*)((unsigned char*)workspace + 2 * bwd_row_bytes(g));
         // with room for the dS tile store, K4a keeps dS and K4c builds dQ from
         // it; otherwise K4b recomputes S and dP
-        const int64_t ds_bytes = ds_store_bytes(g, plan->max_ne);
-        uint16_t* ds_buf = plan->max_ne > 0 && (int64_t)workspace_bytes >= need + ds_bytes
-                               ? (uint16_t*)((unsigned char*)workspace + need)
-                               : nullptr;
+        // The dS tile store takes what the workspace holds beyond `need`, in
+        // units of one kv head's share (its q heads' tiles): with room for
+        // hc >= 1 kv heads, the kv heads are processed hc at a time through
+        // K4a + K4c; with none, K4a runs without the store and K4b recomputes.
+        const int group = g.Hq / g.Hkv;
+        const int64_t per_kvh = (int64_t)g.B * group * plan->max_ne * DS_TILE_ELEMS * 2;
+        const int64_t avail = (int64_t)workspace_bytes - need;
+        const int hc = per_kvh > 0 ? (int)std::min<int64_t>(g.Hkv, avail / per_kvh) : 0;
+        uint16_t* ds_buf = hc > 0 ? (uint16_t*)((unsigned char*)workspace + need) : nullptr;
 
         BwdPreArgs pa{};
         pa.dout = dout; pa.out = out; pa.lse = lse; pa.lse2 = lse2; pa.ndelta = ndelta;
@@ -654,6 +659,8 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
         a.B = g.B; a.S = (int32_t)g.S; a.Skv = (int32_t)g.Skv; a.Hq = g.Hq; a.Hkv = g.Hkv;
         a.nkt = plan->nkt_b;
         a.S_pad = (int32_t)plan->S_pad;
+        a.hk0 = 0;
+        a.nhk = g.Hkv;
         a.total_work = g.B * g.Hkv * plan->nkt_b;
         a.scale = g.scale;
         a.scale_log2 = g.scale * 1.4426950408889634f;
@@ -682,24 +689,41 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
             a.dv = dv + st.j * block_elems;
             a.rng = st.rng; a.t_off = st.b_off; a.t_mid = st.b_mid; a.t_ent = st.b_ent; a.t_order = st.b_order;
             a.ds_ne = st.b_ne;
+            // the dQ kernels write the accumulator on the first step (also when
+            // a step has no visible pair, in which case they write zeros)
+            const int32_t first_flag = first ? 1 : 0;
+            if (ds_buf) {
+                if (st.pairs == 0 && !first) continue;
+                da.k = a.k;
+                da.t_off = st.d_off; da.t_ent = st.d_ent; da.t_order = st.d_order;
+                da.ds_ne = st.b_ne;
+                da.first = first_flag;
+                for (int c0 = 0; c0 < g.Hkv; c0 += hc) {
+                    const int nhk = std::min(hc, g.Hkv - c0);
+                    a.hk0 = c0;
+                    a.nhk = nhk;
+                    a.total_work = g.B * nhk * plan->nkt_b;
+                    if (st.pairs > 0) {
+                        rc = hip_rc(timed(KC_BWD, s, [&] { return launch_bwd_dkdv_bf16(a, g.d, s); }));
+                        if (rc != RA_OK) return rc;
+                    }
+                    da.h0 = c0 * group;
+                    da.nh = nhk * group;
+                    da.total_work = g.B * da.nh * plan->nqt_dq;
+                    rc = hip_rc(timed(KC_BWD_DQ_DS, s, [&] { return launch_bwd_dq_ds_bf16(da, g.d, s); }));
+                    if (rc != RA_OK) return rc;
+                }
+                first = false;
+                continue;
+            }
             if (st.pairs > 0) {
                 rc = hip_rc(timed(KC_BWD, s, [&] { return launch_bwd_dkdv_bf16(a, g.d, s); }));
                 if (rc != RA_OK) return rc;
             }
-            // the dQ kernel writes the accumulator on the first step (also when a
-            // step has no visible pair, in which case it writes zeros)
             qa.k = a.k; qa.v = a.v;
             qa.rng = st.rng; qa.t_off = st.q_off; qa.t_mid = st.q_mid; qa.t_ent = st.q_ent; qa.t_order = st.q_order;
-            qa.first = first ? 1 : 0;
-            if (ds_buf && (st.pairs > 0 || first)) {
-                da.k = a.k;
-                da.t_off = st.d_off; da.t_ent = st.d_ent; da.t_order = st.d_order;
-                da.ds_ne = st.b_ne;
-                da.first = qa.first;
-                rc = hip_rc(timed(KC_BWD_DQ_DS, s, [&] { return launch_bwd_dq_ds_bf16(da, g.d, s); }));
-                if (rc != RA_OK) return rc;
-                first = false;
-            } else if (st.pairs > 0 || first) {
+            qa.first = first_flag;
+            if (st.pairs > 0 || first) {
                 rc = hip_rc(timed(KC_BWD_DQ, s, [&] { return launch_bwd_dq_bf16(qa, g.d, s); }));
                 if (rc != RA_OK) return rc;
                 first = false;

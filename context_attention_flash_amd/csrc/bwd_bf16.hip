@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int work = xcd_work_index(blockIdx.x, gridDim.x);
     if (work >= p.total_work) return;
     const int t = work % p.nkt, bh = work / p.nkt;
-    const int hk = bh % p.Hkv, b = bh / p.Hkv;
+    const int hk = p.hk0 + bh % p.nhk, b = bh / p.nhk;
     const cint_ptr ents = as_const(p.t_ent);
     const int kt = as_const(p.t_order)[t];
     const int e0 = as_const(p.t_off)[kt], e1 = as_const(p.t_off)[kt + 1];
@@ -388,7 +388,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         if (it + 1 < n_iter) load(it + 1, ent_nx, nxt);
         uint16_t* ds_tile = nullptr;   // this tile's place in the dS tile store
         if constexpr (STORE_DS)
-            ds_tile = p.ds + ((int64_t)(b * p.Hq + head_of(it)) * p.ds_ne + index_of(it)) * DS_TILE_ELEMS;
+            ds_tile = p.ds + ((int64_t)(b * p.nhk + hk - p.hk0) * group + head_of(it) - hk * group) *
+                                 p.ds_ne * DS_TILE_ELEMS +
+                      (int64_t)index_of(it) * DS_TILE_ELEMS;
         tile(cur, partial_tag, ds_tile);
         // the scalar load goes out after the tile's LDS reads: while it is in
         // flight every LDS wait must be a full one (scalar loads return out of
@@ -775,7 +777,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(DqDsArgs p) {
     const int work = xcd_work_index(blockIdx.x, gridDim.x);
     if (work >= p.total_work) return;
     const int t = work % p.nqt, bh = work / p.nqt;
-    const int h = bh % p.Hq, b = bh / p.Hq;
+    const int h = p.h0 + bh % p.nh, b = bh / p.nh;
     const int qt = as_const(p.t_order)[t];
     const int hk = (h * p.Hkv) / p.Hq;
     const cint_ptr ents = as_const(p.t_ent);
@@ -787,7 +789,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(DqDsArgs p) {
     lk.init(p.k + (int64_t)b * p.Skv * p.Hkv * DH, p.Skv, p.Hkv, hk, wave, lane);
     DsQuarterLoader<C::NDS> lds_ds;
     lds_ds.init(lane);
-    const uint16_t* ds_head = p.ds + (int64_t)(b * p.Hq + h) * p.ds_ne * DS_TILE_ELEMS;
+    const uint16_t* ds_head = p.ds + (int64_t)(b * p.nh + h - p.h0) * p.ds_ne * DS_TILE_ELEMS;
     // iteration it: key tile kt = entry (it/SPT), keys KH*(it%SPT).. of it
     auto load = [&](int it, int kt, int e, unsigned char* st) {
         lk.load(st + C::OFF_K, C::SPT * kt + it % C::SPT, wave);

@@ -61,15 +61,17 @@ struct BwdArgs {
     float* dv;
     uint16_t* ds;           // NULL, or the dS tile store of the step (see DqDsArgs)
     int32_t ds_ne;          // entries of the step's lists (tiles per (batch, q head))
+    int32_t hk0, nhk;       // the launch covers kv heads [hk0, hk0 + nhk)
     int32_t B, S, Skv, Hq, Hkv, nkt, S_pad;
-    int32_t total_work;     // B * Hkv * nkt
+    int32_t total_work;     // B * nhk * nkt
     float scale;            // softmax scale
     float scale_log2;       // softmax scale * log2(e)
 };
 
 // dS tile store: one 16 KB tile of bf16 dS = P (dP - Delta) per (batch, q head,
 // entry of the dK/dV kernel's lists), i.e. 64 query rows x 128 keys, at tile
-// index (b * Hq + h) * ds_ne + entry.  Inside a tile the values sit in the
+// index (b * nh + h - h0) * ds_ne + entry for the q heads [h0, h0 + nh) of the
+// launch (the q heads of its kv heads).  Inside a tile the values sit in the
 // register order of the dK/dV kernel: u32x4 number (w * 4 + kk) * 64 + lane
 // holds, for key 32w + lane%32, the query rows 16kk + 4(lane/32) + {0..3} and
 // 16kk + 8 + 4(lane/32) + {0..3} (8 bf16, in that order).
@@ -86,7 +88,8 @@ struct DqDsArgs {
     float* dq_acc;          // as in DqArgs
     int32_t B, S, Skv, Hq, Hkv, nqt, S_pad;
     int32_t ds_ne;
-    int32_t total_work;     // B * Hq * nqt
+    int32_t h0, nh;         // the launch covers q heads [h0, h0 + nh)
+    int32_t total_work;     // B * nh * nqt
     int32_t first;
     float scale;
 };

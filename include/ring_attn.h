@@ -184,9 +184,12 @@ int ring_attn_fwd(const ring_attn_desc* desc, const void* q, const void* k,
  * backward for every rank on zeroed dk/dv yields the full gradient, as the
  * gradient accumulators travelling around the ring would.  Requires
  * dtype == RA_BF16.  Workspace: at least ring_attn_workspace_bytes(desc, 1)
- * bytes; with ring_attn_bwd_ds_bytes(desc, cu_seqlens) bytes more, dQ is
- * built from the stored dS (same results up to summation order, less
- * work).  The contents need no initialisation and are garbage afterwards. */
+ * bytes.  Bytes beyond that hold the dS tile store: with E extra bytes and
+ * F = ring_attn_bwd_ds_bytes(desc, cu_seqlens), the kv heads are processed
+ * min(heads_kv, floor(E / (F / heads_kv))) at a time and dQ is built from the
+ * stored dS (same results up to summation order, less work); with less than
+ * F / heads_kv extra bytes, dQ recomputes S and dP.  The contents need no
+ * initialisation and are garbage afterwards. */
 int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q,
                   const void* k, const void* v, const void* out, const float* lse,
                   const int32_t* cu_seqlens, float* dq, float* dk, float* dv,

@@ -194,15 +194,21 @@ def _check_bwd(w, glob, rank, dq, dk, dv):
     return errs
 
 
-def _run_bwd(w, glob, rank, dk=None, dv=None, ds_store=True):
+def _run_bwd(w, glob, rank, dk=None, dv=None, ds_store=True, ds_kv_heads=None):
     """Backward through the C ABI; ds_store=False gives it the minimum
-    workspace, so that dQ recomputes S and dP instead of reading stored dS."""
+    workspace, so that dQ recomputes S and dP instead of reading stored dS;
+    ds_kv_heads=n gives it a dS store for n kv heads at a time."""
     sh = shard(glob, w, rank)
     desc = ca.desc_from_workload(w, rank=rank)
     q, k, v = (to_dev(sh[n], w.dtype) for n in ("q", "k", "v"))
     out, lse = ca.ring_attn_fwd(desc, q, k, v, w.cu_seqlens)
     dout = to_dev(sh["dout"], w.dtype)
-    ws = ca.alloc_workspace(desc, True, cu_seqlens=w.cu_seqlens, ds_store=ds_store)
+    if ds_kv_heads is None:
+        ws = ca.alloc_workspace(desc, True, cu_seqlens=w.cu_seqlens, ds_store=ds_store)
+    else:
+        per = -(-ca.ring_attn_bwd_ds_bytes(desc, w.cu_seqlens) // w.heads_kv)
+        ws = torch.empty(ca.ring_attn_workspace_bytes(desc, True) + ds_kv_heads * per,
+                         dtype=torch.uint8, device="cuda")
     dq, dk, dv = ca.ring_attn_bwd(desc, dout, q, k, v, out, lse, w.cu_seqlens, dk=dk, dv=dv,
                                   workspace=ws)
     torch.cuda.synchronize()
@@ -312,6 +318,21 @@ def test_bwd_edge_shapes(S):
                 say(f"bwd edge S={S} layout={layout} rank={rank} ds_store={ds_store}")
                 dq, dk, dv = _run_bwd(w, glob, rank, ds_store=ds_store)
                 _check_bwd(w, glob, rank, dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
+
+
+@pytest.mark.parametrize("layout,Hq,Hkv,ds_kv_heads", [
+    (ca.BASIC, 6, 3, 1), (ca.BASIC, 6, 3, 2), (ca.ZIGZAG, 8, 4, 3), (ca.LLAMA3, 4, 4, 1),
+    (ca.VARLEN_STRIPE, 6, 3, 2)])
+def test_bwd_ds_store_in_kv_head_passes(layout, Hq, Hkv, ds_kv_heads):
+    """A dS store for fewer kv heads than the problem has: the backward runs
+    the kv heads in passes (the last one shorter when they do not divide)."""
+    w = _small_workload(layout, True, 128, D=3, S=300, B=1, Hq=Hq, Hkv=Hkv, seed=90 + layout,
+                        with_grad=True)
+    glob = synth.draw_global(w)
+    for rank in (0, w.world - 1):
+        say(f"bwd kv-head passes layout={layout} Hq={Hq} Hkv={Hkv} per pass={ds_kv_heads} rank={rank}")
+        dq, dk, dv = _run_bwd(w, glob, rank, ds_kv_heads=ds_kv_heads)
+        _check_bwd(w, glob, rank, dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
 
 
 def test_bwd_ranks_sum_to_full_gradient():
