@@ -248,10 +248,20 @@ def main():
     total_flops = fwd_flops + bwd_flops
     value = total_flops / (ms_step * 1e-3) / 1e12
     flops_unit = w.head_dim * heads_b * pairs   # d * Hq * B * pairs
+    issued_md = os.path.join(ROOT, "profiles", f"mfma_issued_{w.name}.md")
     for name, k in kern.items():
         if name in ALGO_FLOPS_PER_PAIR:
             k["algorithmic_TFLOP/s"] = ALGO_FLOPS_PER_PAIR[name] * flops_unit / (k["ms_per_step"] * 1e-3) / 1e12
-            k["issued_TFLOP/s"] = ISSUED_FLOPS_PER_PAIR[name] * flops_unit / (k["ms_per_step"] * 1e-3) / 1e12
+            # issued: the bf16 MFMA flops the hardware counted per launch (whole
+            # tiles, masked elements included) when a summary for the current
+            # sources exists, else the per-pair count of the kernel's products
+            issued = profsum.read_issued(issued_md, ROCPROF_NAME[name])
+            if issued is not None:
+                k["issued_TFLOP/s"] = issued / (k["avg_launch_ms"] * 1e-3) / 1e12
+                k["issued_from"] = "SQ_INSTS_VALU_MFMA_MOPS_BF16"
+            else:
+                k["issued_TFLOP/s"] = ISSUED_FLOPS_PER_PAIR[name] * flops_unit / (k["ms_per_step"] * 1e-3) / 1e12
+                k["issued_from"] = "products per visible pair"
 
     # roofline of the dominant kernel (most time per step): algorithmic flops
     # per launch (per-pair figure x the visible pairs of one launch, averaged

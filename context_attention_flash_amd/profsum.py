@@ -6,6 +6,13 @@
         --fetch F_counter_collection.csv --write W_counter_collection.csv \
         --copy-fetch CF_counter_collection.csv --copy-write CW_counter_collection.csv \
         --copy-bytes N --kernel bwd_dkdv_bf16_kernel --cmds "..." --out profiles/NAME.md
+    python -m context_attention_flash_amd.profsum mfma M_counter_collection.csv \
+        --cmd "..." --title "..." --out profiles/NAME.md
+
+`mfma` turns SQ_INSTS_VALU_MFMA_MOPS_BF16 (bf16 matrix ops / 512 per
+dispatch), SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE into the bf16 flops
+each kernel issued per launch, its matrix-core busy fraction and its average
+clock, with the same source hash per kernel.
 
 `traffic` turns the FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch, as
 rocprofv3 reports them) of one kernel into bytes per launch.  Each counter is
@@ -123,6 +130,69 @@ def read_traffic(md_path: str, kernel: str):
         return None
 
 
+def _per_dispatch_all(csv_path: str, counter: str):
+    """{dispatch id: (kernel name, summed counter value)} over every kernel."""
+    vals = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        name, v = vals.get(d, (r["Kernel_Name"], 0.0))
+        vals[d] = (name, v + float(r["Counter_Value"]))
+    return vals
+
+
+def mfma_md(csv_path: str, cmd: str, title: str, n_xcd: int = 8, n_simd: int = 1024) -> str:
+    mops = _per_dispatch_all(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    busy = _per_dispatch_all(csv_path, "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui = _per_dispatch_all(csv_path, "GRBM_GUI_ACTIVE")
+    ts = {}
+    for r in csv.DictReader(open(csv_path)):
+        ts[int(r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    out = [f"# Issued bf16 MFMA work: {title}", "", "Command (from the repository root, one MI355X):",
+           "", "```", cmd, "```", "",
+           "| kernel | dispatches | issued GFLOP per launch | matrix cores busy | average clock (GHz) |",
+           "|---|---|---|---|---|"]
+    machine = []
+    for kernel in KERNEL_SOURCES:
+        ds = [d for d, (name, _) in mops.items() if kernel in name and "(" in name
+              and name.split("(")[0].split("<")[0].endswith(kernel)]
+        if not ds:
+            continue
+        fl = statistics.mean(mops[d][1] * 512.0 for d in ds)
+        util = statistics.mean(busy[d][1] / (gui[d][1] / n_xcd * n_simd) for d in ds if d in busy and d in gui)
+        clk = statistics.mean(gui[d][1] / n_xcd / ts[d] for d in ds if d in gui and ts.get(d))
+        out.append(f"| `{kernel}` | {len(ds)} | {fl / 1e9:.1f} | {100 * util:.1f}% | {clk:.2f} |")
+        machine += [f"kernel: {kernel}", f"kernel_source_sha256_16: {source_hash(kernel)}",
+                    f"issued_flops_per_launch: {fl:.6g}", ""]
+    out += ["", "Clock = GRBM_GUI_ACTIVE / 8 XCDs / kernel duration; busy = SQ_VALU_MFMA_BUSY_CYCLES /",
+            "(GRBM_GUI_ACTIVE / 8 x 1024 SIMDs).", "",
+            "Machine-readable (bench.py reads these; each hash covers that kernel's sources):", "",
+            "```", *machine, "```"]
+    return "\n".join(out) + "\n"
+
+
+def read_issued(md_path: str, kernel: str):
+    """Issued bf16 MFMA flops per launch of `kernel` from a summary written by
+    `mfma`, or None when missing or the kernel's sources changed."""
+    if not os.path.exists(md_path):
+        return None
+    cur = {}
+    for line in open(md_path):
+        m = re.match(r"^([a-z_0-9]+): (\S+)$", line.strip())
+        if not m:
+            continue
+        if m.group(1) == "kernel":
+            cur = {"kernel": m.group(2)}
+        else:
+            cur[m.group(1)] = m.group(2)
+        if cur.get("kernel") == kernel and "issued_flops_per_launch" in cur:
+            if cur.get("kernel_source_sha256_16") != source_hash(kernel):
+                return None
+            return float(cur["issued_flops_per_launch"])
+    return None
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -131,6 +201,11 @@ def main(argv=None):
     s.add_argument("--cmd", required=True)
     s.add_argument("--title", required=True)
     s.add_argument("--out", required=True)
+    mf = sub.add_parser("mfma")
+    mf.add_argument("csv")
+    mf.add_argument("--cmd", required=True)
+    mf.add_argument("--title", required=True)
+    mf.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
@@ -141,7 +216,12 @@ def main(argv=None):
     t.add_argument("--cmds", required=True, help="the commands, separated by ' ;; '")
     t.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    text = stats_md(a.csv, a.cmd, a.title) if a.mode == "stats" else traffic_md(a)
+    if a.mode == "stats":
+        text = stats_md(a.csv, a.cmd, a.title)
+    elif a.mode == "mfma":
+        text = mfma_md(a.csv, a.cmd, a.title)
+    else:
+        text = traffic_md(a)
     with open(a.out, "w") as fh:
         fh.write(text)
     print(text)
