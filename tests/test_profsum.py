@@ -30,3 +30,35 @@ def test_committed_summary_parses():
             kv[a] = b
     assert kv["kernel"] == "bwd_dkdv_bf16_kernel"
     assert float(kv["traffic_bytes_per_launch"]) > 0
+
+
+def test_mfma_summary_from_counter_rows(tmp_path):
+    """Per-kernel issued flops (MOPS x 512), busy fraction and clock from
+    counter rows summed over the XCD instances of each dispatch."""
+    import csv
+    rows = []
+    for d, name, mops, busy, gui in ((1, "void ra::fwd_step_bf16_kernel<128>(ra::FwdArgs)", 1000, 4096, 8000),
+                                     (2, "ra::bwd_dkdv_bf16_kernel<128, true>(ra::BwdArgs)", 3000, 2048, 8000),
+                                     (3, "void ra::bwd_dq_bf16_kernel<128>(ra::DqArgs)", 50, 512, 8000)):
+            for xcd in range(8):   # one row per XCD instance
+                for cname, val in (("SQ_INSTS_VALU_MFMA_MOPS_BF16", mops / 8),
+                                   ("SQ_VALU_MFMA_BUSY_CYCLES", busy / 8), ("GRBM_GUI_ACTIVE", gui / 8)):
+                    rows.append({"Dispatch_Id": d, "Kernel_Name": name, "Counter_Name": cname,
+                                 "Counter_Value": val, "Start_Timestamp": 0, "End_Timestamp": 500})
+    p = tmp_path / "c.csv"
+    with open(p, "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+    md = profsum.mfma_md(str(p), "cmd", "title")
+    out = tmp_path / "m.md"
+    out.write_text(md)
+    assert profsum.read_issued(str(out), "fwd_step_bf16_kernel") == 1000 * 512
+    assert profsum.read_issued(str(out), "bwd_dkdv_bf16_kernel") == 3000 * 512
+    assert profsum.read_issued(str(out), "bwd_dq_bf16_kernel") == 50 * 512
+    assert profsum.read_issued(str(out), "bwd_dq_ds_bf16_kernel") is None   # not in the rows
+    # busy = 4096 / (8000 / 8 * 1024) = 0.4%; clock = 8000 / 8 / 500 ns = 2.00 GHz
+    assert "| `fwd_step_bf16_kernel` | 1 | 0.0 | 0.4% | 2.00 |" in md   # 512 kFLOP
+    stale = out.read_text().replace(profsum.source_hash("fwd_step_bf16_kernel"), "0" * 16)
+    out.write_text(stale)
+    assert profsum.read_issued(str(out), "fwd_step_bf16_kernel") is None
