@@ -208,20 +208,28 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // is fetched one iteration ahead so that its scalar load is off the path.
     DkdvLoader<DH> ld;
     ld.init(p, b, wave, lane);
-    auto index_of = [&](int it) {   // position of iteration it's tile in the list
-        const bool full = it < nF;
-        const int n = full ? m - e0 : e1 - m;
-        const int jt = full ? it : it - nF;
-        return (full ? e0 : m) + jt % n;
+    // Iteration cursor: the full tiles of every q head of the group, then the
+    // partial ones; (hd, jt) = (q head within the group, position in the
+    // class's list), base and n = that class's first entry and length.  It
+    // advances by additions only (no division per iteration).
+    struct Cursor {
+        int hd, jt, base, n;
     };
-    auto entry_of = [&](int it) { return ents[index_of(it)]; };
-    auto head_of = [&](int it) {
-        const bool full = it < nF;
-        const int n = full ? m - e0 : e1 - m;
-        return hk * group + (full ? it : it - nF) / n;
+    auto advance = [&](Cursor c) {
+        if (++c.jt == c.n) {
+            c.jt = 0;
+            if (++c.hd == group && c.base == e0 && m != e0) {   // full tiles done
+                c.hd = 0;
+                c.base = m;
+                c.n = e1 - m;
+            }
+        }
+        return c;
     };
-    auto load = [&](int it, int ent, unsigned char* st) {
-        ld.load(st, p, head_of(it), ent & 0x7fffffff, wave, lane);
+    auto index_of = [&](const Cursor& c) { return c.base + c.jt; };
+    auto head_of = [&](const Cursor& c) { return hk * group + c.hd; };
+    auto load = [&](const Cursor& c, int ent, unsigned char* st) {
+        ld.load(st, p, head_of(c), ent & 0x7fffffff, wave, lane);
     };
 
     // S = Q K^T and dP - Delta = dO V^T - Delta for the 32-row half mt of the
@@ -375,7 +383,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // Iteration it: the carried dV/dK MFMAs of tile it-1, then the barrier
     // that makes tile it visible and frees the other stage, which receives
     // tile it+1.  Even iterations use stage A, odd ones stage B.
-    int ent_nx = n_iter > 1 ? entry_of(1) : 0;   // entry of tile it+1
+    // cursors of tiles it, it+1 and it+2
+    Cursor cu0 = m != e0 ? Cursor{0, 0, e0, m - e0} : Cursor{0, 0, m, e1 - m};
+    Cursor cu1 = advance(cu0), cu2 = advance(cu1);
+    int ent_nx = n_iter > 1 ? ents[index_of(cu1)] : 0;   // entry of tile it+1
     auto step = [&](int it, unsigned char* cur, unsigned char* nxt, auto partial_tag) {
         mfma_half(c_oa, c_qa, c_pb, c_db);
 #pragma unroll
@@ -385,22 +396,24 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         // in flight (vmcnt <= 4: vector memory operations complete in order)
         __builtin_amdgcn_s_waitcnt(STORE_DS ? 0x0004 : 0);
         __syncthreads();
-        if (it + 1 < n_iter) load(it + 1, ent_nx, nxt);
+        if (it + 1 < n_iter) load(cu1, ent_nx, nxt);
         uint16_t* ds_tile = nullptr;   // this tile's place in the dS tile store
         if constexpr (STORE_DS)
-            ds_tile = p.ds + ((int64_t)(b * p.nhk + hk - p.hk0) * group + head_of(it) - hk * group) *
-                                 p.ds_ne * DS_TILE_ELEMS +
-                      (int64_t)index_of(it) * DS_TILE_ELEMS;
+            ds_tile = p.ds + ((int64_t)(b * p.nhk + hk - p.hk0) * group + cu0.hd) * p.ds_ne * DS_TILE_ELEMS +
+                      (int64_t)index_of(cu0) * DS_TILE_ELEMS;
         tile(cur, partial_tag, ds_tile);
         // the scalar load goes out after the tile's LDS reads: while it is in
         // flight every LDS wait must be a full one (scalar loads return out of
         // order)
-        if (it + 2 < n_iter) ent_nx = entry_of(it + 2);
+        if (it + 2 < n_iter) ent_nx = ents[index_of(cu2)];
+        cu0 = cu1;
+        cu1 = cu2;
+        cu2 = advance(cu2);
     };
     // The unmasked loop covers an even number of iterations; a last full tile
     // left over goes through the masked loop, where the mask keeps every key.
     const int nF2 = nF & ~1;
-    if (n_iter > 0) load(0, entry_of(0), stA);
+    if (n_iter > 0) load(cu0, ents[index_of(cu0)], stA);
     if constexpr (STORE_DS) __builtin_amdgcn_s_waitcnt(0);   // the first wait counts on none in flight
     int it = 0;
     for (; it < nF2; it += 2) {
