@@ -28,6 +28,10 @@
  *   - Host pointers are read during the call only.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *     device work is enqueued on it; calls return without synchronising.
+ *   - The first call for a shape builds its plan (host work, one hipMalloc
+ *     and a synchronous upload); later calls for that shape enqueue kernels
+ *     only (no allocation, no memset, no copy), so they can be captured into
+ *     a HIP graph and replayed.
  *   - Return value: 0 on success, a negative RA_E_* code on failure.  All
  *     argument validation happens before any device work is enqueued, so a
  *     failing call leaves every buffer untouched.  Nothing is printed and no

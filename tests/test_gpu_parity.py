@@ -397,3 +397,52 @@ def test_random_configs_fwd_bwd(seed):
         for ds_store in (True, False):
             dq, dk, dv = _run_bwd(w, glob, rank, ds_store=ds_store)
             _check_bwd(w, glob, rank, dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
+
+
+def test_hip_graph_capture_and_replay():
+    """After a first eager call (which builds the plan), the forward and the
+    backward enqueue only kernels: they can be captured into a HIP graph.  The
+    graph is replayed several times, with other work and synchronisations in
+    between, and every replay must reproduce the eager results exactly."""
+    w = _small_workload(ca.ZIGZAG, True, 128, D=4, S=320, B=1, seed=123, with_grad=True)
+    glob = synth.draw_global(w)
+    sh = shard(glob, w, 1)
+    desc = ca.desc_from_workload(w, rank=1)
+    q, k, v = (to_dev(sh[n], w.dtype) for n in ("q", "k", "v"))
+    dout = to_dev(sh["dout"], w.dtype)
+    out = torch.empty_like(q)
+    lse = torch.empty(w.batch, w.heads_q, w.shard, device="cuda")
+    dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dk = torch.zeros(k.shape, dtype=torch.float32, device="cuda")
+    dv = torch.zeros(v.shape, dtype=torch.float32, device="cuda")
+    ws_f = ca.alloc_workspace(desc, False)
+    ws_b = ca.alloc_workspace(desc, True)
+
+    def run(stream=None):
+        dk.zero_()   # a fill kernel, not a memset node
+        dv.zero_()
+        ca.ring_attn_fwd(desc, q, k, v, None, out, lse, ws_f, stream=stream)
+        ca.ring_attn_bwd(desc, dout, q, k, v, out, lse, None, dq, dk, dv, ws_b, stream=stream)
+
+    say("graph: eager reference")
+    run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, lse, dq, dk, dv)]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run(stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (out, lse, dq, dk, dv):   # eager work between replays
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        say(f"graph: replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("out", "lse", "dq", "dk", "dv"), (out, lse, dq, dk, dv), ref):
+            assert torch.equal(got, want), (rep, name)
+    _check_fwd(w, glob, 1, out.float().cpu().numpy(), lse.cpu().numpy())
