@@ -797,7 +797,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(DqDsArgs p) {
     const int e0 = as_const(p.t_off)[qt], e1 = as_const(p.t_off)[qt + 1];
     const int n_iter = C::SPT * (e1 - e0);   // SPT stages per 128-key tile
 
-    // K rows of the stage (64 keys of head hk) and this wave's quarter of dS
+    // K rows of the stage (KH keys of head hk) and this wave's quarter of dS
     BufTileLoader<DH, C::KH> lk;
     lk.init(p.k + (int64_t)b * p.Skv * p.Hkv * DH, p.Skv, p.Hkv, hk, wave, lane);
     DsQuarterLoader<C::NDS> lds_ds;
