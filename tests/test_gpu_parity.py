@@ -381,7 +381,20 @@ def _random_config(seed):
                           seed=2000 + seed, cu_seqlens=cu, with_grad=True, window=window)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(12))
+def test_random_configs_fwd_f32(seed):
+    """The fp32 forward (both merge modes) on seeded random configurations."""
+    w = _random_config(100 + seed).replace(dtype="f32", with_grad=False, value_scale=0.5)
+    glob = synth.draw_global(w)
+    for rank in sorted({0, w.world - 1}):
+        for mm in (ca.RA_MERGE_FUSED, ca.RA_MERGE_SEPARATE):
+            say(f"random f32 seed={seed} layout={w.layout} D={w.world} S={w.shard} d={w.head_dim} "
+                f"window={w.window} rank={rank} merge={mm}")
+            _, _, _, out, lse = _run_fwd(w, glob, rank, mm)
+            _check_fwd(w, glob, rank, out, lse)
+
+
+@pytest.mark.parametrize("seed", range(24))
 def test_random_configs_fwd_bwd(seed):
     """Seeded random shapes: layout, world, shard length, GQA ratio, head dim,
     causal flag, window, batch and document split; forward and both backward
