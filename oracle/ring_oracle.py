@@ -23,8 +23,9 @@ Sources (web pages on ring attention; sections named as on the pages):
 The method is exact ([RA] "Online softmax across ring steps"; [IQ]), so the
 oracle is the plain definition of softmax attention over *global* token
 positions, restricted to the rank's rows.  Readings taken where the pages are
-silent (layout definitions of zigzag/stripe/varlen-ring, the LSE base, GQA
-head mapping, fully-masked rows) are stated at each function.
+silent (layout definitions of zigzag/stripe/varlen-ring and of the packed
+zigzag/stripe forms, the sliding window, the LSE base, GQA head mapping,
+fully-masked rows) are stated at each function.
 
 Every function here is pinned by tests that do not re-type its formulas: the
 pages' two-device example, ring == unblocked for every D and layout, brute
