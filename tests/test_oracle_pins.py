@@ -227,6 +227,102 @@ def test_ring_order():
 
 
 # ---------------------------------------------------------------------------
+# The packed ring layout (VARLEN_RING): rank -> part map and the step rule
+# ---------------------------------------------------------------------------
+
+# Written out by hand from the layout's definition: documents [0, 8) and
+# [8, 20) over D = 4 ranks have parts of 2 and 3 tokens; rank r holds part r of
+# each document, in document order.
+VARLEN_RING_LITERAL = {"cu": [0, 8, 20], "world": 4,
+                       "ranks": [[0, 1, 8, 9, 10], [2, 3, 11, 12, 13],
+                                 [4, 5, 14, 15, 16], [6, 7, 17, 18, 19]]}
+
+
+def _varlen_ring_pin_failures(mod):
+    """Every failed check of the packed ring layout against facts the pages fix
+    (instagit/nanotron "Forward Pass Implementation": the varlen forward runs
+    a step only when step <= rank under a causal mask; skillfed "ring-flash-
+    attn": every variant comes in a varlen form that shares one cu_seqlens for
+    q and kv).  Returns a list of strings; empty when the oracle passes."""
+    bad = []
+    L = VARLEN_RING_LITERAL
+    for r, want in enumerate(L["ranks"]):
+        got = mod.positions(VARLEN_RING, L["cu"][-1], L["world"], r, L["cu"]).tolist()
+        if got != want:
+            bad.append(f"literal rank {r}: {got} != {want}")
+    # Causal pair counts per step, per document of length L_k (part P = L_k/D):
+    # a block that precedes the rank's part in every document is fully visible
+    # (P^2 pairs), the rank's own part is a causal triangle (P(P+1)/2), and a
+    # later block is invisible; so exactly the steps s <= rank are active.
+    D = 4
+    cu = [0, 8, 20, 44, 48]   # lengths 8, 12, 24, 4: parts 2, 3, 6, 1
+    parts = np.diff(cu) // D
+    for r in range(D):
+        counts = mod.step_pair_counts(VARLEN_RING, cu[-1], D, r, True, cu)
+        for s, j, pairs in counts:
+            want = int((parts ** 2).sum() if j < r else
+                       (parts * (parts + 1) // 2).sum() if j == r else 0)
+            if pairs != want:
+                bad.append(f"rank {r} step {s} block {j}: {pairs} pairs != {want}")
+        active = [s for s, _, p in counts if p > 0]
+        if active != list(range(r + 1)):
+            bad.append(f"rank {r}: active steps {active} != step <= rank")
+    # The causal rank share with the steps s > rank skipped equals full
+    # per-document causal attention (plain definition, written out here over
+    # the whole packed stream) restricted to the rank's rows.
+    rng = np.random.default_rng(31)
+    N = cu[-1]
+    q, k, v = _inputs(rng, 1, N, 2, 2, 8)
+    t = np.arange(N)
+    doc = np.searchsorted(np.asarray(cu), t, side="right") - 1
+    mask = (t[None, :] <= t[:, None]) & (doc[None, :] == doc[:, None])
+    sc = np.einsum("thd,uhd->htu", q[0], k[0]) / math.sqrt(8)
+    sc = np.where(mask[None], sc, -np.inf)
+    p = np.exp(sc - sc.max(axis=2, keepdims=True))
+    p /= p.sum(axis=2, keepdims=True)
+    full = np.einsum("htu,uhd->thd", p, v[0])
+    for r in range(D):
+        rows = mod.positions(VARLEN_RING, N, D, r, cu)
+        parts_seen = []
+        ring, _ = mod.ring_forward(q, k, v, VARLEN_RING, D, r, True, cu, partial_out=parts_seen)
+        kept = [(s, j, o, l) for s, j, o, l in parts_seen if s <= r]
+        o_run, l_run = kept[0][2], kept[0][3]
+        for _, _, o, l in kept[1:]:
+            o_run, l_run = mod.lse_merge(o_run, l_run, o, l)
+        skipped = np.transpose(o_run, (0, 2, 1, 3))[0]
+        if np.abs(skipped - full[rows]).max() > 1e-12 or np.abs(ring[0] - full[rows]).max() > 1e-12:
+            bad.append(f"rank {r}: rank share with steps s > rank skipped != causal attention")
+    return bad
+
+
+def test_varlen_ring_layout_and_step_rule():
+    assert _varlen_ring_pin_failures(oracle) == []
+
+
+@pytest.mark.parametrize("plant", ["reversed_parts", "interleaved_parts"])
+def test_planted_varlen_ring_map_fails(plant, monkeypatch):
+    """A rank-reversed part map (rank r holds part D-1-r) or an in-document
+    interleave (rank r holds tokens a + r + D*i) must fail the pins above."""
+    import oracle.ring_oracle as ro
+    good = ro.positions
+
+    def bad_positions(layout, n, world, rank, cu_seqlens=None):
+        if layout != VARLEN_RING:
+            return good(layout, n, world, rank, cu_seqlens)
+        parts = []
+        for a, b in zip(cu_seqlens[:-1], cu_seqlens[1:]):
+            part = (b - a) // world
+            if plant == "reversed_parts":
+                parts.append(a + (world - 1 - rank) * part + np.arange(part, dtype=np.int64))
+            else:
+                parts.append(a + rank + world * np.arange(part, dtype=np.int64))
+        return np.concatenate(parts)
+
+    monkeypatch.setattr(ro, "positions", bad_positions)
+    assert len(_varlen_ring_pin_failures(ro)) > 0
+
+
+# ---------------------------------------------------------------------------
 # Brute force with explicit loops
 # ---------------------------------------------------------------------------
 
