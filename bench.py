@@ -61,44 +61,91 @@ def build_inputs(ca, w, torch):
     return g, desc, t
 
 
-def cpu_baseline(w, g, budget_s: float):
-    """The fp64 oracle on a bounded sample of the same workload: the forward
-    (and backward, when the workload has one) of consecutive query rows of head
-    0, chunk after chunk until ~budget_s of CPU time has been spent."""
+def _oracle_worker(args):
+    """One host process of the CPU baseline: the fp64 oracle's forward (and
+    backward) of one q head's rows, heaviest first, 128 rows at a time, until
+    its share of the time budget is spent.  BLAS runs single-threaded here
+    (the pool sets the thread variables before the workers start)."""
+    (w, h, q1, k1, v1, dout1, budget_s) = args
     import oracle
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max([i.get("num_threads", 1) for i in info] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
     S = w.seqlen // w.world
     cu = list(w.cu_seqlens) if w.cu_seqlens else None
     pos_q = oracle.positions(w.layout, w.seqlen, w.world, w.rank, cu)
-    dout_local = g["dout"][:, pos_q] if w.with_grad else None
-    chunk = 128
-    done_rows = 0
-    flops = 0.0
+    chunk, done_rows, flops = 128, 0, 0.0
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < budget_s and done_rows < S:
-        hi = S - done_rows  # the heaviest rows of a causal shard first
+        hi = S - done_rows   # the heaviest rows of a causal shard first
         rows = np.arange(max(0, hi - chunk), hi)
-        oracle.rank_share_forward(g["q"], g["k"], g["v"], w.layout, w.world, w.rank, w.causal, cu,
+        oracle.rank_share_forward(q1, k1, v1, w.layout, w.world, w.rank, w.causal, cu,
                                   rows=rows, heads=[0])
         m = oracle.allowed(pos_q[rows], np.arange(w.seqlen), w.causal,
                            cu if w.layout in oracle.PACKED else None)
         pairs = float(m.sum())
         flops += 4.0 * w.head_dim * pairs
-        if w.with_grad:
-            oracle.rank_share_backward(g["q"], g["k"], g["v"], dout_local, w.layout, w.world,
-                                       w.rank, w.causal, cu, rows=rows, heads=[0])
+        if dout1 is not None:
+            oracle.rank_share_backward(q1, k1, v1, dout1, w.layout, w.world, w.rank, w.causal,
+                                       cu, rows=rows, heads=[0])
             flops += 10.0 * w.head_dim * pairs
         done_rows += len(rows)
-    el = time.perf_counter() - t0
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 numpy oracle, {'fwd+bwd' if w.with_grad else 'fwd'} of {done_rows} "
-                      f"query rows x 1 head of the same rank share ({flops / 1e9:.1f} GFLOP "
-                      f"algorithmic) in {el:.1f} s"}
+    return h, done_rows, flops, time.perf_counter() - t0
+
+
+# Host cores the baseline may use: the CPU share of one GPU on the boxes this
+# runs on (what os.cpu_count() reports there can be the whole machine).
+HOST_CORE_SHARE = 16
+
+
+def start_host_pool(w):
+    """The worker processes of the CPU baseline, one per host core of the share
+    (at most one per q head), each with one BLAS thread.  They are started
+    before this process touches the GPU, so no child is ever started from a
+    process that holds a GPU context."""
+    import multiprocessing as mp
+    workers = max(1, min(os.cpu_count() or 1, HOST_CORE_SHARE, w.batch * w.heads_q))
+    saved = {v: os.environ.get(v) for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                            "MKL_NUM_THREADS")}
+    for var in saved:
+        os.environ[var] = "1"   # inherited by the spawned workers
+    pool = mp.get_context("spawn").Pool(workers)
+    for var, val in saved.items():
+        if val is None:
+            os.environ.pop(var, None)
+        else:
+            os.environ[var] = val
+    return pool, workers
+
+
+def cpu_baseline(w, g, budget_s: float, pool, workers: int):
+    """The fp64 oracle timed on the host cores, on a bounded sample of the same
+    workload: a process pool over (batch, q head) with one BLAS thread per
+    worker, each worker taking the rows of one head, heaviest first, for about
+    budget_s seconds."""
+    n_cpu = os.cpu_count() or 1
+    group = w.heads_q // w.heads_kv
+    pos_q = None
+    if w.with_grad:
+        import oracle
+        cu = list(w.cu_seqlens) if w.cu_seqlens else None
+        pos_q = oracle.positions(w.layout, w.seqlen, w.world, w.rank, cu)
+    tasks = []
+    for i in range(workers):   # (batch 0, q head i): one head's slices per worker
+        h, hk = i % w.heads_q, (i % w.heads_q) // group
+        sl = lambda x, hh: np.ascontiguousarray(x[:1, :, hh:hh + 1])
+        d1 = np.ascontiguousarray(g["dout"][:1, pos_q, h:h + 1]) if w.with_grad else None
+        tasks.append((w.replace(batch=1, heads_q=1, heads_kv=1), h, sl(g["q"], h), sl(g["k"], hk),
+                      sl(g["v"], hk), d1, budget_s))
+    t0 = time.perf_counter()
+    res = pool.map(_oracle_worker, tasks, chunksize=1)
+    wall = time.perf_counter() - t0
+    busy = max(r[3] for r in res)
+    rows = sum(r[1] for r in res)
+    flops = sum(r[2] for r in res)
+    return {"value": flops / busy / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+            "host_cpu_count": n_cpu,
+            "sample": f"fp64 numpy oracle, {'fwd+bwd' if w.with_grad else 'fwd'} of {rows} query "
+                      f"rows in all ({workers} worker processes, one q head each, 1 BLAS thread "
+                      f"each, the heaviest rows of the rank share first; {flops / 1e9:.1f} GFLOP "
+                      f"algorithmic in {busy:.1f} s of compute, {wall:.1f} s with start-up)"}
 
 
 def merge_bandwidth(ca, torch, rows=524288, d=128, reps=20):
@@ -121,8 +168,56 @@ def merge_bandwidth(ca, torch, rows=524288, d=128, reps=20):
     ca.ring_attn_timing_enable(False)
     nbytes = (12 * d + 12) * rows
     gbs = nbytes / (ms / n * 1e-3) / 1e9
+    from context_attention_flash_amd import profsum
+    # HBM bytes per launch counted by FETCH_SIZE + WRITE_SIZE (scaled by the
+    # copy calibration), while the summary matches the kernel's sources
+    traffic = profsum.read_traffic(os.path.join(ROOT, "profiles", MERGE_TRAFFIC_MD), "lse_merge_kernel")
     return {"kernel": "lse_merge", "rows": rows, "head_dim": d, "bytes_per_launch": nbytes,
-            "avg_ms": ms / n, "GB/s": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS}
+            "avg_ms": ms / n, "GB/s": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS,
+            "traffic": traffic,
+            "traffic_GB/s": None if traffic is None else traffic / (ms / n * 1e-3) / 1e9}
+
+
+MERGE_TRAFFIC_MD = "traffic_lse_merge_kernel_rows524288_d128.md"
+
+
+# Forward-only configurations timed in the same run as the headline step (their
+# parity is covered by the tests; here they are timed on seeded N(0,1) inputs
+# drawn on the device, which have the same distribution as the tests' inputs).
+OTHER_FWD = ("basic_s4096", "zigzag", "llama3")
+
+
+def time_forward(ca, torch, synth, name, steps, warmup):
+    w = synth.WORKLOADS[name]
+    desc = ca.desc_from_workload(w)
+    S, Skv, nb = ca.shard_sizes(desc)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    dt = torch.bfloat16
+    q = torch.randn(w.batch, S, w.heads_q, w.head_dim, device="cuda", generator=gen).to(dt)
+    k = torch.randn(nb, w.batch, Skv, w.heads_kv, w.head_dim, device="cuda", generator=gen).to(dt)
+    v = torch.randn(nb, w.batch, Skv, w.heads_kv, w.head_dim, device="cuda", generator=gen).to(dt)
+    out = torch.empty_like(q)
+    lse = torch.empty(w.batch, w.heads_q, S, device="cuda")
+    ws = ca.alloc_workspace(desc, False)
+    pairs = sum(p for _, _, p in ca.ring_attn_schedule(desc, w.cu_seqlens))
+    flops = 4.0 * w.head_dim * w.heads_q * w.batch * pairs
+    for _ in range(warmup):
+        ca.ring_attn_fwd(desc, q, k, v, w.cu_seqlens, out, lse, ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ca.ring_attn_fwd(desc, q, k, v, w.cu_seqlens, out, lse, ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    assert torch.isfinite(out.float()).all().item(), f"{name}: non-finite output"
+    tf = flops / (ms * 1e-3) / 1e12
+    del q, k, v, out, lse, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"{name}: {synth.LAYOUT_NAMES[w.layout]} causal fwd rank share, "
+                        f"N {w.seqlen}, D {w.world}, rank {w.rank}, {w.heads_q}/{w.heads_kv} heads, "
+                        f"d {w.head_dim}", "fwd_tflop": flops / 1e12, "ms": ms, "TFLOP/s": tf,
+            "frac_peak": tf / PEAK_BF16_TFLOPS, "steps": steps}
 
 
 # Algorithmic flops per visible (query, key) pair and query head, per kernel.
@@ -180,22 +275,35 @@ def main():
                     help="give the backward no room for the dS tile store (dQ recomputes S, dP)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the copy kernel used to scale the traffic counters")
+    ap.add_argument("--merge-only", action="store_true",
+                    help="only run the standalone LSE merge measurement")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the forward timing of the other bf16 configurations")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one rank's share on ONE GPU; runs on several GPUs are not "
-              "supported (use --gpus 1).", file=sys.stderr)
+        print("bench.py measures one rank's share on ONE GPU; this build has no multi-GPU "
+              "path (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
+
+    from context_attention_flash_amd import synth
+    w = synth.WORKLOADS[args.workload]
+    if args.with_grad:
+        w = w.replace(with_grad=True)
+    pool = None
+    if not (args.no_cpu_baseline or args.calibrate_copy or args.merge_only):
+        pool, workers = start_host_pool(w)   # before any GPU call
 
     import torch
     if args.calibrate_copy:
         calibrate_copy(torch)
         return
     import context_attention_flash_amd as ca
-    from context_attention_flash_amd import profsum, synth
+    from context_attention_flash_amd import profsum
+    if args.merge_only:
+        torch.cuda.set_device(0)
+        print(json.dumps({"merge": merge_bandwidth(ca, torch)}), flush=True)
+        return
 
-    w = synth.WORKLOADS[args.workload]
-    if args.with_grad:
-        w = w.replace(with_grad=True)
     torch.cuda.set_device(0)
     g, desc, t = build_inputs(ca, w, torch)
     sched = ca.ring_attn_schedule(desc, w.cu_seqlens)
@@ -299,9 +407,20 @@ def main():
     }
     if not args.no_merge:
         res["merge"] = merge_bandwidth(ca, torch)
-    if not args.no_cpu_baseline:
+    if not args.no_other and args.workload == "basic_s8192":
+        del t, out, lse
+        if w.with_grad:
+            del ws_b, dq, dk, dv
+        torch.cuda.empty_cache()
+        res["other_workloads"] = {}
+        for name in OTHER_FWD:
+            log(f"forward of {name} ...")
+            res["other_workloads"][name] = time_forward(ca, torch, synth, name, 10, 3)
+    if pool is not None:
         log("timing the oracle on the host ...")
-        res["cpu_baseline"] = cpu_baseline(w, g, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(w, g, args.cpu_budget, pool, workers)
+        pool.close()
+        pool.join()
     print(json.dumps(res), flush=True)
 
 

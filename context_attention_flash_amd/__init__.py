@@ -66,6 +66,8 @@ _SIGS = {
     "ring_attn_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "ring_attn_timing_read": (ctypes.c_int, [ctypes.c_char_p, _P, _P]),
     "ring_attn_clear_cache": (ctypes.c_int, []),
+    "ring_attn_plan_cache_limit": (ctypes.c_int, [ctypes.c_int32]),
+    "ring_attn_plan_cache_info": (ctypes.c_int, [_P, _P]),
     "ring_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "ring_attn_version": (ctypes.c_int, []),
 }
@@ -337,3 +339,20 @@ def ring_attn_timing_read(name: str):
 
 def ring_attn_clear_cache():
     _check(lib().ring_attn_clear_cache(), "ring_attn_clear_cache")
+
+
+def ring_attn_plan_cache_limit(max_plans: int) -> int:
+    """Set the most plans the library caches; returns the previous limit."""
+    rc = lib().ring_attn_plan_cache_limit(int(max_plans))
+    if rc < 0:
+        raise RingAttnError(rc, "ring_attn_plan_cache_limit")
+    return int(rc)
+
+
+def ring_attn_plan_cache_info():
+    """(number of cached plans, device bytes they hold)."""
+    n = ctypes.c_int64(0)
+    b = ctypes.c_int64(0)
+    _check(lib().ring_attn_plan_cache_info(ctypes.byref(n), ctypes.byref(b)),
+           "ring_attn_plan_cache_info")
+    return int(n.value), int(b.value)

@@ -23,15 +23,17 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{os.path.join(ROOT, 'include')}", f"
           "--offload-arch=gfx950",
           # keep the compiler away from packed fp32 instructions
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          # no value in these kernels is ever NaN; without this every fmaxf
-          # first quiets its operands (one extra instruction per value)
-          "-fno-honor-nans",
           "-Wno-unused-command-line-argument"]
+# Kernel sources only: no value in the kernels is ever NaN, and without this
+# every fmaxf first quiets its operands (one extra instruction per value).  The
+# host sources keep IEEE semantics (argument checks test for NaN).
+KERNEL_ONLY = ["-fno-honor-nans"]
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = KERNEL_ONLY if src.endswith(".hip") else []
+    cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <array>
+#include <list>
 #include <cstring>
 #include <map>
 #include <memory>
@@ -52,6 +53,7 @@ struct DevStep {
 
 struct Plan {
     int device = 0;
+    size_t bytes = 0;   // device bytes held
     int64_t S_pad = 0;
     int32_t nqt = 0;    // forward query tiles
     int32_t nkt_b = 0;  // backward key tiles
@@ -63,14 +65,30 @@ struct Plan {
         if (dbuf) {
             int cur = 0;
             if (hipGetDevice(&cur) == hipSuccess && cur != device) hipSetDevice(device);
+            // kernels enqueued earlier on any stream may still read the plan
+            (void)hipDeviceSynchronize();
             (void)hipFree(dbuf);
             if (cur != device) hipSetDevice(cur);
         }
     }
 };
 
+// Plan cache: least recently used first out, at most g_plan_limit plans.  A
+// call holds its plan through a shared_ptr, so an eviction (or
+// ring_attn_clear_cache) by another thread frees the plan only after that
+// call has enqueued its kernels; the destructor then waits for the device.
 std::mutex g_plan_mu;
-std::map<std::string, std::unique_ptr<Plan>> g_plans;
+std::list<std::pair<std::string, std::shared_ptr<Plan>>> g_plans;   // most recent first
+std::map<std::string, decltype(g_plans)::iterator> g_plan_index;
+int32_t g_plan_limit = 32;
+
+void evict_plans_locked(std::vector<std::shared_ptr<Plan>>& dropped) {
+    while ((int64_t)g_plans.size() > g_plan_limit) {
+        dropped.push_back(std::move(g_plans.back().second));
+        g_plan_index.erase(g_plans.back().first);
+        g_plans.pop_back();
+    }
+}
 
 // Host image of a plan before upload: a list of int32 arrays.
 struct HostArrays {
@@ -216,6 +234,7 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
         offs[i] = total;
         total += round_up((int64_t)std::max<size_t>(1, H.arrays[i].size()) * 4, 256);
     }
+    plan->bytes = total;
     std::vector<unsigned char> img(total, 0);
     for (size_t i = 0; i < H.arrays.size(); ++i)
         if (!H.arrays[i].empty())
@@ -250,19 +269,27 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
     return RA_OK;
 }
 
-int get_plan(const Geometry& g, const Plan** out) {
+int get_plan(const Geometry& g, std::shared_ptr<const Plan>* out) {
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return RA_E_HIP;
     const std::string key = std::to_string(device) + "#" + plan_key(g);
-    std::lock_guard<std::mutex> lock(g_plan_mu);
-    auto it = g_plans.find(key);
-    if (it == g_plans.end()) {
+    std::vector<std::shared_ptr<Plan>> dropped;   // freed after the lock is released
+    {
+        std::lock_guard<std::mutex> lock(g_plan_mu);
+        auto it = g_plan_index.find(key);
+        if (it != g_plan_index.end()) {
+            g_plans.splice(g_plans.begin(), g_plans, it->second);   // now most recent
+            *out = g_plans.front().second;
+            return RA_OK;
+        }
         std::unique_ptr<Plan> p;
         const int rc = build_plan(g, device, p);
         if (rc != RA_OK) return rc;
-        it = g_plans.emplace(key, std::move(p)).first;
+        g_plans.emplace_front(key, std::shared_ptr<Plan>(std::move(p)));
+        g_plan_index[key] = g_plans.begin();
+        *out = g_plans.front().second;
+        evict_plans_locked(dropped);
     }
-    *out = it->second.get();
     return RA_OK;
 }
 
@@ -386,6 +413,7 @@ int64_t host_max_ne(const Geometry& g) {
         best = std::max(best, ne);
     }
     std::lock_guard<std::mutex> lock(mu);
+    if (memo.size() >= 256) memo.clear();   // bounded: one entry per geometry seen
     memo[key] = best;
     return best;
 }
@@ -419,13 +447,14 @@ const char* ring_attn_strerror(int code) {
         case RA_E_DIVISIBILITY: return "seqlen not divisible by world (2*world for zigzag)";
         case RA_E_CU_SEQLENS:
             return "cu_seqlens must start at 0, be non-decreasing and end at seqlen; "
-                   "varlen-ring document lengths must be multiples of world";
+                   "document lengths must be multiples of world (varlen ring, varlen "
+                   "stripe) or of 2*world (varlen zigzag)";
         case RA_E_HEADS: return "heads_q is not a multiple of heads_kv";
         case RA_E_UNSUPPORTED: return "no kernel for this head_dim / dtype combination";
         case RA_E_WORKSPACE: return "workspace is NULL or smaller than required";
         case RA_E_LAYOUT: return "unknown layout, or batch != 1 with a varlen layout";
         case RA_E_HIP: return "the HIP runtime reported an error";
-        case RA_E_ARG: return "an argument is out of range";
+        case RA_E_ARG: return "an argument is out of range (or a NaN / infinite softmax scale)";
         default: return "unknown error code";
     }
 }
@@ -543,7 +572,7 @@ int ring_attn_fwd(const ring_attn_desc* desc, const void* q, const void* k, cons
         if (!q || !k || !v || !out || !lse) return RA_E_NULL;
         const int64_t need = fwd_workspace(g);
         if (!workspace || (int64_t)workspace_bytes < need) return RA_E_WORKSPACE;
-        const Plan* plan = nullptr;
+        std::shared_ptr<const Plan> plan;
         if ((rc = get_plan(g, &plan)) != RA_OK) return rc;
         hipStream_t s = (hipStream_t)stream;
 
@@ -629,7 +658,7 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
         if (!dout || !q || !k || !v || !out || !lse || !dq || !dk || !dv) return RA_E_NULL;
         const int64_t need = bwd_workspace(g);
         if (!workspace || (int64_t)workspace_bytes < need) return RA_E_WORKSPACE;
-        const Plan* plan = nullptr;
+        std::shared_ptr<const Plan> plan;
         if ((rc = get_plan(g, &plan)) != RA_OK) return rc;
         hipStream_t s = (hipStream_t)stream;
         float* lse2 = (float*)workspace;
@@ -769,8 +798,32 @@ int ring_attn_timing_read(const char* name, int64_t* launches, double* total_ms)
 }
 
 int ring_attn_clear_cache(void) {
+    decltype(g_plans) dropped;
+    {
+        std::lock_guard<std::mutex> lock(g_plan_mu);
+        dropped.swap(g_plans);
+        g_plan_index.clear();
+    }
+    return RA_OK;   // plans still held by a call in flight are freed when it returns
+}
+
+int ring_attn_plan_cache_limit(int32_t max_plans) {
+    if (max_plans < 1) return RA_E_ARG;
+    std::vector<std::shared_ptr<Plan>> dropped;
     std::lock_guard<std::mutex> lock(g_plan_mu);
-    g_plans.clear();
+    const int32_t prev = g_plan_limit;
+    g_plan_limit = max_plans;
+    evict_plans_locked(dropped);
+    return prev;
+}
+
+int ring_attn_plan_cache_info(int64_t* n_plans, int64_t* device_bytes) {
+    if (!n_plans || !device_bytes) return RA_E_NULL;
+    std::lock_guard<std::mutex> lock(g_plan_mu);
+    *n_plans = (int64_t)g_plans.size();
+    int64_t b = 0;
+    for (const auto& e : g_plans) b += (int64_t)e.second->bytes;
+    *device_bytes = b;
     return RA_OK;
 }
 

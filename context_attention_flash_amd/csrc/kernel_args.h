@@ -17,11 +17,12 @@ enum FwdMode : int32_t {
     FWD_PARTIAL = 4,  // write the normalised partial, fp32 [B,S,Hq,d], and its lse
 };
 
-constexpr int FWD_BQ = 128;   // query rows per forward work-group (4 waves x 32)
-constexpr int FWD_BK = 64;    // keys per forward tile
+constexpr int FWD_BQ = 128;   // query rows per fp32 forward work-group (one per thread)
+constexpr int FWD_BK = 64;    // keys per forward tile (both forward kernels)
 constexpr int BWD_BQ = 64;    // query rows per backward tile
 constexpr int BWD_BK = 128;   // keys per backward work-group (4 waves x 32)
-constexpr int DQ_BQ = 256;    // query rows per dQ work-group (4 waves x 64)
+constexpr int DQ_BQ = 256;    // query rows per dQ work-group (4 waves x 64) and per
+                              // bf16 forward work-group (8 waves x 32)
 constexpr int DQ_BK = 64;     // keys per dQ tile
 constexpr int S_ALIGN = 256;  // the padded row count S_pad is a multiple of this
 

@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <cstring>
 #include <sstream>
 
 namespace ra {
@@ -27,7 +28,12 @@ int validate(const ring_attn_desc* desc, const int32_t* cu, Geometry* g, bool ch
     if (d.causal != 0 && d.causal != 1) return RA_E_ARG;
     if (d.dtype != RA_F32 && d.dtype != RA_BF16) return RA_E_UNSUPPORTED;
     if (d.merge_mode != RA_MERGE_FUSED && d.merge_mode != RA_MERGE_SEPARATE) return RA_E_ARG;
-    if (!(d.softmax_scale == d.softmax_scale)) return RA_E_ARG;  // NaN
+    {   // a NaN or infinite scale is an error (tested on the bit pattern, which
+        // no floating-point compiler option can fold away)
+        uint32_t bits;
+        std::memcpy(&bits, &d.softmax_scale, sizeof bits);
+        if ((bits & 0x7f800000u) == 0x7f800000u) return RA_E_ARG;
+    }
     if (d.window_left < -1 || d.window_right < -1) return RA_E_ARG;
     const bool varlen = d.layout == RA_VARLEN_RING || d.layout == RA_LLAMA3 ||
                         d.layout == RA_VARLEN_ZIGZAG || d.layout == RA_VARLEN_STRIPE;

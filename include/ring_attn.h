@@ -31,15 +31,20 @@
  *   - The first call for a shape builds its plan (host work, one hipMalloc
  *     and a synchronous upload); later calls for that shape enqueue kernels
  *     only (no allocation, no memset, no copy), so they can be captured into
- *     a HIP graph and replayed.
+ *     a HIP graph and replayed.  The plans live in a cache of at most
+ *     ring_attn_plan_cache_limit() plans (32 by default), least recently used
+ *     first out; every packed-layout cu_seqlens is its own shape.  Evicting a
+ *     plan (or ring_attn_clear_cache()) waits for the device and frees its
+ *     memory, which invalidates any captured graph that used it.
  *   - Return value: 0 on success, a negative RA_E_* code on failure.  All
  *     argument validation happens before any device work is enqueued, so a
  *     failing call leaves every buffer untouched.  Nothing is printed and no
  *     C++ exception crosses the ABI.  ring_attn_strerror() names each code.
  *   - Thread safety: calls may come from several threads.  The library's
  *     mutable globals are each mutex-guarded: the cache of per-shape plans
- *     (step schedule and tile lists uploaded to device memory it owns),
- *     released by ring_attn_clear_cache(); a host-side memo of dS store
+ *     (step schedule and tile lists uploaded to device memory it owns; a call
+ *     keeps its plan alive until it returns, even if another thread evicts
+ *     it or clears the cache meanwhile); a bounded host-side memo of dS store
  *     sizes; and the optional per-kernel timing state.  Calls that use the
  *     same workspace or output buffers on different streams at the same time
  *     race, as any kernels do.
@@ -107,7 +112,8 @@ typedef struct ring_attn_desc {
     int32_t causal;        /* 0 or 1: key u visible to query t iff u <= t      */
     int32_t layout;        /* ra_layout                                        */
     int32_t dtype;         /* ra_dtype                                         */
-    float softmax_scale;   /* <= 0 selects 1/sqrt(head_dim)                    */
+    float softmax_scale;   /* <= 0 selects 1/sqrt(head_dim); NaN or +-inf is
+                            * RA_E_ARG                                         */
     int32_t n_seqs;        /* number of packed documents (varlen layouts), else 0 */
     int32_t merge_mode;    /* ra_merge_mode                                    */
     int32_t window_left;   /* sliding window: key u visible to query t only if */
@@ -205,7 +211,9 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q,
  *   out' = e^(lse-lse') out + e^(lse_j-lse') out_j.
  * A partial with lse = -inf is the identity; two empty inputs stay (0, -inf).
  * out, out_j: fp32 [batch, seqlen, heads, head_dim]; lse, lse_j: fp32
- * [batch, heads, seqlen].  head_dim must be a multiple of 4. */
+ * [batch, heads, seqlen].  head_dim: any positive multiple of 4 (RA_E_SHAPE
+ * otherwise).  Each row is merged by lanes of a single wave, so rows of any
+ * length are safe to update in place. */
 int ring_attn_lse_merge(float* out, float* lse, const float* out_j, const float* lse_j,
                         int32_t batch, int64_t seqlen, int32_t heads, int32_t head_dim,
                         void* stream);
@@ -243,8 +251,18 @@ int ring_attn_tile_kinds(const ring_attn_desc* desc, const int32_t* cu_seqlens,
 int ring_attn_timing_enable(int enable);
 int ring_attn_timing_read(const char* name, int64_t* launches, double* total_ms);
 
-/* Free every cached plan (and its device memory on every device). */
+/* Free every cached plan (and its device memory on every device), waiting
+ * for the device first.  A plan that a call in flight holds is freed when
+ * that call returns. */
 int ring_attn_clear_cache(void);
+
+/* Host only.  Sets the most plans the cache keeps (>= 1; RA_E_ARG otherwise),
+ * evicting the least recently used ones beyond it; returns the previous
+ * limit. */
+int ring_attn_plan_cache_limit(int32_t max_plans);
+
+/* Host only.  Number of cached plans and the device bytes they hold. */
+int ring_attn_plan_cache_info(int64_t* n_plans, int64_t* device_bytes);
 
 const char* ring_attn_strerror(int code);
 

@@ -333,7 +333,8 @@ def rank_share_backward(q_glob, k_glob, v_glob, dout_local, layout: int, world: 
                         rank: int, causal: bool, cu_seqlens=None,
                         scale: Optional[float] = None, rows: Optional[np.ndarray] = None,
                         heads: Optional[Sequence[int]] = None,
-                        window: Tuple[int, int] = (-1, -1)):
+                        window: Tuple[int, int] = (-1, -1),
+                        key_range: Optional[Tuple[int, int]] = None):
     """Gradients of  sum(dout * out)  over the rank's rows.
 
     With P_tu = exp(scale <q_t,k_u> - lse_t) on visible pairs (0 elsewhere) and
@@ -352,6 +353,11 @@ def rank_share_backward(q_glob, k_glob, v_glob, dout_local, layout: int, world: 
     ``rows`` (local row indices) and ``heads`` optionally restrict the sum to
     those query rows and heads: dq then holds those rows in the given order
     and dk, dv hold only their contribution (used to time a bounded sample).
+    ``key_range`` = (k0, k1) runs the sums over the global keys [k0, k1) only.
+    That changes no result when none of the rows sees a key outside the range,
+    since an invisible key enters every sum with weight exactly 0; the function
+    checks this and raises otherwise.  (Dropping invisible keys only saves
+    time on long packed streams whose documents end far from the rank's rows.)
     """
     B, N, Hq, d = q_glob.shape
     Hkv = k_glob.shape[2]
@@ -363,6 +369,13 @@ def rank_share_backward(q_glob, k_glob, v_glob, dout_local, layout: int, world: 
     pos_q = pos_q[local]
     S = len(pos_q)
     pos_k = np.arange(N, dtype=np.int64)
+    if key_range is not None:
+        k0, k1 = key_range
+        for a, b in _row_chunks(S, N):
+            vis = allowed(pos_q[a:b], pos_k, causal, cu, window)
+            if vis[:, :k0].any() or vis[:, k1:].any():
+                raise ValueError("key_range drops a visible key")
+        pos_k = np.arange(k0, k1, dtype=np.int64)
     mask = allowed(pos_q, pos_k, causal, cu, window)
     nb = num_blocks(layout, world)
     blocks = [kv_positions(layout, N, world, j, cu) for j in range(nb)]
@@ -375,8 +388,8 @@ def rank_share_backward(q_glob, k_glob, v_glob, dout_local, layout: int, world: 
             # gradients of every global key of KV head hk, summed over its q heads
             dk_h = np.zeros((N, d))
             dv_h = np.zeros((N, d))
-            k = k_glob[bi, :, hk].astype(np.float64)
-            v = v_glob[bi, :, hk].astype(np.float64)
+            k = k_glob[bi, pos_k, hk].astype(np.float64)
+            v = v_glob[bi, pos_k, hk].astype(np.float64)
             for h in q_heads:
                 if kv_head_of(h, Hq, Hkv) != hk:
                     continue
@@ -388,10 +401,10 @@ def rank_share_backward(q_glob, k_glob, v_glob, dout_local, layout: int, world: 
                 p = np.where(mask & finite[:, None],
                              np.exp(np.where(mask, s, 0.0) - np.where(finite, lse, 0.0)[:, None]), 0.0)
                 delta = (do * out).sum(axis=1)
-                dv_h += p.T @ do
+                dv_h[pos_k] += p.T @ do
                 ds = p * (do @ v.T - delta[:, None])
                 dq[bi, :, h] = scale * (ds @ k)
-                dk_h += scale * (ds.T @ q)
+                dk_h[pos_k] += scale * (ds.T @ q)
             for j, pk in enumerate(blocks):
                 dk[j, bi, :, hk] = dk_h[pk]
                 dv[j, bi, :, hk] = dv_h[pk]

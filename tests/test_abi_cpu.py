@@ -154,6 +154,8 @@ def test_validation_errors_before_device_work():
         (dict(layout=ca.VARLEN_STRIPE, batch=2, cu=[0, 64]), -9),
         (dict(head_dim=96), -7), (dict(dtype=5), -7),
         (dict(window=(-2, -1)), -11), (dict(window=(3, -5)), -11),
+        (dict(softmax_scale=float("nan")), -11), (dict(softmax_scale=float("inf")), -11),
+        (dict(softmax_scale=float("-inf")), -11),
     ]
     for kw, code in cases:
         desc, cu = d(**kw)
@@ -171,6 +173,11 @@ def test_validation_errors_before_device_work():
     rc = ca.lib().ring_attn_bwd(ctypes.byref(desc), *([fake] * 6), None, fake, fake, fake, fake,
                                 1 << 30, None)
     assert rc == -7
+    # a NaN / infinite scale is refused by every entry point that reads the descriptor
+    for bad in (float("nan"), float("inf")):
+        desc, _ = d(softmax_scale=bad)
+        assert ca.lib().ring_attn_workspace_bytes(ctypes.byref(desc), 0) == -11
+        assert ca.lib().ring_attn_workspace_bytes(ctypes.byref(desc), 1) == -11
     # merge: bad head_dim
     assert ca.lib().ring_attn_lse_merge(fake, fake, fake, fake, 1, 4, 2, 6, None) == -2
 

@@ -143,9 +143,13 @@ def test_identity_v_gives_exact_zeros_where_masked():
         assert np.all(P[m] > 0.0)
 
 
-def test_lse_merge_kernel():
-    rng = np.random.default_rng(17)
-    B, S, H, d = 2, 777, 3, 128
+@pytest.mark.parametrize("d", [128, 64, 96, 4, 12, 260, 512])
+def test_lse_merge_kernel(d):
+    """Every head_dim the entry point accepts (multiples of 4), including rows
+    that do not fill a power-of-two lane group (96, 12) and rows longer than
+    one wave's 64 float4 items (260, 512)."""
+    rng = np.random.default_rng(17 + d)
+    B, S, H = 2, 777, 3
     o = rng.standard_normal((B, S, H, d)).astype(np.float32)
     oj = rng.standard_normal((B, S, H, d)).astype(np.float32)
     l = (rng.standard_normal((B, H, S)) * 5).astype(np.float32)
@@ -158,7 +162,7 @@ def test_lse_merge_kernel():
     oj[0, 5:20, 1] = 0.0
     o[1, 30:40, 2] = 0.0
     oj[1, 30:40, 2] = 0.0
-    say("lse merge")
+    say(f"lse merge d={d}")
     to = torch.from_numpy(o).cuda()
     tl = torch.from_numpy(l).cuda()
     ca.ring_attn_lse_merge(to, tl, torch.from_numpy(oj).cuda(), torch.from_numpy(lj).cuda())
@@ -459,3 +463,41 @@ def test_hip_graph_capture_and_replay():
         for name, got, want in zip(("out", "lse", "dq", "dk", "dv"), (out, lse, dq, dk, dv), ref):
             assert torch.equal(got, want), (rep, name)
     _check_fwd(w, glob, 1, out.float().cpu().numpy(), lse.cpu().numpy())
+
+
+def test_plan_cache_is_bounded():
+    """Packed training sends new document boundaries every step: 200 forward
+    calls with distinct cu_seqlens keep at most the cache limit of plans, and
+    once the cache is full the library's device memory stays the same."""
+    D, S, H, d = 4, 96, 2, 64
+    N = D * S
+    rng = np.random.default_rng(404)
+    q = torch.randn(1, S, H, d, device="cuda").to(torch.bfloat16)
+    k = torch.randn(D, 1, S, H, d, device="cuda").to(torch.bfloat16)
+    v = torch.randn(D, 1, S, H, d, device="cuda").to(torch.bfloat16)
+    ca.ring_attn_clear_cache()
+    prev = ca.ring_attn_plan_cache_limit(8)
+    try:
+        seen, used = set(), []
+        say("plan cache: 200 calls with distinct cu_seqlens")
+        while len(seen) < 200:
+            cu = tuple(synth.random_cu_seqlens(N, 5, rng, multiple=D))
+            if cu in seen:
+                continue
+            seen.add(cu)
+            desc = ca.make_desc(1, H, H, d, N, D, 1, True, ca.VARLEN_RING, cu_seqlens=cu)
+            ca.ring_attn_fwd(desc, q, k, v, cu)
+            n, nbytes = ca.ring_attn_plan_cache_info()
+            assert n == min(len(seen), 8)
+            used.append((nbytes, torch.cuda.mem_get_info()[0]))
+        torch.cuda.synchronize()
+        # plans of this shape differ only in their tile lists (a few KiB): the
+        # bytes held stay below 8 of the largest, and the device's free memory
+        # stops moving once the cache is full
+        largest = max(used[0][0], *(b - a for (a, _), (b, _) in zip(used[:7], used[1:8])))
+        assert max(b for b, _ in used) <= 8 * largest
+        free = [f for _, f in used[20:]]
+        assert max(free) - min(free) <= 4 << 20, (max(free), min(free))
+    finally:
+        ca.ring_attn_plan_cache_limit(prev)
+        ca.ring_attn_clear_cache()

@@ -51,7 +51,7 @@ def test_workload_forward(name):
     if cu is not None:  # rows at document boundaries inside the shard
         extra = tuple(int(c - pos_q[0]) + o for c in cu for o in (-1, 0, 1))
     rows = _sample_rows(S, np.random.default_rng(5), extra)
-    heads = sorted({0, w.heads_q // 2 + 1, w.heads_q - 1})
+    heads = list(range(w.heads_q))   # every q head (and so every kv head) on the sampled rows
     ref_out, ref_lse = oracle.rank_share_forward(g["q"], g["k"], g["v"], w.layout, w.world, w.rank,
                                                  w.causal, cu, rows=rows, heads=heads)
     got_out = out[:, torch.tensor(rows)].float().cpu().numpy()
@@ -77,7 +77,7 @@ def test_workload_backward_basic_s8192():
     S = w.shard
     # dq on sampled rows x heads (each row's dq depends on that row only)
     rows = _sample_rows(S, np.random.default_rng(6))
-    heads = [0, 17, 31]
+    heads = list(range(w.heads_q))
     rdq, _, _ = oracle.rank_share_backward(g["q"], g["k"], g["v"], dout_local, w.layout, w.world,
                                            w.rank, w.causal, rows=rows, heads=heads)
     got_dq = dq[:, torch.tensor(rows)].cpu().numpy()
@@ -97,16 +97,36 @@ def test_workload_backward_basic_s8192():
     got_dv = dv[..., hk, :].cpu().numpy()
     assert np.abs(got_dk - rdk).max() <= 5e-2 * np.abs(rdk).max()
     assert np.abs(got_dv - rdv).max() <= 5e-2 * np.abs(rdv).max()
-    # blocks this rank never sees stay untouched (causal basic: none here, rank 7)
     assert torch.isfinite(dk).all().item() and torch.isfinite(dv).all().item()
+    _check_dv_sums(w, dout_local, dk, dv)
+
+
+def _check_dv_sums(w, dout_local, dk, dv):
+    """Properties of the complete dK/dV that hold at any size, per kv head:
+    the softmax rows sum to one, so the dV rows of a kv head, summed over
+    every block and key, equal the dout rows of its q heads summed over the
+    rank's rows; and dS = P (dP - Delta) sums to zero over the keys of a row,
+    so the dK rows of a kv head sum to zero.  A kv-head (GQA group) indexing
+    error in the dK/dV kernels or in the dS store breaks the first."""
+    group = w.heads_q // w.heads_kv
+    dv64 = dv.double().sum(dim=(0, 2)).cpu().numpy()          # [B, Hkv, d]
+    dk_sum = dk.double().sum(dim=(0, 2)).cpu().numpy()
+    dk_abs = dk.double().abs().sum(dim=(0, 2)).cpu().numpy()
+    do = dout_local.astype(np.float64).reshape(w.batch, -1, w.heads_kv, group, w.head_dim)
+    ref = do.sum(axis=(1, 3))                                 # [B, Hkv, d]
+    assert np.abs(dv64 - ref).max() <= 2e-2 * np.abs(ref).max(), np.abs(dv64 - ref).max()
+    assert np.all(np.abs(dk_sum) <= 1e-2 * dk_abs + 1e-3)
 
 
 @pytest.mark.parametrize("name", ["zigzag", "llama3"])
-def test_workload_backward_dq_sampled(name):
+def test_workload_backward_full_size(name):
     """The backward at the zigzag (GQA 32/8, 16384-row shard) and llama3
     (packed, one step over the gathered 65536 keys) sizes, through the stored-dS
-    path the bench uses: dq on sampled rows x heads (each row's dq depends on
-    that row alone); dk, dv finite."""
+    path the bench uses: dq of every q head on sampled rows (each row's dq
+    depends on that row alone); the dV/dK sums over keys of every kv head; and
+    for llama3 the complete dK/dV of one kv head (its 4 q heads, every query row
+    of the rank), with the oracle's sums restricted to the keys the rank's
+    documents hold."""
     w = synth.WORKLOADS[name].replace(with_grad=True)
     say(f"workload bwd {name}")
     g, desc, cu, pos_q, dev = _inputs(w)
@@ -116,12 +136,33 @@ def test_workload_backward_dq_sampled(name):
     dq, dk, dv = ca.ring_attn_bwd(desc, dev["dout"], dev["q"], dev["k"], dev["v"], out, lse, cu,
                                   workspace=ws)
     torch.cuda.synchronize()
+    assert torch.isfinite(dk).all().item() and torch.isfinite(dv).all().item()
+    dout_local = g["dout"][:, pos_q]
     rows = _sample_rows(w.shard, np.random.default_rng(8))
-    heads = [0, 13, 31]
-    rdq, _, _ = oracle.rank_share_backward(g["q"], g["k"], g["v"], g["dout"][:, pos_q], w.layout,
+    heads = list(range(w.heads_q))
+    rdq, _, _ = oracle.rank_share_backward(g["q"], g["k"], g["v"], dout_local, w.layout,
                                            w.world, w.rank, w.causal, cu, rows=rows, heads=heads)
     got = dq[:, torch.tensor(rows)].cpu().numpy()
     for h in heads:
         ref = rdq[:, :, h]
         assert np.abs(got[:, :, h] - ref).max() <= 5e-2 * np.abs(ref).max(), h
-    assert torch.isfinite(dk).all().item() and torch.isfinite(dv).all().item()
+    _check_dv_sums(w, dout_local, dk, dv)
+    if w.layout == ca.LLAMA3:
+        # keys the rank's rows can see: from the start of the first document
+        # that overlaps the shard to the shard's end
+        k0 = max(c for c in cu if c <= pos_q[0])
+        k1 = int(pos_q[-1]) + 1
+        hk = 5
+        group = w.heads_q // w.heads_kv
+        rdk = rdv = None
+        for a in range(0, w.shard, 2048):
+            _, ck, cv = oracle.rank_share_backward(
+                g["q"], g["k"], g["v"], dout_local, w.layout, w.world, w.rank, w.causal, cu,
+                rows=np.arange(a, min(w.shard, a + 2048)),
+                heads=list(range(hk * group, (hk + 1) * group)), key_range=(k0, k1))
+            rdk = ck[..., hk, :] if rdk is None else rdk + ck[..., hk, :]
+            rdv = cv[..., hk, :] if rdv is None else rdv + cv[..., hk, :]
+        got_dk = dk[..., hk, :].cpu().numpy()
+        got_dv = dv[..., hk, :].cpu().numpy()
+        assert np.abs(got_dk - rdk).max() <= 5e-2 * np.abs(rdk).max()
+        assert np.abs(got_dv - rdv).max() <= 5e-2 * np.abs(rdv).max()

@@ -707,3 +707,22 @@ def test_bf16_rounding_is_nearest_even():
     assert np.array_equal(q, ref)
     r = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 10
     assert np.array_equal(synth.quantize_bf16(r), torch.tensor(r).to(torch.bfloat16).float().numpy())
+
+
+def test_backward_key_range_is_exact_and_guarded():
+    """Restricting the backward's sums to a key range that holds every visible
+    key changes nothing (invisible keys carry weight 0); a range that drops a
+    visible key is refused."""
+    rng = np.random.default_rng(77)
+    N, D, r = 96, 4, 2
+    cu = [0, 10, 40, 70, 96]
+    q, k, v = _inputs(rng, 1, N, 4, 2, 8)
+    S = N // D
+    dout = rng.standard_normal((1, S, 4, 8))
+    full = oracle.rank_share_backward(q, k, v, dout, LLAMA3, D, r, True, cu)
+    # rank 2 holds [48, 72): documents [40, 70) and [70, 96) -> keys [40, 72)
+    part = oracle.rank_share_backward(q, k, v, dout, LLAMA3, D, r, True, cu, key_range=(40, 72))
+    for a, b in zip(full, part):
+        assert np.abs(a - b).max() < 1e-12
+    with pytest.raises(ValueError):
+        oracle.rank_share_backward(q, k, v, dout, LLAMA3, D, r, True, cu, key_range=(41, 72))
