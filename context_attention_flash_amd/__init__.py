@@ -20,7 +20,7 @@ from .synth import BASIC, ZIGZAG, STRIPE, VARLEN_RING, LLAMA3, VARLEN_ZIGZAG, VA
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libringattn.so")
 
 RA_F32, RA_BF16 = 0, 1
-RA_MERGE_FUSED, RA_MERGE_SEPARATE = 0, 1
+RA_MERGE_FUSED, RA_MERGE_SEPARATE, RA_MERGE_STEPWISE = 0, 1, 2
 
 ERRORS = {
     -1: "RA_E_NULL", -2: "RA_E_SHAPE", -3: "RA_E_WORLD", -4: "RA_E_DIVISIBILITY",

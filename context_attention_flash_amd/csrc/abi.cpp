@@ -59,6 +59,17 @@ struct Plan {
     int32_t nkt_b = 0;  // backward key tiles
     int32_t nqt_dq = 0; // dQ query tiles
     int32_t max_ne = 0; // largest b_ne over the steps
+    // One-launch forward over every active step (bf16): per 256-row query
+    // tile, the 64-key tiles of all steps (unmasked ones first), entries
+    // key tile | step << RING_STEP_SHIFT | partial << 31; the per-row
+    // intervals of every step back to back; the KV block of every step.
+    bool ring_ok = false;
+    const int32_t* ring_off = nullptr;
+    const int32_t* ring_mid = nullptr;
+    const int32_t* ring_ent = nullptr;
+    const int32_t* ring_order = nullptr;
+    const int32_t* rng_all = nullptr;
+    const int32_t* blk = nullptr;
     void* dbuf = nullptr;
     std::vector<DevStep> steps;
     ~Plan() {
@@ -158,6 +169,13 @@ void build_ds_lists(const std::vector<int32_t>& boff, const std::vector<int32_t>
     });
 }
 
+// Whether the bf16 forward runs as one launch over every ring step: the
+// entries hold the key tile in 20 bits and the step in 11.
+bool ring_capable(const Geometry& g) {
+    return g.dtype == RA_BF16 && g.nb <= RING_MAX_STEPS &&
+           (g.Skv + DQ_BK - 1) / DQ_BK <= RING_MAX_KEY_TILES;
+}
+
 int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
     auto plan = std::make_unique<Plan>();
     plan->device = device;
@@ -173,6 +191,10 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
                  doff, dent, dord; };
     std::vector<Idx> idx;
     std::vector<StepRanges> all(g.nb);
+    // per active step: the forward lists of 256-row query tiles over 64-key
+    // tiles (kept for the one-launch lists) and the per-row intervals
+    std::vector<std::vector<int32_t>> q_off_h, q_mid_h, q_ent_h;
+    std::vector<int32_t> rng_all_h, blk_h;
     int64_t total_pairs = 0;
     for (int32_t s = 0; s < g.nb; ++s) {
         step_ranges(g, s, all[s]);
@@ -195,6 +217,8 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
             rng[2 * i + 1] = sr.b[i];
         }
         Idx ix;
+        rng_all_h.insert(rng_all_h.end(), rng.begin(), rng.end());
+        blk_h.push_back(sr.j);
         ix.rng = H.add(std::move(rng));
         std::vector<int32_t> off, mid, ent, order;
         classify(sr, g.S, g.Skv, FWD_BQ, FWD_BK, kinds);
@@ -220,12 +244,50 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
         ix.bord = H.add(std::move(order));
         classify(sr, g.S, g.Skv, DQ_BQ, DQ_BK, kinds);
         build_lists(kinds, plan->nqt_dq, (g.Skv + DQ_BK - 1) / DQ_BK, true, off, mid, ent, order);
+        q_off_h.push_back(off);
+        q_mid_h.push_back(mid);
+        q_ent_h.push_back(ent);
         ix.qoff = H.add(std::move(off));
         ix.qmid = H.add(std::move(mid));
         ix.qent = H.add(std::move(ent));
         ix.qord = H.add(std::move(order));
         plan->steps.push_back(ds);
         idx.push_back(ix);
+    }
+    // The one-launch forward lists: for each query tile, the unmasked entries
+    // of every step in ring order, then the masked ones.
+    size_t i_roff = 0, i_rmid = 0, i_rent = 0, i_rord = 0, i_rng_all = 0, i_blk = 0;
+    const int64_t n_active = (int64_t)plan->steps.size();
+    plan->ring_ok = ring_capable(g) && n_active <= RING_MAX_STEPS;
+    if (plan->ring_ok) {
+        const int64_t nq = plan->nqt_dq;
+        std::vector<int32_t> roff(nq + 1, 0), rmid(nq, 0), rent, rord(nq);
+        for (int64_t q = 0; q < nq; ++q) {
+            for (int pass = 0; pass < 2; ++pass) {
+                if (pass == 1) rmid[q] = (int32_t)rent.size();
+                for (int64_t st = 0; st < n_active; ++st) {
+                    const auto& off = q_off_h[st];
+                    const int32_t a = pass == 0 ? off[q] : q_mid_h[st][q];
+                    const int32_t b = pass == 0 ? q_mid_h[st][q] : off[q + 1];
+                    for (int32_t e = a; e < b; ++e) {
+                        const int32_t kt = q_ent_h[st][e] & 0x7fffffff;
+                        rent.push_back(kt | (int32_t)(st << RING_STEP_SHIFT) |
+                                       (pass == 1 ? (int32_t)0x80000000u : 0));
+                    }
+                }
+            }
+            roff[q + 1] = (int32_t)rent.size();
+        }
+        std::iota(rord.begin(), rord.end(), 0);
+        std::stable_sort(rord.begin(), rord.end(), [&](int32_t x, int32_t y) {
+            return roff[x + 1] - roff[x] > roff[y + 1] - roff[y];
+        });
+        i_roff = H.add(std::move(roff));
+        i_rmid = H.add(std::move(rmid));
+        i_rent = H.add(std::move(rent));
+        i_rord = H.add(std::move(rord));
+        i_rng_all = H.add(std::move(rng_all_h));
+        i_blk = H.add(std::move(blk_h));
     }
     // One device allocation holding every array, each 256-byte aligned.
     std::vector<size_t> offs(H.arrays.size());
@@ -264,6 +326,14 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
         d.d_off = P(idx[k].doff);
         d.d_ent = P(idx[k].dent);
         d.d_order = P(idx[k].dord);
+    }
+    if (plan->ring_ok) {
+        plan->ring_off = P(i_roff);
+        plan->ring_mid = P(i_rmid);
+        plan->ring_ent = P(i_rent);
+        plan->ring_order = P(i_rord);
+        plan->rng_all = P(i_rng_all);
+        plan->blk = P(i_blk);
     }
     out = std::move(plan);
     return RA_OK;
@@ -368,7 +438,9 @@ int64_t elem_bytes(const Geometry& g) { return g.dtype == RA_BF16 ? 2 : 4; }
 
 int64_t fwd_workspace(const Geometry& g) {
     const int64_t S_pad = round_up(g.S, S_ALIGN);
-    if (g.merge_mode == RA_MERGE_FUSED) return round_up((int64_t)g.B * g.Hq * S_pad * g.d * 4, 256);
+    // the one-launch forward keeps the running result in registers
+    if (g.merge_mode == RA_MERGE_FUSED && ring_capable(g)) return 0;
+    if (g.merge_mode != RA_MERGE_SEPARATE) return round_up((int64_t)g.B * g.Hq * S_pad * g.d * 4, 256);
     const int64_t o = round_up((int64_t)g.B * g.S * g.Hq * g.d * 4, 256);
     return 2 * o + round_up((int64_t)g.B * g.Hq * g.S * 4, 256);
 }
@@ -571,7 +643,7 @@ int ring_attn_fwd(const ring_attn_desc* desc, const void* q, const void* k, cons
         if ((rc = check_support(g, false)) != RA_OK) return rc;
         if (!q || !k || !v || !out || !lse) return RA_E_NULL;
         const int64_t need = fwd_workspace(g);
-        if (!workspace || (int64_t)workspace_bytes < need) return RA_E_WORKSPACE;
+        if (need > 0 && (!workspace || (int64_t)workspace_bytes < need)) return RA_E_WORKSPACE;
         std::shared_ptr<const Plan> plan;
         if ((rc = get_plan(g, &plan)) != RA_OK) return rc;
         hipStream_t s = (hipStream_t)stream;
@@ -603,7 +675,23 @@ int ring_attn_fwd(const ring_attn_desc* desc, const void* q, const void* k, cons
             });
         };
         const size_t n = plan->steps.size();
-        if (g.merge_mode == RA_MERGE_FUSED) {
+        if (g.merge_mode == RA_MERGE_FUSED && plan->ring_ok) {
+            // one launch over every active step, the merge carried in registers
+            a.ring = 1;
+            a.k = k;
+            a.v = v;
+            a.block_elems = block_elems;
+            a.rng = plan->rng_all;
+            a.rng_stride = (int32_t)(2 * plan->S_pad);
+            a.blk = plan->blk;
+            a.t_off = plan->ring_off;
+            a.t_mid = plan->ring_mid;
+            a.t_ent = plan->ring_ent;
+            a.t_order = plan->ring_order;
+            a.mode = FWD_SOLO;
+            return hip_rc(launch_step(a));
+        }
+        if (g.merge_mode != RA_MERGE_SEPARATE) {   // one launch per step, merge in the epilogue
             a.o_run = (float*)workspace;
             for (size_t i = 0; i < n; ++i) {
                 const DevStep& st = plan->steps[i];

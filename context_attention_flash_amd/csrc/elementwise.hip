@@ -15,12 +15,13 @@
 namespace ra {
 
 // Rows are owned by waves: a row of c4 = d/4 float4 items is handled by a
-// group of G lanes of ONE wave (G = the smallest power of two >= c4, at most
-// 64; lane c of the group takes items c, c + G, ...), so the lanes that read a
-// row's running lse and the lane that writes the merged one belong to the same
-// wave, whose store cannot issue before its own loads have returned.  Each
-// wave walks MERGE_ITEMS groups of 64/G rows, loading all of them before
-// using any, to keep enough bytes in flight.
+// group of G = 2^lg lanes of ONE wave (G = the smallest power of two >= c4,
+// at most 64; lane c of the group takes items c, c + G, ...), so the lanes that
+// read a row's running lse and the lane that writes the merged one belong to
+// the same wave, whose store cannot issue before its own loads have returned.
+// Each wave walks MERGE_ITEMS groups of 64/G rows; every item's loads are
+// issued (from clamped, always valid addresses) before any item is used, to
+// keep enough bytes in flight, and only the stores are predicated.
 constexpr int MERGE_ITEMS = 4;
 
 __global__ __launch_bounds__(256) void lse_merge_kernel(float* __restrict__ out,
@@ -28,50 +29,50 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(float* __restrict__ out,
                                                         const float* __restrict__ oj,
                                                         const float* __restrict__ lj,
                                                         int64_t n_rows, int64_t S, int32_t H,
-                                                        int32_t c4, int32_t G) {
+                                                        int32_t c4, int32_t lg) {
     const int lane = threadIdx.x & 63;
-    const int rg = 64 / G;                           // rows per wave pass
-    const int c0 = lane % G;
+    const int c0 = lane & ((1 << lg) - 1), rsub = lane >> lg, rg = 64 >> lg;
     const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    for (int cb = 0; cb < c4; cb += G) {             // one pass unless d > 256
-        const int c = cb + c0;
+    for (int cb = 0; cb < c4; cb += 1 << lg) {       // one pass unless d > 256
+        const int c = cb + c0, cc = min(c, c4 - 1);
         f32x4_t o[MERGE_ITEMS], x[MERGE_ITEMS];
         float L[MERGE_ITEMS], Lj[MERGE_ITEMS];
         int64_t li[MERGE_ITEMS], item[MERGE_ITEMS];
         bool live[MERGE_ITEMS];
 #pragma unroll
         for (int it = 0; it < MERGE_ITEMS; ++it) {
-            const int64_t row = (wave * MERGE_ITEMS + it) * rg + lane / G;   // (b, s, h)
+            const int64_t row = (wave * MERGE_ITEMS + it) * rg + rsub;   // (b, s, h)
             live[it] = row < n_rows && c < c4;
-            if (live[it]) {
-                const int64_t h = row % H, bs = row / H;
-                const int64_t b = bs / S, s = bs % S;
-                li[it] = (b * H + h) * S + s;
-                item[it] = row * c4 + c;
-                o[it] = __builtin_nontemporal_load((const f32x4_t*)out + item[it]);
-                x[it] = __builtin_nontemporal_load((const f32x4_t*)oj + item[it]);
-                L[it] = lse[li[it]];
-                Lj[it] = lj[li[it]];
-            }
+            const int64_t rw = min(row, n_rows - 1);
+            const int64_t h = rw % H, bs = rw / H;
+            const int64_t b = bs / S, s = bs % S;
+            li[it] = (b * H + h) * S + s;
+            item[it] = rw * c4 + cc;
         }
+        // all loads of the pass in one group, ahead of every use
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int it = 0; it < MERGE_ITEMS; ++it) {
-            if (!live[it]) continue;
+            o[it] = __builtin_nontemporal_load((const f32x4_t*)out + item[it]);
+            x[it] = __builtin_nontemporal_load((const f32x4_t*)oj + item[it]);
+            L[it] = lse[li[it]];
+            Lj[it] = lj[li[it]];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int it = 0; it < MERGE_ITEMS; ++it) {
             const float M = fmaxf(L[it], Lj[it]);
-            f32x4_t r;
-            float Ln;
-            if (M == -INFINITY) {
-                r = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-                Ln = -INFINITY;
-            } else {
-                const float a = expf(L[it] - M), e = expf(Lj[it] - M), den = a + e;
-                Ln = M + logf(den);
-                const float wa = a / den, we = e / den;
-                r = wa * o[it] + we * x[it];
+            const bool empty = M == -INFINITY;
+            const float Ms = empty ? 0.f : M;
+            const float a = expf(L[it] - Ms), e = expf(Lj[it] - Ms), den = a + e;
+            const float Ln = empty ? -INFINITY : Ms + logf(den);
+            const float wa = empty ? 0.f : a / den, we = empty ? 0.f : e / den;
+            const f32x4_t r = wa * o[it] + we * x[it];
+            if (live[it]) {
+                __builtin_nontemporal_store(r, (f32x4_t*)out + item[it]);
+                // lane 0 of the group writes the merged lse in the row's last pass
+                if (c0 == 0 && cb + (1 << lg) >= c4) lse[li[it]] = Ln;
             }
-            __builtin_nontemporal_store(r, (f32x4_t*)out + item[it]);
-            // lane 0 of the group writes the merged lse in the row's last pass
-            if (c0 == 0 && cb + G >= c4) lse[li[it]] = Ln;
         }
     }
 }
@@ -81,12 +82,12 @@ hipError_t launch_lse_merge(float* out, float* lse, const float* out_j, const fl
     const int64_t n_rows = (int64_t)B * S * H;
     const int c4 = d / 4;
     if (n_rows == 0 || c4 == 0) return hipSuccess;
-    int G = 1;
-    while (G < c4 && G < 64) G *= 2;
-    const int64_t rows_per_block = 4LL * MERGE_ITEMS * (64 / G);
+    int lg = 0;
+    while ((1 << lg) < c4 && lg < 6) ++lg;
+    const int64_t rows_per_block = 4LL * MERGE_ITEMS * (64 >> lg);
     const int64_t grid = (n_rows + rows_per_block - 1) / rows_per_block;
     hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)grid), dim3(256), 0, s, out, lse, out_j,
-                       lse_j, n_rows, S, H, c4, G);
+                       lse_j, n_rows, S, H, c4, lg);
     return hipGetLastError();
 }
 

@@ -58,7 +58,15 @@ __device__ __forceinline__ u32x2_t fwd_tr16(const unsigned char* p) {
     return __builtin_bit_cast(u32x2_t, r);
 }
 
-template <int DH>
+// RING = false: one launch per ring step, over the step's tile lists, with the
+// step epilogue of p.mode.  RING = true: one launch over every active step of
+// the rank's share (FWD_SOLO): each query tile's list holds the key tiles of
+// all steps (those that need no mask first), each entry naming its step, so
+// the running max, sum and output stay in registers from one ring step to the
+// next; carrying the unnormalised partial with its running max and sum across
+// the steps is the log-sum-exp merge of the normalised partials, done in
+// registers (the "online softmax across ring steps" of the ai360xpert page).
+template <int DH, bool RING>
 __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
     using C = FwdCfg<DH>;
     // K and V stages as separate objects, each access naming its stage
@@ -88,14 +96,24 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
     u32x4_t qreg[C::NKS];
 #pragma unroll
     for (int ks = 0; ks < C::NKS; ++ks) qreg[ks] = *(const u32x4_t*)(qrow + 16 * ks + 8 * g);
-    const int ra = p.rng[2 * iq], rb = p.rng[2 * iq + 1];
+    // the visible key interval [ra, rb) of this lane's row (per ring step when RING)
+    int ra = 0, rb = 0;
+    if (!RING) {
+        ra = p.rng[2 * iq];
+        rb = p.rng[2 * iq + 1];
+    }
 
     BufTileLoader<DH, C::BK, C::NT> lk, lv;   // K and V tiles of 64 keys
-    {
-        const int64_t batch = (int64_t)b * p.Skv * p.Hkv * DH;
-        lk.init((const uint16_t*)p.k + batch, p.Skv, p.Hkv, hk, wave, lane);
-        lv.init((const uint16_t*)p.v + batch, p.Skv, p.Hkv, hk, wave, lane);
-    }
+    const int64_t kv_batch = (int64_t)b * p.Skv * p.Hkv * DH;
+    lk.init((const uint16_t*)p.k + kv_batch, p.Skv, p.Hkv, hk, wave, lane);
+    lv.init((const uint16_t*)p.v + kv_batch, p.Skv, p.Hkv, hk, wave, lane);
+    // RING: the K/V buffers of the block of a plan step
+    auto k_rsrc = [&](int jb) {
+        return lk.rsrc_of((const uint16_t*)p.k + kv_batch + jb * p.block_elems, p.Skv, p.Hkv);
+    };
+    auto v_rsrc = [&](int jb) {
+        return lv.rsrc_of((const uint16_t*)p.v + kv_batch + jb * p.block_elems, p.Skv, p.Hkv);
+    };
 
     // per-lane LDS offsets: natural K reads of row l32 (+32 mt), chunk 2ks+g;
     // transpose reads of V rows {4g, 8+4g} + j/4 (+16 kk), head-dim block dt.
@@ -211,32 +229,68 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
         }
     };
 
-    // Key-tile indices of tiles i, i+1 and i+2 (0 past the list), the last
-    // one fetched an iteration ahead.
-    auto ent_at = [&](int i) { return i < n ? ents[e0 + i] & 0x7fffffff : 0; };
-    int kt0 = ent_at(0), kt1 = ent_at(1), kt2 = ent_at(2);
+    // Entries of tiles i, i+1 and i+2 (0 past the list), the last one fetched
+    // an iteration ahead; key tile, plan step and KV block of each.
+    constexpr int KT_MASK = RING ? (1 << RING_STEP_SHIFT) - 1 : 0x7fffffff;
+    auto raw_at = [&](int i) { return i < n ? ents[e0 + i] : 0; };
+    auto step_of = [&](int e) { return RING ? (e >> RING_STEP_SHIFT) & (RING_MAX_STEPS - 1) : 0; };
+    auto blk_of = [&](int e) { return RING ? as_const(p.blk)[step_of(e)] : 0; };
+    int en0 = raw_at(0), en1 = raw_at(1), en2 = raw_at(2);
+    int jb1 = blk_of(en1), jb2 = blk_of(en2);
+    // RING: the interval of the lane's row in the next tile's step, loaded a
+    // tile ahead when that tile needs the mask; a tile that needs none (the
+    // odd last one of the unmasked tiles runs in the masked loop) keeps every key
+    int2 rng_nx = {0, 0x7fffffff};
+    auto fetch_rng = [&](int e) {
+        if (!RING) return;
+        if (e < 0)
+            rng_nx = *(const int2*)(p.rng + (int64_t)step_of(e) * p.rng_stride + 2 * iq);
+        else
+            rng_nx = {0, 0x7fffffff};
+    };
 
     // iteration i: refill, S(i+1) on the matrix cores with softmax(i), P V of
     // tile i.  S(i+1) of the last tile reads a stale stage and is discarded.
     auto body = [&](int i, f32x16_t (&cur)[2], f32x16_t (&nxt)[2], const unsigned char* Kn,
                     unsigned char* Kl, const unsigned char* Vc, unsigned char* Vl,
                     auto partial_tag) {
+        constexpr bool PARTIAL = decltype(partial_tag)::value;
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into LDS have landed
         __syncthreads();  // K(i+1) and V(i) are in LDS; the stages refilled below are free
-        if (i + 2 < n) lk.load(Kl, kt2, wave);
-        if (i + 1 < n) lv.load(Vl, kt1, wave);
-        const int kt = kt0;
-        kt0 = kt1;
-        kt1 = kt2;
-        kt2 = ent_at(i + 3);
+        if (RING && PARTIAL) {
+            ra = rng_nx.x;
+            rb = rng_nx.y;
+        }
+        if (RING) {
+            if (i + 2 < n) lk.load_from(Kl, k_rsrc(jb2), en2 & KT_MASK, wave);
+            if (i + 1 < n) lv.load_from(Vl, v_rsrc(jb1), en1 & KT_MASK, wave);
+            fetch_rng(en1);
+        } else {
+            if (i + 2 < n) lk.load(Kl, en2 & KT_MASK, wave);
+            if (i + 1 < n) lv.load(Vl, en1 & KT_MASK, wave);
+        }
+        const int kt = en0 & KT_MASK;
+        en0 = en1;
+        en1 = en2;
+        jb1 = jb2;
+        en2 = raw_at(i + 3);
+        if (RING) jb2 = blk_of(en2);
         s_tile(nxt, Kn);
         pv_tile(cur, kt, Vc, partial_tag);
     };
 
     if (n > 0) {
-        lk.load(KA, kt0, wave);
-        lv.load(VA, kt0, wave);
-        if (n > 1) lk.load(KB, kt1, wave);
+        if (RING) {
+            const int jb0 = blk_of(en0);
+            lk.load_from(KA, k_rsrc(jb0), en0 & KT_MASK, wave);
+            lv.load_from(VA, v_rsrc(jb0), en0 & KT_MASK, wave);
+            if (n > 1) lk.load_from(KB, k_rsrc(jb1), en1 & KT_MASK, wave);
+            fetch_rng(en0);
+        } else {
+            lk.load(KA, en0 & KT_MASK, wave);
+            lv.load(VA, en0 & KT_MASK, wave);
+            if (n > 1) lk.load(KB, en1 & KT_MASK, wave);
+        }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         f32x16_t sa[2], sb[2];
@@ -342,12 +396,22 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
     }
 }
 
+template __global__ void fwd_step_bf16_kernel<128, false>(FwdArgs);
+template __global__ void fwd_step_bf16_kernel<128, true>(FwdArgs);
+template __global__ void fwd_step_bf16_kernel<64, false>(FwdArgs);
+template __global__ void fwd_step_bf16_kernel<64, true>(FwdArgs);
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, hipStream_t s) {
     const int grid = (a.total_work + 7) / 8 * 8;
-    if (head_dim == 128)
-        hipLaunchKernelGGL(fwd_step_bf16_kernel<128>, dim3(grid), dim3(512), 0, s, a);
+    if (grid == 0) return hipSuccess;
+    if (head_dim == 128 && a.ring)
+        hipLaunchKernelGGL((fwd_step_bf16_kernel<128, true>), dim3(grid), dim3(512), 0, s, a);
+    else if (head_dim == 128)
+        hipLaunchKernelGGL((fwd_step_bf16_kernel<128, false>), dim3(grid), dim3(512), 0, s, a);
+    else if (head_dim == 64 && a.ring)
+        hipLaunchKernelGGL((fwd_step_bf16_kernel<64, true>), dim3(grid), dim3(512), 0, s, a);
     else if (head_dim == 64)
-        hipLaunchKernelGGL(fwd_step_bf16_kernel<64>, dim3(grid), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((fwd_step_bf16_kernel<64, false>), dim3(grid), dim3(512), 0, s, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

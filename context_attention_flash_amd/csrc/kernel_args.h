@@ -25,6 +25,10 @@ constexpr int DQ_BQ = 256;    // query rows per dQ work-group (4 waves x 64) and
                               // bf16 forward work-group (8 waves x 32)
 constexpr int DQ_BK = 64;     // keys per dQ tile
 constexpr int S_ALIGN = 256;  // the padded row count S_pad is a multiple of this
+// Entries of the one-launch forward: bits 0-19 key tile, 20-30 plan step, 31 partial.
+constexpr int RING_STEP_SHIFT = 20;
+constexpr int RING_MAX_STEPS = 1 << 11;
+constexpr int RING_MAX_KEY_TILES = 1 << 20;
 
 struct FwdArgs {
     const void* q;          // [B, S, Hq, d]
@@ -35,6 +39,14 @@ struct FwdArgs {
     const int32_t* t_mid;   // [nqt] first PARTIAL entry of each list (FULL ones before it)
     const int32_t* t_ent;   // key tile index | (partial << 31)
     const int32_t* t_order; // [nqt] query tiles, heaviest first
+    // One launch over every ring step (bf16 kernel, FWD_SOLO): entries are
+    // key tile | plan step << RING_STEP_SHIFT | partial << 31, the per-row
+    // intervals of plan step p start at rng + p * rng_stride, and blk[p] is the
+    // KV block of plan step p (k and v then point at block 0).
+    const int32_t* blk;
+    int64_t block_elems;    // elements of one KV block [B, Skv, Hkv, d]
+    int32_t rng_stride;     // ints between the interval arrays of two plan steps
+    int32_t ring;           // 1: the entries span the ring steps as above
     float* o_run;           // running fp32 output (layout private to the kernel family)
     float* lse;             // [B, Hq, S] running / final lse
     void* out;              // [B, S, Hq, d] final output (input dtype)

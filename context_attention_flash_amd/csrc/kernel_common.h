@@ -109,12 +109,23 @@ struct BufTileLoader {
     }
     // tile `t` (rows ROWS*t ..) of head `head` (default: the head of init)
     __device__ __forceinline__ void load(unsigned char* lds, int t, int wave, int head = -1) const {
+        load_from(lds, rsrc, t, wave, head);
+    }
+    // the same tile of another buffer of the same shape (e.g. another KV block)
+    __device__ __forceinline__ void load_from(unsigned char* lds, __amdgpu_buffer_rsrc_t r, int t,
+                                              int wave, int head = -1) const {
         const int soff = t * tile_bytes + (head < 0 ? head_off : head * DH * 2);
 #pragma unroll
         for (int c = 0; c < NLD; ++c)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, (__attribute__((address_space(3))) void*)(lds + (NT * c + 64 * wave) * 16), 16,
+                r, (__attribute__((address_space(3))) void*)(lds + (NT * c + 64 * wave) * 16), 16,
                 voff[c], soff, 0, 0);
+    }
+    // buffer over the nrows rows of another tensor laid out like the first
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const uint16_t* base, int nrows,
+                                                              int heads) const {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrows * heads * DH * 2,
+                                                 0x00020000);
     }
 };
 

@@ -27,7 +27,9 @@ int validate(const ring_attn_desc* desc, const int32_t* cu, Geometry* g, bool ch
     if (d.layout < RA_BASIC || d.layout > RA_VARLEN_STRIPE) return RA_E_LAYOUT;
     if (d.causal != 0 && d.causal != 1) return RA_E_ARG;
     if (d.dtype != RA_F32 && d.dtype != RA_BF16) return RA_E_UNSUPPORTED;
-    if (d.merge_mode != RA_MERGE_FUSED && d.merge_mode != RA_MERGE_SEPARATE) return RA_E_ARG;
+    if (d.merge_mode != RA_MERGE_FUSED && d.merge_mode != RA_MERGE_SEPARATE &&
+        d.merge_mode != RA_MERGE_STEPWISE)
+        return RA_E_ARG;
     {   // a NaN or infinite scale is an error (tested on the bit pattern, which
         // no floating-point compiler option can fold away)
         uint32_t bits;

@@ -93,13 +93,22 @@ typedef enum {
 /* Element type of q, k, v, out and dout.  Accumulation is always fp32. */
 typedef enum { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
 
-/* How the forward folds the per-step partials.
- *   RA_MERGE_FUSED      each step's kernel merges its partial into the running
- *                       fp32 result in its epilogue; the last step writes out.
+/* How the forward folds the per-step partials ("Numerically-Stable Output
+ * Fusion"; "Online softmax across ring steps").
+ *   RA_MERGE_FUSED      bf16: ONE kernel launch walks every active ring step
+ *                       of each query tile and folds each step's partial into
+ *                       the running result in registers (running max, sum and
+ *                       unnormalised output: the log-sum-exp merge without a
+ *                       round trip through memory); no workspace.  fp32 inputs
+ *                       (or more than 2048 steps, or more than 2^20 64-key
+ *                       tiles per block) use RA_MERGE_STEPWISE instead.
  *   RA_MERGE_SEPARATE   each step's kernel writes its partial (out_j, lse_j);
  *                       the standalone merge kernel (ring_attn_lse_merge)
- *                       folds it in; a final kernel casts the result. */
-typedef enum { RA_MERGE_FUSED = 0, RA_MERGE_SEPARATE = 1 } ra_merge_mode;
+ *                       folds it in; a final kernel casts the result.
+ *   RA_MERGE_STEPWISE   one launch per step; each merges its partial into the
+ *                       running fp32 result in its epilogue and the last one
+ *                       writes out. */
+typedef enum { RA_MERGE_FUSED = 0, RA_MERGE_SEPARATE = 1, RA_MERGE_STEPWISE = 2 } ra_merge_mode;
 
 typedef struct ring_attn_desc {
     int32_t batch;         /* B (must be 1 for the packed layouts)   */
@@ -157,8 +166,9 @@ typedef struct ring_attn_desc {
 
 /* Bytes of device workspace ring_attn_fwd (is_bwd = 0) or ring_attn_bwd
  * (is_bwd = 1) needs for this descriptor; negative RA_E_* if the descriptor is
- * invalid (cu_seqlens is not inspected).  Forward: the fp32 running output
- * (plus one partial in RA_MERGE_SEPARATE mode).  Backward: two per-row fp32
+ * invalid (cu_seqlens is not inspected).  Forward: 0 for the one-launch
+ * RA_MERGE_FUSED path, else the fp32 running output (plus one partial in
+ * RA_MERGE_SEPARATE mode).  Backward: two per-row fp32
  * arrays of B * Hq * S_pad floats (the lse in base 2 and -Delta, Delta =
  * rowsum(dout * out)) and an fp32 dQ accumulator of B * Hq * S_pad * d floats
  * (S_pad = S rounded up to 256; each part starts on a 256-byte boundary). */

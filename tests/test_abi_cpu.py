@@ -163,6 +163,9 @@ def test_validation_errors_before_device_work():
         assert ca.ring_attn_strerror(code) != "unknown error code"
     desc, _ = d()
     assert _rc_fwd(desc, nulls=True) == -1
+    desc.merge_mode = ca.RA_MERGE_STEPWISE   # the one-launch forward needs no workspace
+    assert _rc_fwd(desc, ws_bytes=16) == -8
+    desc.merge_mode = ca.RA_MERGE_SEPARATE
     assert _rc_fwd(desc, ws_bytes=16) == -8
     desc, _ = d(layout=ca.LLAMA3)
     desc.n_seqs = 1
@@ -185,7 +188,13 @@ def test_validation_errors_before_device_work():
 def test_workspace_sizes():
     desc = ca.make_desc(1, 32, 32, 128, 32768, 8, 7, True, ca.BASIC)
     S_pad = 4096
+    assert ca.ring_attn_workspace_bytes(desc, False) == 0   # one launch, registers
+    desc.merge_mode = ca.RA_MERGE_STEPWISE
     assert ca.ring_attn_workspace_bytes(desc, False) == 32 * S_pad * 128 * 4
+    desc.merge_mode = ca.RA_MERGE_FUSED
+    desc.dtype = ca.RA_F32                                   # fp32: one launch per step
+    assert ca.ring_attn_workspace_bytes(desc, False) == 32 * S_pad * 128 * 4
+    desc.dtype = ca.RA_BF16
     assert ca.ring_attn_workspace_bytes(desc, True) == 2 * 32 * S_pad * 4 + 32 * S_pad * 128 * 4
     desc.merge_mode = ca.RA_MERGE_SEPARATE
     assert ca.ring_attn_workspace_bytes(desc, False) == 2 * 32 * 4096 * 128 * 4 + 32 * 4096 * 4

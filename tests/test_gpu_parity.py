@@ -58,7 +58,8 @@ def _check_fwd(w, glob, rank, out, lse):
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("head_dim", [128, 64])
-@pytest.mark.parametrize("merge_mode", [ca.RA_MERGE_FUSED, ca.RA_MERGE_SEPARATE])
+@pytest.mark.parametrize("merge_mode", [ca.RA_MERGE_FUSED, ca.RA_MERGE_SEPARATE,
+                                        ca.RA_MERGE_STEPWISE])
 def test_fwd_bf16_small(layout, causal, head_dim, merge_mode):
     w = _small_workload(layout, causal, head_dim, seed=layout * 4 + causal)
     glob = synth.draw_global(w)
