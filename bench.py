@@ -279,6 +279,8 @@ def main():
                     help="only run the standalone LSE merge measurement")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the forward timing of the other bf16 configurations")
+    ap.add_argument("--fwd-only", action="store_true",
+                    help="time the forward alone (drop the backward of the workload)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one rank's share on ONE GPU; this build has no multi-GPU "
@@ -289,6 +291,8 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if args.with_grad:
         w = w.replace(with_grad=True)
+    if args.fwd_only:
+        w = w.replace(with_grad=False)
     pool = None
     if not (args.no_cpu_baseline or args.calibrate_copy or args.merge_only):
         pool, workers = start_host_pool(w)   # before any GPU call

@@ -172,6 +172,75 @@ def mfma_md(csv_path: str, cmd: str, title: str, n_xcd: int = 8, n_simd: int = 1
     return "\n".join(out) + "\n"
 
 
+# Per-SIMD and per-CU normalisations of the SQ counters (rocprofv3 sums them
+# over the shader engines of the chip): 8 XCDs, 256 CUs, 1024 SIMDs.
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
+
+
+def counters_md(csv_paths, kernels, cmds: str, title: str) -> str:
+    """Average per dispatch of every counter in the given CSVs (one rocprofv3
+    --pmc run each) for each kernel, plus derived fractions."""
+    per = {}   # kernel -> counter -> [values per dispatch]
+    dur = {}
+    for path in csv_paths:
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            k = next((k for k in kernels if k in name), None)
+            if k is None:
+                continue
+            key = (k, int(r["Dispatch_Id"]), r["Counter_Name"])
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+            dur.setdefault(k, {})[int(r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        for (k, d, c), v in acc.items():
+            per.setdefault(k, {}).setdefault(c, []).append(v)
+    out = [f"# SQ counters: {title}", "", "Commands (from the repository root, one MI355X; one run per "
+           "counter set):", "", "```", *cmds.split(" ;; "), "```", ""]
+    for k in kernels:
+        if k not in per:
+            continue
+        c = {n: statistics.mean(v) for n, v in per[k].items()}
+        ndisp = max(len(v) for v in per[k].values())
+        out += [f"## `{k}` ({ndisp} dispatches per counter set)", "", "| counter | mean per dispatch |",
+                "|---|---|"]
+        out += [f"| {n} | {c[n]:.4g} |" for n in sorted(c)]
+        gui = c.get("GRBM_GUI_ACTIVE")
+        der = []
+        if gui:
+            cyc = gui / N_XCD   # cycles of one XCD's clock over the dispatch
+            ns = statistics.mean(dur[k].values())
+            der.append(f"- average clock: {cyc / ns:.2f} GHz (GRBM_GUI_ACTIVE / 8 / duration)")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                der.append(f"- matrix cores busy: {100 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * N_SIMD):.1f}% "
+                           "of SIMD-cycles")
+            if "SQ_LDS_IDX_ACTIVE" in c:
+                der.append(f"- LDS busy (indexed access): {100 * c['SQ_LDS_IDX_ACTIVE'] / (cyc * N_CU):.1f}% "
+                           "of CU-cycles")
+            if "SQ_LDS_BANK_CONFLICT" in c:
+                der.append(f"- LDS stalled on bank conflicts: "
+                           f"{100 * c['SQ_LDS_BANK_CONFLICT'] / (cyc * N_CU):.1f}% of CU-cycles")
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in c and c.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+            der.append(f"- VALU issued while the matrix cores were busy: "
+                       f"{100 * c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.1f}% of "
+                       "their busy cycles")
+        wc = c.get("SQ_WAVE_CYCLES")
+        if wc:
+            for n in ("SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+                      "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_VMEM", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+                      "SQ_WAIT_INST_LDS"):
+                if n in c:
+                    der.append(f"- {n} / SQ_WAVE_CYCLES: {c[n] / wc:.3f}")
+        if "SQ_INSTS_VALU" in c and "SQ_INSTS_MFMA" in c and c["SQ_INSTS_MFMA"]:
+            der.append(f"- VALU instructions per MFMA: {c['SQ_INSTS_VALU'] / c['SQ_INSTS_MFMA']:.2f} "
+                       "(SQ_INSTS_VALU counts the MFMAs too)")
+        if "SQ_INSTS_LDS" in c and c.get("SQ_INSTS_MFMA"):
+            der.append(f"- LDS instructions per MFMA: {c['SQ_INSTS_LDS'] / c['SQ_INSTS_MFMA']:.2f}")
+        if der:
+            out += ["", "Derived:", "", *der]
+        out.append("")
+    return "\n".join(out) + "\n"
+
+
 def read_issued(md_path: str, kernel: str):
     """Issued bf16 MFMA flops per launch of `kernel` from a summary written by
     `mfma`, or None when missing or the kernel's sources changed."""
@@ -206,6 +275,12 @@ def main(argv=None):
     mf.add_argument("--cmd", required=True)
     mf.add_argument("--title", required=True)
     mf.add_argument("--out", required=True)
+    cn = sub.add_parser("counters")
+    cn.add_argument("csv", nargs="+")
+    cn.add_argument("--kernels", required=True, help="comma-separated kernel name substrings")
+    cn.add_argument("--title", required=True)
+    cn.add_argument("--cmds", required=True, help="the commands, separated by ' ;; '")
+    cn.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
@@ -220,6 +295,8 @@ def main(argv=None):
         text = stats_md(a.csv, a.cmd, a.title)
     elif a.mode == "mfma":
         text = mfma_md(a.csv, a.cmd, a.title)
+    elif a.mode == "counters":
+        text = counters_md(a.csv, a.kernels.split(","), a.cmds, a.title)
     else:
         text = traffic_md(a)
     with open(a.out, "w") as fh:
