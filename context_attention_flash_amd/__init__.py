@@ -25,7 +25,7 @@ RA_MERGE_FUSED, RA_MERGE_SEPARATE, RA_MERGE_STEPWISE = 0, 1, 2
 ERRORS = {
     -1: "RA_E_NULL", -2: "RA_E_SHAPE", -3: "RA_E_WORLD", -4: "RA_E_DIVISIBILITY",
     -5: "RA_E_CU_SEQLENS", -6: "RA_E_HEADS", -7: "RA_E_UNSUPPORTED", -8: "RA_E_WORKSPACE",
-    -9: "RA_E_LAYOUT", -10: "RA_E_HIP", -11: "RA_E_ARG",
+    -9: "RA_E_LAYOUT", -10: "RA_E_HIP", -11: "RA_E_ARG", -12: "RA_E_NO_PLAN", -13: "RA_E_SCRATCH",
 }
 
 
@@ -56,6 +56,8 @@ _SIGS = {
     "ring_attn_fwd": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "ring_attn_bwd": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                      ctypes.c_size_t, _P]),
+    "ring_attn_bwd_noalloc": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "ring_attn_noalloc_scratch_bytes": (ctypes.c_int64, []),
     "ring_attn_lse_merge": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int64,
                                            ctypes.c_int32, ctypes.c_int32, _P]),
     "ring_attn_positions": (ctypes.c_int, [_DP, _P, ctypes.c_int32, _P]),
@@ -309,6 +311,29 @@ def ring_attn_bwd(desc: RingAttnDesc, dout, q, k, v, out, lse, cu_seqlens=None, 
                              _stream_ptr(stream))
     _check(rc, "ring_attn_bwd")
     return dq, dk, dv
+
+
+def ring_attn_bwd_noalloc(desc: RingAttnDesc, dout, q, k, v, out, lse, dq, dk, dv,
+                          cu_seqlens=None, stream=None):
+    """ring_attn_bwd with the library's static scratch as workspace: allocates
+    nothing (every tensor is the caller's); the shape's plan must exist."""
+    torch = _torch()
+    sh = _shapes(desc)
+    dt = _elem_dtype(desc)
+    f32 = torch.float32
+    keep, cu = _cu_arg(cu_seqlens)
+    rc = lib().ring_attn_bwd_noalloc(ctypes.byref(desc), _expect(dout, sh["q"], dt, "dout"),
+                                     _expect(q, sh["q"], dt, "q"), _expect(k, sh["kv"], dt, "k"),
+                                     _expect(v, sh["kv"], dt, "v"), _expect(out, sh["q"], dt, "out"),
+                                     _expect(lse, sh["lse"], f32, "lse"), cu,
+                                     _expect(dq, sh["q"], f32, "dq"), _expect(dk, sh["kv"], f32, "dk"),
+                                     _expect(dv, sh["kv"], f32, "dv"), _stream_ptr(stream))
+    _check(rc, "ring_attn_bwd_noalloc")
+    return dq, dk, dv
+
+
+def ring_attn_noalloc_scratch_bytes() -> int:
+    return int(lib().ring_attn_noalloc_scratch_bytes())
 
 
 def ring_attn_lse_merge(out, lse, out_j, lse_j, stream=None):

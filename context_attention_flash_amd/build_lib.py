@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libringattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["abi.cpp", "planner.cpp", "fwd_bf16.hip", "fwd_f32.hip", "elementwise.hip",
-           "bwd_bf16.hip"]
+           "bwd_bf16.hip", "noalloc.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
           "--offload-arch=gfx950",

@@ -15,6 +15,7 @@
 #include <tuple>
 #include <vector>
 
+#include "abi_internal.h"
 #include "kernel_args.h"
 #include "planner.h"
 #include "ring_attn.h"
@@ -339,7 +340,9 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
     return RA_OK;
 }
 
-int get_plan(const Geometry& g, std::shared_ptr<const Plan>* out) {
+// The cached plan of this geometry on the current device; with build = false
+// a missing plan is RA_E_NO_PLAN instead of being built (no device allocation).
+int get_plan(const Geometry& g, std::shared_ptr<const Plan>* out, bool build = true) {
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return RA_E_HIP;
     const std::string key = std::to_string(device) + "#" + plan_key(g);
@@ -352,6 +355,7 @@ int get_plan(const Geometry& g, std::shared_ptr<const Plan>* out) {
             *out = g_plans.front().second;
             return RA_OK;
         }
+        if (!build) return RA_E_NO_PLAN;
         std::unique_ptr<Plan> p;
         const int rc = build_plan(g, device, p);
         if (rc != RA_OK) return rc;
@@ -383,12 +387,17 @@ struct Timing {
     double ms[KC_COUNT] = {};
 } g_timing;
 
+// Set while a call that may not allocate is running on this thread: the
+// timing then uses pooled events only.
+thread_local bool t_no_alloc = false;
+
 hipEvent_t take_event() {
     if (!g_timing.pool.empty()) {
         hipEvent_t e = g_timing.pool.back();
         g_timing.pool.pop_back();
         return e;
     }
+    if (t_no_alloc) return nullptr;   // the launch then runs untimed
     hipEvent_t e = nullptr;
     if (hipEventCreate(&e) != hipSuccess) return nullptr;
     return e;
@@ -527,6 +536,11 @@ const char* ring_attn_strerror(int code) {
         case RA_E_LAYOUT: return "unknown layout, or batch != 1 with a varlen layout";
         case RA_E_HIP: return "the HIP runtime reported an error";
         case RA_E_ARG: return "an argument is out of range (or a NaN / infinite softmax scale)";
+        case RA_E_NO_PLAN:
+            return "no cached plan for this shape: an ordinary call builds it (the no-allocation "
+                   "entry point only uses plans that exist)";
+        case RA_E_SCRATCH:
+            return "the call needs more scratch than the no-allocation entry point's static array";
         default: return "unknown error code";
     }
 }
@@ -734,10 +748,19 @@ int ring_attn_fwd(const ring_attn_desc* desc, const void* q, const void* k, cons
     }
 }
 
-int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, const void* k,
-                  const void* v, const void* out, const float* lse, const int32_t* cu,
-                  float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
-                  void* stream) {
+}  // extern "C"
+
+namespace ra {
+
+int bwd_impl(const ring_attn_desc* desc, const void* dout, const void* q, const void* k,
+             const void* v, const void* out, const float* lse, const int32_t* cu, float* dq,
+             float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream,
+             bool build_plan) {
+    struct NoAllocScope {   // no event creation in a call that may not allocate
+        bool prev;
+        explicit NoAllocScope(bool on) : prev(t_no_alloc) { t_no_alloc = on || prev; }
+        ~NoAllocScope() { t_no_alloc = prev; }
+    } scope(!build_plan);
     try {
         Geometry g;
         int rc = validate(desc, cu, &g, true);
@@ -747,7 +770,7 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
         const int64_t need = bwd_workspace(g);
         if (!workspace || (int64_t)workspace_bytes < need) return RA_E_WORKSPACE;
         std::shared_ptr<const Plan> plan;
-        if ((rc = get_plan(g, &plan)) != RA_OK) return rc;
+        if ((rc = get_plan(g, &plan, build_plan)) != RA_OK) return rc;
         hipStream_t s = (hipStream_t)stream;
         float* lse2 = (float*)workspace;
         float* ndelta = (float*)((unsigned char*)workspace + bwd_row_bytes(g));
@@ -853,6 +876,25 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, c
     } catch (...) {
         return RA_E_HIP;
     }
+}
+
+int64_t bwd_need_bytes(const ring_attn_desc* desc) {
+    Geometry g;
+    const int rc = validate(desc, nullptr, &g, false);
+    if (rc != RA_OK) return rc;
+    return bwd_workspace(g);
+}
+
+}  // namespace ra
+
+extern "C" {
+
+int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q, const void* k,
+                  const void* v, const void* out, const float* lse, const int32_t* cu,
+                  float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    return bwd_impl(desc, dout, q, k, v, out, lse, cu, dq, dk, dv, workspace, workspace_bytes,
+                    stream, true);
 }
 
 int ring_attn_timing_enable(int enable) {

@@ -151,6 +151,8 @@ typedef struct ring_attn_desc {
 #define RA_E_LAYOUT          -9  /* unknown layout, or batch != 1 for varlen   */
 #define RA_E_HIP            -10  /* the HIP runtime reported an error          */
 #define RA_E_ARG            -11  /* another argument out of range              */
+#define RA_E_NO_PLAN        -12  /* ring_attn_bwd_noalloc: shape never planned */
+#define RA_E_SCRATCH        -13  /* ring_attn_bwd_noalloc: scratch too small   */
 
 /* Shapes (all row-major, last dimension fastest):
  *   S   = N / D local rows;  Skv = S for ring layouts, N for RA_LLAMA3;
@@ -214,6 +216,29 @@ int ring_attn_bwd(const ring_attn_desc* desc, const void* dout, const void* q,
                   const void* k, const void* v, const void* out, const float* lse,
                   const int32_t* cu_seqlens, float* dq, float* dk, float* dv,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ring_attn_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving or training loops, harnesses that forbid
+ * hipMalloc): the same backward, with its workspace in a static device array
+ * of ring_attn_noalloc_scratch_bytes() bytes (64 MiB) that the library holds
+ * on every GPU it runs on until the process ends.  It calls no hipMalloc,
+ * hipFree or other allocating routine, and never builds a plan: the shape's
+ * plan must already be cached by an ordinary call (ring_attn_fwd or
+ * ring_attn_bwd with the same descriptor and cu_seqlens), else RA_E_NO_PLAN.
+ * A descriptor whose minimum backward workspace exceeds the array is
+ * RA_E_SCRATCH; what the array holds beyond that minimum serves as the dS
+ * tile store (kv heads in passes, or dQ by recomputation when none fits).
+ * All calls on one GPU share its array: calls that overlap in time on one GPU
+ * (other streams, other threads) race.  The array's contents are garbage
+ * between calls and need no clearing.  Arguments and results as for
+ * ring_attn_bwd. */
+int ring_attn_bwd_noalloc(const ring_attn_desc* desc, const void* dout, const void* q,
+                          const void* k, const void* v, const void* out, const float* lse,
+                          const int32_t* cu_seqlens, float* dq, float* dk, float* dv,
+                          void* stream);
+
+/* Bytes of the static scratch array ring_attn_bwd_noalloc uses (per GPU). */
+int64_t ring_attn_noalloc_scratch_bytes(void);
 
 /* Log-sum-exp merge ("Numerically-Stable Output Fusion"), standalone.  Folds a
  * partial (out_j, lse_j) into the running (out, lse) in place:
