@@ -58,9 +58,9 @@ struct BwdCfg {
     static constexpr int OFF_Q = 0;
     static constexpr int OFF_DO = Q_BYTES;
     static constexpr int OFF_L = 2 * Q_BYTES;
-    static constexpr int OFF_ND = OFF_L + BQ * 4;
-    static constexpr int OFF_RNG = OFF_ND + BQ * 4;
-    static constexpr int STAGE = OFF_RNG + BQ * 8;
+    static constexpr int OFF_ND = OFF_L + 1024;
+    static constexpr int OFF_RNG = OFF_ND + 1024;
+    static constexpr int STAGE = OFF_RNG + 2048;
     static_assert(BQ * 16 == 1024, "row values: one 16-byte chunk per lane of a wave");
 };
 
@@ -102,40 +102,38 @@ struct DkdvLoader {
     using C = BwdCfg<DH>;
     BufTileLoader<DH, C::BQ> lq, lo;
     // row values: lse2 and -Delta of batch entry b ([Hq][S_pad] each), the
-    // intervals ([S_pad][2]); lanes 0-15, 16-31 and 32-63 of wave 0 each load
-    // one of them with its own buffer (a direct-to-LDS global load instead
-    // would make the compiler drain every later LDS wait completely)
-    __amdgpu_buffer_rsrc_t rl, rd, rr;
+    // intervals ([S_pad][2]); waves 0, 1 and 2 each load 1 KiB of one of them
+    // (wave 3 loads lse2 again into a spare slot), so that every wave issues
+    // the same instructions and no lane mask splits the loop body
+    __amdgpu_buffer_rsrc_t rv;
+    int rv_h, rv_q;   // byte offset of the tile: head * rv_h + query tile * rv_q
 
     __device__ __forceinline__ void init(const BwdArgs& p, int b, int wave, int lane) {
         const int64_t batch = (int64_t)b * p.S * p.Hq * DH;
         lq.init(p.q + batch, p.S, p.Hq, 0, wave, lane);
         lo.init(p.dout + batch, p.S, p.Hq, 0, wave, lane);
         const int rows = p.Hq * p.S_pad * 4;
-        rl = __builtin_amdgcn_make_buffer_rsrc((void*)(p.lse2 + (int64_t)b * p.Hq * p.S_pad), (short)0,
-                                               rows, 0x00020000);
-        rd = __builtin_amdgcn_make_buffer_rsrc((void*)(p.ndelta + (int64_t)b * p.Hq * p.S_pad), (short)0,
-                                               rows, 0x00020000);
-        rr = __builtin_amdgcn_make_buffer_rsrc((void*)p.rng, (short)0, p.S_pad * 8, 0x00020000);
+        const float* base = wave == 1 ? p.ndelta : p.lse2;
+        rv_h = wave != 2 ? p.S_pad * 4 : 0;
+        rv_q = wave != 2 ? C::BQ * 4 : C::BQ * 8;
+        rv = wave == 2 ? __builtin_amdgcn_make_buffer_rsrc((void*)p.rng, (short)0, p.S_pad * 8, 0x00020000)
+                       : __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)b * p.Hq * p.S_pad),
+                                                           (short)0, rows, 0x00020000);
     }
 
     __device__ __forceinline__ void load(unsigned char* stage, const BwdArgs& p, int h, int qt,
                                          int wave, int lane) const {
         lq.load(stage + C::OFF_Q, qt, wave, h);
         lo.load(stage + C::OFF_DO, qt, wave, h);
-        if (wave == 0) {
-            auto* dst = (__attribute__((address_space(3))) void*)(stage + C::OFF_L);
-            const int row_off = (h * p.S_pad + qt * C::BQ) * 4;
-            if (lane < 16)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, dst, 16, lane * 16, row_off, 0, 0);
-            else if (lane < 32)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, dst, 16, (lane - 16) * 16, row_off, 0, 0);
-            else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, dst, 16, (lane - 32) * 16, qt * C::BQ * 8, 0, 0);
-        }
+        const int soff = h * rv_h + qt * rv_q;
+        auto* dst = (__attribute__((address_space(3))) void*)(stage + C::OFF_L + wave * 1024);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, lane * 16, soff, 0, 0);
     }
 };
 
+// Vector instructions the scheduler places after each MFMA (and its two LDS
+// reads) in the regions that compute P and dS.
+constexpr int K4A_VALU_PER_MFMA = 4;
 template <int DH, bool STORE_DS>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_bf16_kernel(BwdArgs p) {
     using C = BwdCfg<DH>;
@@ -147,7 +145,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     __shared__ __attribute__((aligned(16))) unsigned char stB[C::STAGE];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 5,
+              l32 = lane & 31;
     const int work = xcd_work_index(blockIdx.x, gridDim.x);
     if (work >= p.total_work) return;
     const int t = work % p.nkt, bh = work / p.nkt;
@@ -240,19 +239,34 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     struct SOps {
         u32x4_t qa[C::NKS], oa[C::NKS];
         f32x16_t nd;
+        f32x4_t L[4];        // lse2 of the half's rows, used by p_half
+        int4 ab[4][2];       // their key intervals (masked tiles only)
     };
-    auto s_read = [&](const unsigned char* st, int mt, SOps& o) {
-#pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) {
-            o.qa[ks] = *(const u32x4_t*)(st + C::OFF_Q + nat[ks] + mt * 32 * C::ROWB);
-            o.oa[ks] = *(const u32x4_t*)(st + C::OFF_DO + nat[ks] + mt * 32 * C::ROWB);
-        }
+    auto s_read = [&](const unsigned char* st, int mt, SOps& o, auto partial_tag) {
+        constexpr bool PARTIAL = decltype(partial_tag)::value;
+        // -Delta first: the first dP MFMA needs all of it
         const float* nd = (const float*)(st + C::OFF_ND);
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
             const f32x4_t x = *(const f32x4_t*)(nd + 32 * mt + 8 * rg + 4 * g);
 #pragma unroll
             for (int i = 0; i < 4; ++i) o.nd[4 * rg + i] = x[i];
+        }
+        const float* L2 = (const float*)(st + C::OFF_L);
+        const int32_t* R = (const int32_t*)(st + C::OFF_RNG);
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+            const int r0 = 32 * mt + 8 * rg + 4 * g;
+            o.L[rg] = *(const f32x4_t*)(L2 + r0);
+            if (PARTIAL) {
+                o.ab[rg][0] = *(const int4*)(R + 2 * r0);
+                o.ab[rg][1] = *(const int4*)(R + 2 * r0 + 4);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+            o.qa[ks] = *(const u32x4_t*)(st + C::OFF_Q + nat[ks] + mt * 32 * C::ROWB);
+            o.oa[ks] = *(const u32x4_t*)(st + C::OFF_DO + nat[ks] + mt * 32 * C::ROWB);
         }
     };
     auto s_mfma = [&](const SOps& o, f32x16_t& sacc, f32x16_t& pacc) {
@@ -268,21 +282,18 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // P = exp2(S * scale * log2(e) - lse2) and dS = P (dP - Delta) of half mt,
     // packed to bf16 as the B operands of dV^T and dK^T for the query blocks
     // kk = 2*mt and 2*mt + 1.
-    auto p_half = [&](const unsigned char* st, int mt, auto partial_tag, const f32x16_t& sacc,
+    auto p_half = [&](const SOps& o, int mt, auto partial_tag, const f32x16_t& sacc,
                       const f32x16_t& pacc, u32x4_t (&pb)[2], u32x4_t (&db)[2], uint16_t* ds_tile) {
         constexpr bool PARTIAL = decltype(partial_tag)::value;
-        const float* L2 = (const float*)(st + C::OFF_L);
-        const int32_t* R = (const int32_t*)(st + C::OFF_RNG);
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-            const int r0 = 32 * mt + 8 * rg + 4 * g;
-            const f32x4_t L = *(const f32x4_t*)(L2 + r0);
+            const f32x4_t L = o.L[rg];
             float pr[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(sacc[4 * rg + i], c2, -L[i]));
             if (PARTIAL) {  // keys outside a row's interval [a, b) are invisible
-                const int4 ab0 = *(const int4*)(R + 2 * r0);
-                const int4 ab1 = *(const int4*)(R + 2 * r0 + 4);
+                const int4 ab0 = o.ab[rg][0];
+                const int4 ab1 = o.ab[rg][1];
                 const int av[4] = {ab0.x, ab0.z, ab1.x, ab1.z};
                 const int bv[4] = {ab0.y, ab0.w, ab1.y, ab1.w};
 #pragma unroll
@@ -340,11 +351,11 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             }
     };
 
-    // dV/dK of the second half of a tile run at the start of the next
-    // iteration, before its barrier: their operands (read below, at the end of
-    // the tile) and P/dS wait in registers, and the MFMAs execute while the
-    // wave waits at the barrier.  Every LDS read of a stage is complete before
-    // that barrier, so two stages still suffice.  Zero-initialised, the first
+    // dV/dK of the second half of a tile run in the next iteration, after its
+    // barrier: their operands (read below, at the end of the tile) and P/dS
+    // wait in registers, and the MFMAs execute while the wave issues the next
+    // tile's loads.  Every LDS read of a stage is complete before that
+    // barrier, so two stages still suffice.  Zero-initialised, the first
     // iteration's carried MFMAs add nothing.
     u32x4_t c_oa[C::NDT][2], c_qa[C::NDT][2], c_pb[2], c_db[2];
 #pragma unroll
@@ -358,50 +369,87 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // cores while P/dS of half 0 run on the vector ALUs, then dV/dK of half 0
     // while P/dS of half 1; the operands of half 1's dV/dK are read last.
     // Scheduling fences split the tile into regions; the LDS reads of each
-    // region's MFMAs are issued in the region before, so that the MFMAs do
-    // not wait for them, and the fences bound the registers in flight.
-    auto tile = [&](const unsigned char* st, auto partial_tag, uint16_t* ds_tile) {
+    // region's MFMAs (and the row values its vector work needs) are issued in
+    // the region before, so that the MFMAs do not wait for them, and the
+    // fences bound the registers in flight.  Inside a region, group barriers
+    // interleave the MFMAs with the LDS reads and the vector work: with one
+    // wave per SIMD nothing else fills the matrix pipe while the wave issues
+    // a run of other instructions.
+    auto tile = [&](const unsigned char* st, auto partial_tag, uint16_t* ds_tile, const SOps& o0) {
         f32x16_t s0, p0, s1, p1;
         u32x4_t pb0[2], db0[2];
-        SOps o0, o1;
+        SOps o1;
         u32x4_t oa[C::NDT][2], qa[C::NDT][2];
-        s_read(st, 0, o0);
-        __builtin_amdgcn_sched_barrier(0);
         s_mfma(o0, s0, p0);
-        s_read(st, 1, o1);
+        s_read(st, 1, o1, partial_tag);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+        }
         __builtin_amdgcn_sched_barrier(0);
         s_mfma(o1, s1, p1);
-        p_half(st, 0, partial_tag, s0, p0, pb0, db0, ds_tile);
+        p_half(o0, 0, partial_tag, s0, p0, pb0, db0, ds_tile);
         read_half(st, 0, oa, qa);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+            __builtin_amdgcn_sched_group_barrier(0x002, K4A_VALU_PER_MFMA, 2);
+        }
         __builtin_amdgcn_sched_barrier(0);
         mfma_half(oa, qa, pb0, db0);
-        p_half(st, 1, partial_tag, s1, p1, c_pb, c_db, ds_tile);
+        p_half(o1, 1, partial_tag, s1, p1, c_pb, c_db, ds_tile);
         read_half(st, 1, c_oa, c_qa);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 3);
+            __builtin_amdgcn_sched_group_barrier(0x002, K4A_VALU_PER_MFMA, 3);
+        }
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // Iteration it: the carried dV/dK MFMAs of tile it-1, then the barrier
-    // that makes tile it visible and frees the other stage, which receives
-    // tile it+1.  Even iterations use stage A, odd ones stage B.
+    // Iteration it: the barrier that makes tile it visible and frees the
+    // other stage; then, in one region, the loads of tile it+1 into that
+    // stage, the LDS reads of half 0 of tile it and the carried dV/dK MFMAs
+    // of tile it-1, interleaved so that the MFMAs run while the wave issues
+    // the loads (each direct-to-LDS load holds the wave for about as long as
+    // an MFMA executes).  The last iteration loads a tile again (the loads
+    // are unconditional, so that no branch splits the region).  Even
+    // iterations use stage A, odd ones stage B.
     // cursors of tiles it, it+1 and it+2
     Cursor cu0 = m != e0 ? Cursor{0, 0, e0, m - e0} : Cursor{0, 0, m, e1 - m};
     Cursor cu1 = advance(cu0), cu2 = advance(cu1);
     int ent_nx = n_iter > 1 ? ents[index_of(cu1)] : 0;   // entry of tile it+1
     auto step = [&](int it, unsigned char* cur, unsigned char* nxt, auto partial_tag) {
-        mfma_half(c_oa, c_qa, c_pb, c_db);
-#pragma unroll
-        for (int dt = 0; dt < C::NDT; ++dt) asm volatile("" : "+a"(dk_acc[dt]), "+a"(dv_acc[dt]));
         // this wave's loads of tile it have landed; with the dS store, the
         // four dS stores of tile it-1, issued after those loads, may still be
         // in flight (vmcnt <= 4: vector memory operations complete in order)
         __builtin_amdgcn_s_waitcnt(STORE_DS ? 0x0004 : 0);
         __syncthreads();
-        if (it + 1 < n_iter) load(cu1, ent_nx, nxt);
+        {
+            const bool more = it + 1 < n_iter;
+            const Cursor cl = more ? cu1 : cu0;
+            load(cl, ent_nx, nxt);
+        }
+        SOps o0;
+        s_read(cur, 0, o0, partial_tag);
+        mfma_half(c_oa, c_qa, c_pb, c_db);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt) asm volatile("" : "+a"(dk_acc[dt]), "+a"(dv_acc[dt]));
         uint16_t* ds_tile = nullptr;   // this tile's place in the dS tile store
         if constexpr (STORE_DS)
             ds_tile = p.ds + ((int64_t)(b * p.nhk + hk - p.hk0) * group + cu0.hd) * p.ds_ne * DS_TILE_ELEMS +
                       (int64_t)index_of(cu0) * DS_TILE_ELEMS;
-        tile(cur, partial_tag, ds_tile);
+        tile(cur, partial_tag, ds_tile, o0);
         // the scalar load goes out after the tile's LDS reads: while it is in
         // flight every LDS wait must be a full one (scalar loads return out of
         // order)
@@ -425,6 +473,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         if (it + 1 < n_iter) step(it + 1, stB, stA, std::true_type{});
     }
     mfma_half(c_oa, c_qa, c_pb, c_db);   // the last tile's second half
+    // the last iteration's load (of a tile nobody reads) lands before the
+    // work-group can end and release its LDS
+    __builtin_amdgcn_s_waitcnt(0);
 
     // dK_j += scale * dK^T acc, dV_j += dV^T acc (this lane's key, 64 head-dim values)
     if (key < p.Skv) {
