@@ -232,21 +232,31 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
     // Entries of tiles i, i+1 and i+2 (0 past the list), the last one fetched
     // an iteration ahead; key tile, plan step and KV block of each.
     constexpr int KT_MASK = RING ? (1 << RING_STEP_SHIFT) - 1 : 0x7fffffff;
-    auto raw_at = [&](int i) { return i < n ? ents[e0 + i] : 0; };
+    // (called with n > 0 only; the load is clamped to the list so that the
+    // loop needs no branch)
+    auto raw_at = [&](int i) {
+        const int v = ents[e0 + min(i, n - 1)];
+        return i < n ? v : 0;
+    };
     auto step_of = [&](int e) { return RING ? (e >> RING_STEP_SHIFT) & (RING_MAX_STEPS - 1) : 0; };
     auto blk_of = [&](int e) { return RING ? as_const(p.blk)[step_of(e)] : 0; };
-    int en0 = raw_at(0), en1 = raw_at(1), en2 = raw_at(2);
-    int jb1 = blk_of(en1), jb2 = blk_of(en2);
+    int en0 = 0, en1 = 0, en2 = 0, jb1 = 0, jb2 = 0;
+    if (n > 0) {
+        en0 = raw_at(0);
+        en1 = raw_at(1);
+        en2 = raw_at(2);
+        jb1 = blk_of(en1);
+        jb2 = blk_of(en2);
+    }
     // RING: the interval of the lane's row in the next tile's step, loaded a
     // tile ahead when that tile needs the mask; a tile that needs none (the
     // odd last one of the unmasked tiles runs in the masked loop) keeps every key
     int2 rng_nx = {0, 0x7fffffff};
     auto fetch_rng = [&](int e) {
         if (!RING) return;
-        if (e < 0)
-            rng_nx = *(const int2*)(p.rng + (int64_t)step_of(e) * p.rng_stride + 2 * iq);
-        else
-            rng_nx = {0, 0x7fffffff};
+        const int2 v = *(const int2*)(p.rng + (int64_t)step_of(e) * p.rng_stride + 2 * iq);
+        rng_nx.x = e < 0 ? v.x : 0;
+        rng_nx.y = e < 0 ? v.y : 0x7fffffff;
     };
 
     // iteration i: refill, S(i+1) on the matrix cores with softmax(i), P V of
@@ -261,13 +271,15 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
             ra = rng_nx.x;
             rb = rng_nx.y;
         }
+        // unconditional: past the list the entries are 0, a valid tile that
+        // nobody reads (no branch splits the region of the MFMAs below)
         if (RING) {
-            if (i + 2 < n) lk.load_from(Kl, k_rsrc(jb2), en2 & KT_MASK, wave);
-            if (i + 1 < n) lv.load_from(Vl, v_rsrc(jb1), en1 & KT_MASK, wave);
+            lk.load_from(Kl, k_rsrc(jb2), en2 & KT_MASK, wave);
+            lv.load_from(Vl, v_rsrc(jb1), en1 & KT_MASK, wave);
             fetch_rng(en1);
         } else {
-            if (i + 2 < n) lk.load(Kl, en2 & KT_MASK, wave);
-            if (i + 1 < n) lv.load(Vl, en1 & KT_MASK, wave);
+            lk.load(Kl, en2 & KT_MASK, wave);
+            lv.load(Vl, en1 & KT_MASK, wave);
         }
         const int kt = en0 & KT_MASK;
         en0 = en1;
@@ -307,6 +319,9 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
             body(i, sa, sb, KB, KA, VA, VB, std::true_type{});
             if (i + 1 < n) body(i + 1, sb, sa, KA, KB, VB, VA, std::true_type{});
         }
+        // the last iterations' loads (of tiles nobody reads) land before the
+        // stages are reused below
+        __builtin_amdgcn_s_waitcnt(0);
     }
 
     // ---- epilogue: normalise the step's partial and apply the step mode ----
