@@ -260,6 +260,29 @@ def calibrate_copy(torch, nbytes=256 << 20, reps=5):
                       "bytes_written_per_dispatch": nbytes, "dispatches": reps}), flush=True)
 
 
+def sustain(ca, torch, args, desc, w, t, out, lse, ws_f, ws_b, grads):
+    """Run one pass of the workload back to back for args.seconds, so that the
+    GPU's power draw and clocks can be read while it holds a steady load."""
+    def one():
+        if args.sustain in ("fwd", "step"):
+            ca.ring_attn_fwd(desc, t["q"], t["k"], t["v"], w.cu_seqlens, out, lse, ws_f)
+        if args.sustain in ("bwd", "step"):
+            ca.ring_attn_bwd(desc, t["dout"], t["q"], t["k"], t["v"], out, lse, w.cu_seqlens,
+                             *grads, ws_b)
+    ca.ring_attn_fwd(desc, t["q"], t["k"], t["v"], w.cu_seqlens, out, lse, ws_f)
+    torch.cuda.synchronize()
+    log(f"sustain {args.sustain} for {args.seconds} s")
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < args.seconds:
+        for _ in range(4):
+            one()
+        n += 4
+        torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    print(json.dumps({"sustain": args.sustain, "workload": w.name, "calls": n,
+                      "ms_per_call": elapsed / n * 1e3, "seconds": elapsed}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +304,10 @@ def main():
                     help="skip the forward timing of the other bf16 configurations")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time the forward alone (drop the backward of the workload)")
+    ap.add_argument("--sustain", choices=("fwd", "bwd", "step"),
+                    help="only run that pass of the workload back to back for --seconds "
+                         "(a steady load for reading power and clocks from outside)")
+    ap.add_argument("--seconds", type=float, default=20.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one rank's share on ONE GPU; this build has no multi-GPU "
@@ -293,8 +320,10 @@ def main():
         w = w.replace(with_grad=True)
     if args.fwd_only:
         w = w.replace(with_grad=False)
+    if args.sustain:
+        w = w.replace(with_grad=args.sustain != "fwd")
     pool = None
-    if not (args.no_cpu_baseline or args.calibrate_copy or args.merge_only):
+    if not (args.no_cpu_baseline or args.calibrate_copy or args.merge_only or args.sustain):
         pool, workers = start_host_pool(w)   # before any GPU call
 
     import torch
@@ -330,6 +359,11 @@ def main():
         if w.with_grad:
             ca.ring_attn_bwd(desc, t["dout"], t["q"], t["k"], t["v"], out, lse, w.cu_seqlens,
                              dq, dk, dv, ws_b)
+
+    if args.sustain:
+        sustain(ca, torch, args, desc, w, t, out, lse, ws_f, ws_b if w.with_grad else None,
+                (dq, dk, dv) if w.with_grad else None)
+        return
 
     for i in range(args.warmup):
         step()

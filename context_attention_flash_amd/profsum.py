@@ -14,6 +14,10 @@ dispatch), SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE into the bf16 flops
 each kernel issued per launch, its matrix-core busy fraction and its average
 clock, with the same source hash per kernel.
 
+`power` turns samples of `amd-smi metric -p -c` (socket power and the clock
+of every XCD), taken while bench.py holds a pass of the workload running back
+to back (`--sustain`), into a table per pass.
+
 `traffic` turns the FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch, as
 rocprofv3 reports them) of one kernel into bytes per launch.  Each counter is
 scaled by the factor that maps what it reads for a plain copy kernel of known
@@ -241,6 +245,34 @@ def counters_md(csv_paths, kernels, cmds: str, title: str) -> str:
     return "\n".join(out) + "\n"
 
 
+def parse_smi_samples(text: str):
+    """(socket watts, [GFX clock MHz of each XCD]) of every `amd-smi metric -p
+    -c` sample in `text`."""
+    out = []
+    for chunk in re.split(r"^GPU: \d+\s*$", text, flags=re.M)[1:]:
+        pw = re.search(r"SOCKET_POWER:\s*(\d+(?:\.\d+)?)\s*W", chunk)
+        clks = [float(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+(?:\.\d+)?)\s*MHz", chunk)]
+        if pw and clks:
+            out.append((float(pw.group(1)), clks))
+    return out
+
+
+def power_md(files, labels, cmds: str, title: str) -> str:
+    lines = [f"# Power and clocks under a sustained load: {title}", "",
+             "Commands (from the repository root, one MI355X):", "", "```"]
+    lines += [c.strip() for c in cmds.split(" ;; ")]
+    lines += ["```", "", "| pass | sample | socket power (W) | XCD clocks (MHz) | mean clock (MHz) |",
+              "|---|---|---|---|---|"]
+    for path, label in zip(files, labels):
+        with open(path) as fh:
+            samples = parse_smi_samples(fh.read())
+        for i, (w, clks) in enumerate(samples):
+            lines.append(f"| {label} | {i} | {w:.0f} | {', '.join(f'{c:.0f}' for c in clks)} | "
+                         f"{statistics.mean(clks):.0f} |")
+    lines.append("")
+    return "\n".join(lines)
+
+
 def read_issued(md_path: str, kernel: str):
     """Issued bf16 MFMA flops per launch of `kernel` from a summary written by
     `mfma`, or None when missing or the kernel's sources changed."""
@@ -281,6 +313,12 @@ def main(argv=None):
     cn.add_argument("--title", required=True)
     cn.add_argument("--cmds", required=True, help="the commands, separated by ' ;; '")
     cn.add_argument("--out", required=True)
+    pw = sub.add_parser("power")
+    pw.add_argument("files", nargs="+", help="amd-smi outputs, one per pass")
+    pw.add_argument("--labels", required=True, help="comma-separated pass names")
+    pw.add_argument("--title", required=True)
+    pw.add_argument("--cmds", required=True, help="the commands, separated by ' ;; '")
+    pw.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
@@ -297,6 +335,8 @@ def main(argv=None):
         text = mfma_md(a.csv, a.cmd, a.title)
     elif a.mode == "counters":
         text = counters_md(a.csv, a.kernels.split(","), a.cmds, a.title)
+    elif a.mode == "power":
+        text = power_md(a.files, a.labels.split(","), a.cmds, a.title)
     else:
         text = traffic_md(a)
     with open(a.out, "w") as fh:

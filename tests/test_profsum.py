@@ -62,3 +62,28 @@ def test_mfma_summary_from_counter_rows(tmp_path):
     stale = out.read_text().replace(profsum.source_hash("fwd_step_bf16_kernel"), "0" * 16)
     out.write_text(stale)
     assert profsum.read_issued(str(out), "fwd_step_bf16_kernel") is None
+
+
+def test_power_samples_parse():
+    text = """GPU: 0
+    POWER:
+        SOCKET_POWER: 1349 W
+        GFX_VOLTAGE: N/A
+    CLOCK:
+        GFX_0:
+            CLK: 1870 MHz
+            MIN_CLK: 500 MHz
+        GFX_1:
+            CLK: 1792 MHz
+            MIN_CLK: 500 MHz
+        MEM_0:
+            CLK: 2000 MHz
+GPU: 0
+    POWER:
+        SOCKET_POWER: 1400 W
+    CLOCK:
+        GFX_0:
+            CLK: 1641 MHz
+"""
+    got = profsum.parse_smi_samples(text)
+    assert got == [(1349.0, [1870.0, 1792.0]), (1400.0, [1641.0])]
