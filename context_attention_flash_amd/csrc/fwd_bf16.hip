@@ -163,16 +163,24 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
         }
     };
 
-    // softmax of tile i (scores in sacc) and O^T += V^T P^T
-    auto pv_tile = [&](f32x16_t (&sacc)[2], int kt, const unsigned char* Vs, auto partial_tag) {
+    // The softmax of a tile is split around the tile boundary: the row max of
+    // tile i+1 (and the rescale of O it may call for) is taken at the end of
+    // iteration i, right after its scores are computed, so that iteration
+    // i+1 can start its exponentials at once, beside the S MFMAs of tile i+2,
+    // and the MFMAs of P V run beside the next max.  The order of operations
+    // on every row is unchanged.
+
+    // mask of a tile (keys outside [a, b) are invisible) and its row max,
+    // in log2 units
+    auto mask_max = [&](f32x16_t (&sacc)[2], int kt, int a, int b, auto partial_tag) {
         constexpr bool PARTIAL = decltype(partial_tag)::value;
-        if (PARTIAL) {  // keys outside [ra, rb) are invisible
+        if (PARTIAL) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = kt * C::BK + 32 * mt + (r >> 2) * 8 + g * 4 + (r & 3);
-                    sacc[mt][r] = ((key >= ra) & (key < rb)) ? sacc[mt][r] : -INFINITY;
+                    sacc[mt][r] = ((key >= a) & (key < b)) ? sacc[mt][r] : -INFINITY;
                 }
         }
         // linear chain: the compiler fuses pairs into v_max3_f32 (built with
@@ -180,17 +188,25 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
         float mx = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, sacc[0][r]), sacc[1][r]);
-        mx = pair_max(mx) * c2;
-        // move the reference max only when this tile exceeds it by > kSlack;
-        // lanes that do not move keep alpha = 1 (m_run may be -inf there)
-        const bool bump = mx > m_run + kSlack;
+        return pair_max(mx) * c2;
+    };
+    // move the reference max only when the tile exceeds it by > kSlack;
+    // lanes that do not move keep alpha = 1 (m_run may be -inf there); the O
+    // rescale is skipped by the whole wave in almost every tile
+    auto rebase = [&](float mx, bool valid) {
+        const bool bump = valid & (mx > m_run + kSlack);
         const float alpha = bump ? fast_exp2(m_run - mx) : 1.f;  // 0 if m_run = -inf
         m_run = bump ? mx : m_run;
         l_run *= alpha;
+        if (__builtin_amdgcn_ballot_w64(bump)) {
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] *= alpha;
+        }
+    };
+    // P rounded to bf16 for P V; the row sum stays in fp32 (a sum of the
+    // rounded values would cost up to 2^-9 in lse on rows with few keys)
+    auto p_tile = [&](const f32x16_t (&sacc)[2], u32x4_t (&pb)[4]) {
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        // P rounded to bf16 for P V; the row sum stays in fp32 (a sum of the
-        // rounded values would cost up to 2^-9 in lse on rows with few keys)
-        u32x4_t pb[4];
         float rsum = 0.f;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -202,14 +218,11 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
                 pb[2 * mt + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(p0, p1);
             }
         l_run += rsum;
-        // the O rescale is skipped by the whole wave in almost every tile
-        if (__builtin_amdgcn_ballot_w64(bump)) {
-#pragma unroll
-            for (int dt = 0; dt < C::NDT; ++dt) oacc[dt] *= alpha;
-        }
-        // O^T += V^T P^T; the K dimension (keys) of step kk takes rows
-        // 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3, as P is held.  The V^T
-        // operands of step kk+1 are read while the MFMAs of step kk run.
+    };
+    // O^T += V^T P^T; the K dimension (keys) of step kk takes rows
+    // 16kk + 4g + 0..3 and 16kk + 8 + 4g + 0..3, as P is held.  The V^T
+    // operands of step kk+1 are read while the MFMAs of step kk run.
+    auto pv_tile = [&](const u32x4_t (&pb)[4], const unsigned char* Vs) {
         u32x4_t va[2][C::NDT];
         auto read_v = [&](u32x4_t (&dst)[C::NDT], int kk) {
 #pragma unroll
@@ -248,56 +261,64 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
         jb1 = blk_of(en1);
         jb2 = blk_of(en2);
     }
-    // RING: the interval of the lane's row in the next tile's step, loaded a
-    // tile ahead when that tile needs the mask; a tile that needs none (the
-    // odd last one of the unmasked tiles runs in the masked loop) keeps every key
-    int2 rng_nx = {0, 0x7fffffff};
+    // RING: the interval of the lane's row in a tile's step (every key for a
+    // tile that needs no mask), loaded two tiles ahead: rng1 is tile i+1's
+    // (masked at the end of iteration i), the load issued in iteration i is
+    // tile i+2's.
+    int2 rng1 = {ra, rb};
     auto fetch_rng = [&](int e) {
-        if (!RING) return;
-        const int2 v = *(const int2*)(p.rng + (int64_t)step_of(e) * p.rng_stride + 2 * iq);
-        rng_nx.x = e < 0 ? v.x : 0;
-        rng_nx.y = e < 0 ? v.y : 0x7fffffff;
+        int2 r = {ra, rb};
+        if (RING) {
+            const int2 v = *(const int2*)(p.rng + (int64_t)step_of(e) * p.rng_stride + 2 * iq);
+            r.x = e < 0 ? v.x : 0;
+            r.y = e < 0 ? v.y : 0x7fffffff;
+        }
+        return r;
     };
 
-    // iteration i: refill, S(i+1) on the matrix cores with softmax(i), P V of
-    // tile i.  S(i+1) of the last tile reads a stale stage and is discarded.
+    // iteration i: refill; S(i+1) on the matrix cores beside P(i); P V of
+    // tile i beside the max of tile i+1, then its rebase.  S(i+1) of the last
+    // tile reads a stale stage and is discarded.
     auto body = [&](int i, f32x16_t (&cur)[2], f32x16_t (&nxt)[2], const unsigned char* Kn,
                     unsigned char* Kl, const unsigned char* Vc, unsigned char* Vl,
                     auto partial_tag) {
-        constexpr bool PARTIAL = decltype(partial_tag)::value;
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into LDS have landed
         __syncthreads();  // K(i+1) and V(i) are in LDS; the stages refilled below are free
-        if (RING && PARTIAL) {
-            ra = rng_nx.x;
-            rb = rng_nx.y;
-        }
         // unconditional: past the list the entries are 0, a valid tile that
         // nobody reads (no branch splits the region of the MFMAs below)
+        int2 rng2 = rng1;
         if (RING) {
             lk.load_from(Kl, k_rsrc(jb2), en2 & KT_MASK, wave);
             lv.load_from(Vl, v_rsrc(jb1), en1 & KT_MASK, wave);
-            fetch_rng(en1);
+            rng2 = fetch_rng(en2);
         } else {
             lk.load(Kl, en2 & KT_MASK, wave);
             lv.load(Vl, en1 & KT_MASK, wave);
         }
-        const int kt = en0 & KT_MASK;
+        const int kt1 = en1 & KT_MASK;
         en0 = en1;
         en1 = en2;
         jb1 = jb2;
         en2 = raw_at(i + 3);
         if (RING) jb2 = blk_of(en2);
         s_tile(nxt, Kn);
-        pv_tile(cur, kt, Vc, partial_tag);
+        u32x4_t pb[4];
+        p_tile(cur, pb);
+        pv_tile(pb, Vc);
+        const float mx = mask_max(nxt, kt1, rng1.x, rng1.y, partial_tag);
+        rebase(mx, i + 1 < n);
+        rng1 = rng2;
     };
 
     if (n > 0) {
+        int2 rng0 = {ra, rb};
         if (RING) {
             const int jb0 = blk_of(en0);
             lk.load_from(KA, k_rsrc(jb0), en0 & KT_MASK, wave);
             lv.load_from(VA, v_rsrc(jb0), en0 & KT_MASK, wave);
             if (n > 1) lk.load_from(KB, k_rsrc(jb1), en1 & KT_MASK, wave);
-            fetch_rng(en0);
+            rng0 = fetch_rng(en0);
+            rng1 = fetch_rng(en1);
         } else {
             lk.load(KA, en0 & KT_MASK, wave);
             lv.load(VA, en0 & KT_MASK, wave);
@@ -307,11 +328,13 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
         __syncthreads();
         f32x16_t sa[2], sb[2];
         s_tile(sa, KA);
-        // full tiles in pairs, unmasked; a last odd full tile joins the masked
-        // loop (its mask keeps every key)
-        const int nF2 = (m_full - e0) & ~1;
+        rebase(mask_max(sa, en0 & KT_MASK, rng0.x, rng0.y, std::true_type{}), true);
+        // iterations whose next tile needs no mask, in pairs; the rest mask
+        // the next tile (a tile that needs none keeps every key)
+        const int nF = m_full - e0;
+        const int nU = nF > 1 ? (nF - 1) & ~1 : 0;
         int i = 0;
-        for (; i < nF2; i += 2) {
+        for (; i < nU; i += 2) {
             body(i, sa, sb, KB, KA, VA, VB, std::false_type{});
             body(i + 1, sb, sa, KA, KB, VB, VA, std::false_type{});
         }
