@@ -181,6 +181,102 @@ def merge_bandwidth(ca, torch, rows=524288, d=128, reps=20):
 MERGE_TRAFFIC_MD = "traffic_lse_merge_kernel_rows524288_d128.md"
 
 
+def merge_rotating(ca, torch, rows=131072, d=128, sets=3, reps=30):
+    """The merge at basic_s4096's per-step shape (131072 rows x 128, 193.5 MiB
+    per call, which alone would fit in the 256 MB MALL), cycling through three
+    buffer sets so that a call does not find its operands cached by the last."""
+    B, H = 1, 32
+    S = rows // H
+    bufs = [(torch.randn(B, S, H, d, device="cuda"), torch.randn(B, H, S, device="cuda"),
+             torch.randn(B, S, H, d, device="cuda"), torch.randn(B, H, S, device="cuda"))
+            for _ in range(sets)]
+    for i in range(sets):
+        ca.ring_attn_lse_merge(bufs[i][0], bufs[i][1], bufs[i][2], bufs[i][3])
+    torch.cuda.synchronize()
+    ca.ring_attn_timing_enable(False)
+    ca.ring_attn_timing_enable(True)
+    for i in range(reps):
+        o, l, oj, lj = bufs[i % sets]
+        ca.ring_attn_lse_merge(o, l, oj, lj)
+    n, ms = ca.ring_attn_timing_read("lse_merge")
+    ca.ring_attn_timing_enable(False)
+    nbytes = (12 * d + 12) * rows
+    gbs = nbytes / (ms / n * 1e-3) / 1e9
+    del bufs
+    torch.cuda.empty_cache()
+    return {"rows": rows, "head_dim": d, "buffer_sets": sets, "bytes_per_launch": nbytes,
+            "avg_ms": ms / n, "GB/s": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS}
+
+
+def measured_peaks(torch):
+    """What this GPU delivers in isolation, beside the spec peaks: bf16 MFMAs
+    alone (libraprobe.so's MFMA-only kernel, two work-groups of four waves per
+    CU, timed after a second of the same load so that the clock has settled)
+    and a plain device copy of 1 GiB (torch's copy kernel; bytes read +
+    written)."""
+    import ctypes
+    path = os.path.join(ROOT, "context_attention_flash_amd", "libraprobe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with python -c 'import __graft_entry__ as g; g.build()'")
+    probe = ctypes.CDLL(path)
+    probe.ra_probe_mfma.restype = ctypes.c_int
+    probe.ra_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    probe.ra_probe_mfma_flops.restype = ctypes.c_double
+    probe.ra_probe_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    blocks, iters = 512, 16384
+    out = torch.empty(blocks * 256, device="cuda")
+    stream = torch.cuda.current_stream()
+    def launch():
+        rc = probe.ra_probe_mfma(out.data_ptr(), blocks, iters, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"ra_probe_mfma failed ({rc})")
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:
+        launch()
+        torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    ev0.record(stream)
+    for _ in range(reps):
+        launch()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    mfma_tf = probe.ra_probe_mfma_flops(blocks, iters) * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e12
+    assert torch.isfinite(out).all().item()
+    x = torch.empty(1 << 28, device="cuda")   # 1 GiB of fp32
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    ev0.record(stream)
+    for _ in range(reps):
+        y.copy_(x)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * x.numel() * 4 * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del x, y, out
+    torch.cuda.empty_cache()
+    return {"mfma_only_bf16_TFLOP/s": mfma_tf, "mfma_only_frac_of_spec": mfma_tf / PEAK_BF16_TFLOPS,
+            "copy_GB/s": copy_gbs, "copy_frac_of_spec": copy_gbs / PEAK_HBM_GBS,
+            "spec": {"bf16_TFLOP/s": PEAK_BF16_TFLOPS, "hbm_GB/s": PEAK_HBM_GBS}}
+
+
+def plan_cost(ca, torch, desc, w, call):
+    """Time of the first call for a shape (plan built on the host and uploaded,
+    then the kernels) against the same call once the plan is cached."""
+    ca.ring_attn_clear_cache()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    call()
+    torch.cuda.synchronize()
+    first = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    call()
+    torch.cuda.synchronize()
+    cached = time.perf_counter() - t0
+    return {"first_call_ms": first * 1e3, "cached_call_ms": cached * 1e3,
+            "plan_ms": (first - cached) * 1e3}
+
+
 # Forward-only configurations timed in the same run as the headline step (their
 # parity is covered by the tests; here they are timed on seeded N(0,1) inputs
 # drawn on the device, which have the same distribution as the tests' inputs).
@@ -202,6 +298,7 @@ def time_forward(ca, torch, synth, name, steps, warmup):
     ws = ca.alloc_workspace(desc, False)
     pairs = sum(p for _, _, p in ca.ring_attn_schedule(desc, w.cu_seqlens))
     flops = 4.0 * w.head_dim * w.heads_q * w.batch * pairs
+    plan = plan_cost(ca, torch, desc, w, lambda: ca.ring_attn_fwd(desc, q, k, v, w.cu_seqlens, out, lse, ws))
     for _ in range(warmup):
         ca.ring_attn_fwd(desc, q, k, v, w.cu_seqlens, out, lse, ws)
     torch.cuda.synchronize()
@@ -217,7 +314,8 @@ def time_forward(ca, torch, synth, name, steps, warmup):
     return {"workload": f"{name}: {synth.LAYOUT_NAMES[w.layout]} causal fwd rank share, "
                         f"N {w.seqlen}, D {w.world}, rank {w.rank}, {w.heads_q}/{w.heads_kv} heads, "
                         f"d {w.head_dim}", "fwd_tflop": flops / 1e12, "ms": ms, "TFLOP/s": tf,
-            "frac_peak": tf / PEAK_BF16_TFLOPS, "steps": steps}
+            "frac_peak": tf / PEAK_BF16_TFLOPS, "steps": steps,
+            "plan": plan}
 
 
 # Algorithmic flops per visible (query, key) pair and query head, per kernel.
@@ -304,6 +402,8 @@ def main():
                     help="skip the forward timing of the other bf16 configurations")
     ap.add_argument("--fwd-only", action="store_true",
                     help="time the forward alone (drop the backward of the workload)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the MFMA-only and copy-bandwidth measurements")
     ap.add_argument("--sustain", choices=("fwd", "bwd", "step"),
                     help="only run that pass of the workload back to back for --seconds "
                          "(a steady load for reading power and clocks from outside)")
@@ -365,6 +465,7 @@ def main():
                 (dq, dk, dv) if w.with_grad else None)
         return
 
+    plan = plan_cost(ca, torch, desc, w, step)
     for i in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -441,10 +542,12 @@ def main():
                    "bwd_tflop": bwd_flops / 1e12},
         "roofline": roofline,
         "kernels": kern,
+        "plan": plan,
         "mfma_frac_whole_step": value / PEAK_BF16_TFLOPS,
     }
     if not args.no_merge:
         res["merge"] = merge_bandwidth(ca, torch)
+        res["merge"]["rotating_basic_s4096_shape"] = merge_rotating(ca, torch)
     if not args.no_other and args.workload == "basic_s8192":
         del t, out, lse
         if w.with_grad:
@@ -454,6 +557,9 @@ def main():
         for name in OTHER_FWD:
             log(f"forward of {name} ...")
             res["other_workloads"][name] = time_forward(ca, torch, synth, name, 10, 3)
+    if not args.no_peaks:
+        log("measuring the MFMA-only and copy peaks ...")
+        res["measured_peaks"] = measured_peaks(torch)
     if pool is not None:
         log("timing the oracle on the host ...")
         res["cpu_baseline"] = cpu_baseline(w, g, args.cpu_budget, pool, workers)

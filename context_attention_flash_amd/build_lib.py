@@ -1,4 +1,5 @@
-"""Builds libringattn.so (HIP kernels for gfx950 + the host C ABI) in-tree.
+"""Builds libringattn.so (HIP kernels for gfx950 + the host C ABI) in-tree,
+and libraprobe.so (the MFMA-only peak probe that bench.py measures with).
 
 Usage: python -m context_attention_flash_amd.build_lib [-v]
 """
@@ -14,6 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libringattn.so")
+PROBE_LIB = os.path.join(PKG, "libraprobe.so")
+PROBE_SOURCES = ["peak_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["abi.cpp", "planner.cpp", "fwd_bf16.hip", "fwd_f32.hip", "elementwise.hip",
@@ -44,11 +47,8 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> str:
+    tmp = out + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -59,8 +59,17 @@ def build(verbose: bool = False) -> str:
     missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "__device_stub__" in ln]
     if nm.returncode != 0 or missing:
         raise RuntimeError(f"library check failed: {nm.stderr.strip()} undefined kernel stubs {missing}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
+    return _link([objs[s] for s in SOURCES], LIB)
 
 
 if __name__ == "__main__":

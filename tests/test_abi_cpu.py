@@ -32,6 +32,21 @@ def test_exports_every_declared_symbol():
     assert ca.ring_attn_version() == 1
 
 
+def test_peak_probe_library_loads():
+    """bench.py's MFMA-only probe is built beside the library and exports its
+    two calls; its flop count is the kernel's (4 waves x 4 chains x 32x32x16x2
+    per MFMA, the MFMAs per chain rounded up to a multiple of 8)."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "context_attention_flash_amd", "libraprobe.so"))
+    assert hasattr(lib, "ra_probe_mfma")
+    lib.ra_probe_mfma_flops.restype = ctypes.c_double
+    lib.ra_probe_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    assert lib.ra_probe_mfma_flops(2, 8) == 2 * 4 * 8 * 4 * 32768.0
+    assert lib.ra_probe_mfma_flops(1, 9) == 4 * 16 * 4 * 32768.0
+    lib.ra_probe_mfma.restype = ctypes.c_int
+    lib.ra_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    assert lib.ra_probe_mfma(None, 1, 8, None) != 0   # refused before any launch
+
+
 def _cu(layout, N, D, rng, n_docs=5):
     if layout not in synth.VARLEN_LAYOUTS:
         return None
