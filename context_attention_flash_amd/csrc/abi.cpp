@@ -89,17 +89,57 @@ struct Plan {
 // call holds its plan through a shared_ptr, so an eviction (or
 // ring_attn_clear_cache) by another thread frees the plan only after that
 // call has enqueued its kernels; the destructor then waits for the device.
+// Evicted plans are retired and freed in batches of g_plan_limit (or by
+// ring_attn_clear_cache), so that a caller with new document boundaries on
+// every step waits for the device once per batch, not on every new plan.
 std::mutex g_plan_mu;
 std::list<std::pair<std::string, std::shared_ptr<Plan>>> g_plans;   // most recent first
 std::map<std::string, decltype(g_plans)::iterator> g_plan_index;
 int32_t g_plan_limit = 32;
+std::vector<std::shared_ptr<Plan>> g_retired;
 
 void evict_plans_locked(std::vector<std::shared_ptr<Plan>>& dropped) {
     while ((int64_t)g_plans.size() > g_plan_limit) {
-        dropped.push_back(std::move(g_plans.back().second));
+        g_retired.push_back(std::move(g_plans.back().second));
         g_plan_index.erase(g_plans.back().first);
         g_plans.pop_back();
     }
+    if ((int64_t)g_retired.size() >= g_plan_limit) {
+        for (auto& r : g_retired) dropped.push_back(std::move(r));
+        g_retired.clear();
+    }
+}
+
+// Pinned host staging for plan uploads, grown as needed and reused (plans
+// are built under g_plan_mu, one at a time), and a library stream per device
+// that carries the copy: the host waits for the copy alone, not for work
+// queued on the caller's stream.
+struct Uploader {
+    void* stage = nullptr;
+    size_t cap = 0;
+    std::map<int, hipStream_t> streams;
+} g_up;
+
+int upload_plan(int device, void* dst, const void* src, size_t bytes) {
+    if (bytes > g_up.cap) {
+        if (g_up.stage) (void)hipHostFree(g_up.stage);
+        g_up.stage = nullptr;
+        g_up.cap = 0;
+        size_t want = std::max<size_t>(bytes, (size_t)1 << 20);
+        if (hipHostMalloc(&g_up.stage, want, hipHostMallocDefault) != hipSuccess) {
+            g_up.stage = nullptr;
+            return RA_E_HIP;
+        }
+        g_up.cap = want;
+    }
+    hipStream_t& st = g_up.streams[device];
+    if (st == nullptr && hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) {
+        st = nullptr;
+        return RA_E_HIP;
+    }
+    std::memcpy(g_up.stage, src, bytes);
+    if (hipMemcpyAsync(dst, g_up.stage, bytes, hipMemcpyHostToDevice, st) != hipSuccess) return RA_E_HIP;
+    return hipStreamSynchronize(st) == hipSuccess ? RA_OK : RA_E_HIP;
 }
 
 // Host image of a plan before upload: a list of int32 arrays.
@@ -197,8 +237,10 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
     std::vector<std::vector<int32_t>> q_off_h, q_mid_h, q_ent_h;
     std::vector<int32_t> rng_all_h, blk_h;
     int64_t total_pairs = 0;
+    std::vector<int64_t> pq;
+    rank_positions(g, g.r, pq);
     for (int32_t s = 0; s < g.nb; ++s) {
-        step_ranges(g, s, all[s]);
+        step_ranges(g, s, all[s], &pq);
         total_pairs += all[s].pairs;
     }
     std::vector<int8_t> kinds;
@@ -222,8 +264,17 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
         blk_h.push_back(sr.j);
         ix.rng = H.add(std::move(rng));
         std::vector<int32_t> off, mid, ent, order;
-        classify(sr, g.S, g.Skv, FWD_BQ, FWD_BK, kinds);
-        build_lists(kinds, plan->nqt, nkt_f, true, off, mid, ent, order);
+        // the 128-row forward lists serve the fp32 kernel only (the bf16
+        // forward uses the 256-row lists below)
+        if (g.dtype == RA_BF16) {
+            off.clear();
+            mid.clear();
+            ent.clear();
+            order.clear();
+        } else {
+            classify(sr, g.S, g.Skv, FWD_BQ, FWD_BK, kinds);
+            build_lists(kinds, plan->nqt, nkt_f, true, off, mid, ent, order);
+        }
         ix.foff = H.add(std::move(off));
         ix.fmid = H.add(std::move(mid));
         ix.fent = H.add(std::move(ent));
@@ -317,8 +368,7 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
         plan->dbuf = nullptr;
         return RA_E_HIP;
     }
-    if (hipMemcpy(plan->dbuf, img.data(), total, hipMemcpyHostToDevice) != hipSuccess)
-        return RA_E_HIP;
+    if (const int rc = upload_plan(device, plan->dbuf, img.data(), total); rc != RA_OK) return rc;
     auto P = [&](size_t i) { return (const int32_t*)((unsigned char*)plan->dbuf + offs[i]); };
     for (size_t k = 0; k < plan->steps.size(); ++k) {
         DevStep& d = plan->steps[k];
@@ -353,7 +403,9 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
 
 // The cached plan of this geometry on the current device; with build = false
 // a missing plan is RA_E_NO_PLAN instead of being built (no device allocation).
-int get_plan(const Geometry& g, std::shared_ptr<const Plan>* out, bool build = true) {
+// A plan is not built while `stream` is being captured into a graph (the
+// build allocates and copies): RA_E_NO_PLAN then too.
+int get_plan(const Geometry& g, std::shared_ptr<const Plan>* out, bool build, hipStream_t stream) {
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return RA_E_HIP;
     const std::string key = std::to_string(device) + "#" + plan_key(g);
@@ -367,6 +419,9 @@ int get_plan(const Geometry& g, std::shared_ptr<const Plan>* out, bool build = t
             return RA_OK;
         }
         if (!build) return RA_E_NO_PLAN;
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return RA_E_HIP;
+        if (cap != hipStreamCaptureStatusNone) return RA_E_NO_PLAN;
         std::unique_ptr<Plan> p;
         const int rc = build_plan(g, device, p);
         if (rc != RA_OK) return rc;
@@ -496,8 +551,10 @@ int64_t host_max_ne(const Geometry& g) {
     int64_t best = 0;
     StepRanges sr;
     std::vector<int8_t> kinds;
+    std::vector<int64_t> pq;
+    rank_positions(g, g.r, pq);
     for (int32_t s = 0; s < g.nb; ++s) {
-        step_ranges(g, s, sr);
+        step_ranges(g, s, sr, &pq);
         if (sr.pairs == 0) continue;
         classify(sr, g.S, g.Skv, BWD_BQ, BWD_BK, kinds);
         const int64_t ne = std::count_if(kinds.begin(), kinds.end(),
@@ -548,8 +605,8 @@ const char* ring_attn_strerror(int code) {
         case RA_E_HIP: return "the HIP runtime reported an error";
         case RA_E_ARG: return "an argument is out of range (or a NaN / infinite softmax scale)";
         case RA_E_NO_PLAN:
-            return "no cached plan for this shape: an ordinary call builds it (the no-allocation "
-                   "entry point only uses plans that exist)";
+            return "no cached plan for this shape: an ordinary call outside graph capture builds it "
+                   "(the no-allocation entry point and captured calls only use plans that exist)";
         case RA_E_SCRATCH:
             return "the call needs more scratch than the no-allocation entry point's static array";
         default: return "unknown error code";
@@ -616,8 +673,10 @@ int ring_attn_schedule(const ring_attn_desc* desc, const int32_t* cu, int32_t* b
         if (rc != RA_OK) return rc;
         if (!block_out || !pairs_out || !n_steps) return RA_E_NULL;
         StepRanges sr;
+        std::vector<int64_t> pq;
+        rank_positions(g, g.r, pq);
         for (int32_t s = 0; s < g.nb; ++s) {
-            step_ranges(g, s, sr);
+            step_ranges(g, s, sr, &pq);
             block_out[s] = sr.j;
             pairs_out[s] = sr.pairs;
         }
@@ -670,7 +729,7 @@ int ring_attn_fwd(const ring_attn_desc* desc, const void* q, const void* k, cons
         const int64_t need = fwd_workspace(g);
         if (need > 0 && (!workspace || (int64_t)workspace_bytes < need)) return RA_E_WORKSPACE;
         std::shared_ptr<const Plan> plan;
-        if ((rc = get_plan(g, &plan)) != RA_OK) return rc;
+        if ((rc = get_plan(g, &plan, true, (hipStream_t)stream)) != RA_OK) return rc;
         hipStream_t s = (hipStream_t)stream;
 
         const int64_t eb = elem_bytes(g);
@@ -781,7 +840,7 @@ int bwd_impl(const ring_attn_desc* desc, const void* dout, const void* q, const 
         const int64_t need = bwd_workspace(g);
         if (!workspace || (int64_t)workspace_bytes < need) return RA_E_WORKSPACE;
         std::shared_ptr<const Plan> plan;
-        if ((rc = get_plan(g, &plan, build_plan)) != RA_OK) return rc;
+        if ((rc = get_plan(g, &plan, build_plan, (hipStream_t)stream)) != RA_OK) return rc;
         hipStream_t s = (hipStream_t)stream;
         float* lse2 = (float*)workspace;
         float* ndelta = (float*)((unsigned char*)workspace + bwd_row_bytes(g));
@@ -940,9 +999,11 @@ int ring_attn_timing_read(const char* name, int64_t* launches, double* total_ms)
 
 int ring_attn_clear_cache(void) {
     decltype(g_plans) dropped;
+    std::vector<std::shared_ptr<Plan>> retired;
     {
         std::lock_guard<std::mutex> lock(g_plan_mu);
         dropped.swap(g_plans);
+        retired.swap(g_retired);
         g_plan_index.clear();
     }
     return RA_OK;   // plans still held by a call in flight are freed when it returns

@@ -126,28 +126,52 @@ void block_positions(const Geometry& g, int32_t block, std::vector<int64_t>& out
     rank_positions(g, block, out);
 }
 
-void step_ranges(const Geometry& g, int32_t s, StepRanges& out) {
+void step_ranges(const Geometry& g, int32_t s, StepRanges& out, const std::vector<int64_t>* pq_in) {
     out.s = s;
     out.j = g.layout == RA_LLAMA3 ? 0 : (int32_t)(((g.r - s) % g.D + g.D) % g.D);
-    std::vector<int64_t> pq, pk;
-    rank_positions(g, g.r, pq);
+    std::vector<int64_t> pq_own, pk;
+    if (pq_in == nullptr) rank_positions(g, g.r, pq_own);
+    const std::vector<int64_t>& pq = pq_in != nullptr ? *pq_in : pq_own;
     block_positions(g, out.j, pk);
     out.a.resize(g.S);
     out.b.resize(g.S);
     out.pairs = 0;
+    // The visible global positions of row t form the interval [lo, hi]: its
+    // document (varlen), up to t (causal), inside the window.  Both ends only
+    // grow with t, and every layout's rows and blocks hold ascending
+    // positions, so the interval's first and last key index are found by two
+    // cursors that only move forward (binary search otherwise).
+    const bool sweep = std::is_sorted(pq.begin(), pq.end()) && std::is_sorted(pk.begin(), pk.end());
+    const int64_t nk = (int64_t)pk.size();
+    int64_t ia = 0, ib = 0;   // first key with position >= lo, first with position > hi
+    size_t doc = 0;           // varlen: document of the current row (sweep)
     for (int64_t i = 0; i < g.S; ++i) {
         const int64_t t = pq[i];
         int64_t lo = 0, hi = g.N - 1;  // visible global positions [lo, hi]
         if (g.varlen) {
-            const auto it = std::upper_bound(g.cu.begin(), g.cu.end(), t);
-            lo = *(it - 1);
-            hi = *it - 1;
+            if (sweep) {
+                while (doc + 2 < g.cu.size() && g.cu[doc + 1] <= t) ++doc;
+                lo = g.cu[doc];
+                hi = g.cu[doc + 1] - 1;
+            } else {
+                const auto it = std::upper_bound(g.cu.begin(), g.cu.end(), t);
+                lo = *(it - 1);
+                hi = *it - 1;
+            }
         }
         if (g.causal) hi = std::min(hi, t);
         if (g.win_left >= 0) lo = std::max(lo, t - g.win_left);
         if (g.win_right >= 0) hi = std::min(hi, t + g.win_right);
-        const int64_t a = std::lower_bound(pk.begin(), pk.end(), lo) - pk.begin();
-        const int64_t b = std::upper_bound(pk.begin(), pk.end(), hi) - pk.begin();
+        int64_t a, b;
+        if (sweep) {
+            while (ia < nk && pk[ia] < lo) ++ia;
+            while (ib < nk && pk[ib] <= hi) ++ib;
+            a = ia;
+            b = ib;
+        } else {
+            a = std::lower_bound(pk.begin(), pk.end(), lo) - pk.begin();
+            b = std::upper_bound(pk.begin(), pk.end(), hi) - pk.begin();
+        }
         out.a[i] = (int32_t)a;
         out.b[i] = (int32_t)std::max(a, b);
         out.pairs += std::max<int64_t>(0, b - a);
@@ -185,10 +209,11 @@ void classify(const StepRanges& sr, int64_t S, int64_t Skv, int32_t bq, int32_t 
 }
 
 std::string plan_key(const Geometry& g) {
-    // The schedule and tile lists depend only on the token geometry.
+    // The schedule and tile lists depend on the token geometry; which lists a
+    // plan holds also depends on the input type.
     std::ostringstream o;
     o << g.N << ',' << g.D << ',' << g.r << ',' << g.causal << ',' << g.layout << ','
-      << g.win_left << ',' << g.win_right;
+      << g.win_left << ',' << g.win_right << ',' << g.dtype;
     if (g.varlen) {
         o << '|';
         for (int64_t c : g.cu) o << c << ',';

@@ -50,7 +50,10 @@ struct StepRanges {
     std::vector<int32_t> a, b;
 };
 
-void step_ranges(const Geometry& g, int32_t s, StepRanges& out);
+// pq: the rank's row positions (rank_positions(g, g.r)) when the caller has
+// them already, else computed here.
+void step_ranges(const Geometry& g, int32_t s, StepRanges& out,
+                 const std::vector<int64_t>* pq = nullptr);
 
 enum TileKind : int8_t { TILE_EMPTY = 0, TILE_PARTIAL = 1, TILE_FULL = 2 };
 

@@ -28,14 +28,18 @@
  *   - Host pointers are read during the call only.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *     device work is enqueued on it; calls return without synchronising.
- *   - The first call for a shape builds its plan (host work, one hipMalloc
- *     and a synchronous upload); later calls for that shape enqueue kernels
- *     only (no allocation, no memset, no copy), so they can be captured into
- *     a HIP graph and replayed.  The plans live in a cache of at most
- *     ring_attn_plan_cache_limit() plans (32 by default), least recently used
- *     first out; every packed-layout cu_seqlens is its own shape.  Evicting a
- *     plan (or ring_attn_clear_cache()) waits for the device and frees its
- *     memory, which invalidates any captured graph that used it.
+ *   - The first call for a shape builds its plan: host work, one hipMalloc
+ *     and an upload that the host waits for (on a stream of the library's
+ *     own, so not behind work queued on `stream`).  Later calls for that shape
+ *     enqueue kernels only (no allocation, no memset, no copy), so they can
+ *     be captured into a HIP graph and replayed; a call made while `stream`
+ *     is being captured never builds a plan (RA_E_NO_PLAN).  The plans live
+ *     in a cache of at most ring_attn_plan_cache_limit() plans (32 by
+ *     default), least recently used first out; every packed-layout
+ *     cu_seqlens is its own shape.  Evicted plans are freed in batches of the
+ *     cache limit (the release waits for the device once per batch), and
+ *     ring_attn_clear_cache() frees them all; either invalidates any captured
+ *     graph that used those plans.
  *   - Return value: 0 on success, a negative RA_E_* code on failure.  All
  *     argument validation happens before any device work is enqueued, so a
  *     failing call leaves every buffer untouched.  Nothing is printed and no
@@ -151,7 +155,9 @@ typedef struct ring_attn_desc {
 #define RA_E_LAYOUT          -9  /* unknown layout, or batch != 1 for varlen   */
 #define RA_E_HIP            -10  /* the HIP runtime reported an error          */
 #define RA_E_ARG            -11  /* another argument out of range              */
-#define RA_E_NO_PLAN        -12  /* ring_attn_bwd_noalloc: shape never planned */
+#define RA_E_NO_PLAN        -12  /* shape never planned, and no plan can be built
+                                   * here (ring_attn_bwd_noalloc, or a call
+                                   * made during graph capture)               */
 #define RA_E_SCRATCH        -13  /* ring_attn_bwd_noalloc: scratch too small   */
 
 /* Shapes (all row-major, last dimension fastest):
@@ -286,17 +292,19 @@ int ring_attn_tile_kinds(const ring_attn_desc* desc, const int32_t* cu_seqlens,
 int ring_attn_timing_enable(int enable);
 int ring_attn_timing_read(const char* name, int64_t* launches, double* total_ms);
 
-/* Free every cached plan (and its device memory on every device), waiting
- * for the device first.  A plan that a call in flight holds is freed when
- * that call returns. */
+/* Free every cached plan and every evicted one not yet released (and their
+ * device memory on every device), waiting for the device first.  A plan that
+ * a call in flight holds is freed when that call returns. */
 int ring_attn_clear_cache(void);
 
 /* Host only.  Sets the most plans the cache keeps (>= 1; RA_E_ARG otherwise),
  * evicting the least recently used ones beyond it; returns the previous
- * limit. */
+ * limit.  Evicted plans wait, up to as many again, for their batched
+ * release. */
 int ring_attn_plan_cache_limit(int32_t max_plans);
 
-/* Host only.  Number of cached plans and the device bytes they hold. */
+/* Host only.  Number of cached plans and the device bytes they hold (evicted
+ * plans awaiting release are not counted). */
 int ring_attn_plan_cache_info(int64_t* n_plans, int64_t* device_bytes);
 
 const char* ring_attn_strerror(int code);
