@@ -466,6 +466,56 @@ def test_hip_graph_capture_and_replay():
     _check_fwd(w, glob, 1, out.float().cpu().numpy(), lse.cpu().numpy())
 
 
+def test_no_plan_is_built_during_capture():
+    """Building a plan allocates and uploads, which a graph cannot hold: a call
+    for a shape that was never planned, made while its stream is captured,
+    returns RA_E_NO_PLAN before enqueuing anything; after an eager call has
+    planned the shape, the same call captures and replays correctly."""
+    w = _small_workload(ca.STRIPE, True, 64, D=4, S=136, B=1, seed=321)
+    glob = synth.draw_global(w)
+    sh = shard(glob, w, 2)
+    desc = ca.desc_from_workload(w, rank=2)
+    q, k, v = (to_dev(sh[n], w.dtype) for n in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    lse = torch.empty(w.batch, w.heads_q, w.shard, device="cuda")
+    ca.ring_attn_clear_cache()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    say("capture: unplanned shape")
+    err = None
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            out.zero_()   # a fill kernel, so that the graph is not empty
+            try:
+                ca.ring_attn_fwd(desc, q, k, v, None, out, lse, stream=s)
+            except ca.RingAttnError as e:
+                err = e
+    torch.cuda.synchronize()
+    assert err is not None and err.code == -12, err
+    n, _ = ca.ring_attn_plan_cache_info()
+    assert n == 0
+    say("capture: after an eager call")
+    ca.ring_attn_fwd(desc, q, k, v, None, out, lse)
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone())
+    g2 = torch.cuda.CUDAGraph()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g2, stream=s):
+            ca.ring_attn_fwd(desc, q, k, v, None, out, lse, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g2.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), rep
+
+
 def test_plan_cache_is_bounded():
     """Packed training sends new document boundaries every step: 200 forward
     calls with distinct cu_seqlens keep at most the cache limit of plans, and
