@@ -410,7 +410,7 @@ def main():
     ap.add_argument("--seconds", type=float, default=20.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one rank's share on ONE GPU; this build has no multi-GPU "
+        print("bench.py measures one rank's share on ONE GPU; this library has no multi-GPU "
               "path (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
