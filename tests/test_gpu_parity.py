@@ -417,6 +417,24 @@ def test_random_configs_fwd_bwd(seed):
             _check_bwd(w, glob, rank, dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
 
 
+@pytest.mark.parametrize("Hq,Hkv,layout", [(8, 1, ca.BASIC), (16, 2, ca.VARLEN_RING),
+                                            (32, 1, ca.ZIGZAG), (12, 4, ca.STRIPE)])
+def test_gqa_large_groups(Hq, Hkv, layout):
+    """Query-head groups larger than the random configurations draw (up to 32
+    q heads on one kv head): the forward reads kv head h * Hkv / Hq, the
+    dK/dV kernel walks every q head of its group, both dQ paths."""
+    w = _small_workload(layout, True, 64, D=2, S=264, B=1, Hq=Hq, Hkv=Hkv, seed=Hq + Hkv,
+                        with_grad=True)
+    glob = synth.draw_global(w)
+    for rank in range(w.world):
+        say(f"gqa Hq={Hq} Hkv={Hkv} layout={layout} rank={rank}")
+        _, _, _, out, lse = _run_fwd(w, glob, rank)
+        _check_fwd(w, glob, rank, out, lse)
+        for ds_store in (True, False):
+            dq, dk, dv = _run_bwd(w, glob, rank, ds_store=ds_store)
+            _check_bwd(w, glob, rank, dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
+
+
 def test_hip_graph_capture_and_replay():
     """After a first eager call (which builds the plan), the forward and the
     backward enqueue only kernels: they can be captured into a HIP graph.  The
