@@ -1,7 +1,10 @@
-// Measurement aid (not part of the attention path): a kernel that does
+// Measurement aids (not part of the attention path): a kernel that does
 // nothing but bf16 MFMAs, to measure what the matrix cores of this GPU deliver
-// when they are the only thing running, under the clocks the chip then holds.
-// Built into its own library (libraprobe.so), loaded by bench.py only.
+// when they are the only thing running, under the clocks the chip then holds,
+// and streaming kernels (a copy, and an add that reads two bytes per byte
+// written, as the LSE merge does), to measure what HBM delivers to plain
+// read-and-write kernels.  Built into their own library (libraprobe.so), loaded by bench.py
+// and the tests only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,6 +48,59 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(float* out, int iters) {
     out[blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int STREAM_UNROLL = 8;   // independent 16-byte chunks in flight per thread
+
+template <bool NT>
+__device__ __forceinline__ f32x4_t ld16(const f32x4_t* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void st16(f32x4_t v, f32x4_t* p) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+// Over n 16-byte chunks: dst[i] = a[i] (ADD = false, one byte read per byte
+// written, like a copy) or dst[i] = a[i] + b[i] as four floats (ADD = true,
+// two read per written, like the LSE merge).  Chunk i of a pass goes to
+// thread i % (grid threads), so each wave instruction moves 1 KiB of
+// contiguous memory; every thread keeps STREAM_UNROLL chunks in flight.
+template <bool ADD, bool NT_LD, bool NT_ST>
+__global__ __launch_bounds__(256) void stream_kernel(const f32x4_t* __restrict__ a,
+                                                     const f32x4_t* __restrict__ b,
+                                                     f32x4_t* __restrict__ dst, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + (STREAM_UNROLL - 1) * stride < n; i += STREAM_UNROLL * stride) {
+        f32x4_t v[STREAM_UNROLL];
+#pragma unroll
+        for (int u = 0; u < STREAM_UNROLL; ++u) v[u] = ld16<NT_LD>(a + i + u * stride);
+        if constexpr (ADD) {
+#pragma unroll
+            for (int u = 0; u < STREAM_UNROLL; ++u) v[u] += ld16<NT_LD>(b + i + u * stride);
+        }
+#pragma unroll
+        for (int u = 0; u < STREAM_UNROLL; ++u) st16<NT_ST>(v[u], dst + i + u * stride);
+    }
+    for (; i < n; i += stride) {
+        if constexpr (ADD) dst[i] = a[i] + b[i];
+        else dst[i] = a[i];
+    }
+}
+
+template <bool ADD>
+void launch_stream(int flags, int blocks, hipStream_t s, const f32x4_t* a, const f32x4_t* b,
+                   f32x4_t* d, int64_t n) {
+    switch (flags & 3) {
+        case 0: hipLaunchKernelGGL((stream_kernel<ADD, false, false>), dim3(blocks), dim3(256), 0, s, a, b, d, n); break;
+        case 1: hipLaunchKernelGGL((stream_kernel<ADD, true, false>), dim3(blocks), dim3(256), 0, s, a, b, d, n); break;
+        case 2: hipLaunchKernelGGL((stream_kernel<ADD, false, true>), dim3(blocks), dim3(256), 0, s, a, b, d, n); break;
+        default: hipLaunchKernelGGL((stream_kernel<ADD, true, true>), dim3(blocks), dim3(256), 0, s, a, b, d, n); break;
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -59,6 +115,25 @@ double ra_probe_mfma_flops(int32_t blocks, int32_t iters) {
 int ra_probe_mfma(float* out, int32_t blocks, int32_t iters, hipStream_t stream) {
     if (out == nullptr || blocks <= 0 || iters <= 0) return (int)hipErrorInvalidValue;
     hipLaunchKernelGGL(mfma_peak_kernel, dim3(blocks), dim3(256), 0, stream, out, iters);
+    return (int)hipGetLastError();
+}
+
+// dst = a (b == NULL) or dst = a + b as floats (b != NULL), over `bytes`
+// bytes of device memory (every pointer 16-byte aligned, bytes a multiple of
+// 16, dst overlapping neither input) with `blocks` work-groups of 256 threads
+// on `stream`.  flags bit 0: non-temporal loads, bit 1: non-temporal stores.
+// Returns a hipError_t value.
+int ra_probe_stream(const void* a, const void* b, void* dst, int64_t bytes, int32_t blocks,
+                    int32_t flags, hipStream_t stream) {
+    if (a == nullptr || dst == nullptr || bytes < 0 || bytes % 16 != 0 || blocks <= 0 ||
+        flags < 0 || flags > 3 || ((uintptr_t)a | (uintptr_t)b | (uintptr_t)dst) % 16 != 0)
+        return (int)hipErrorInvalidValue;
+    if (bytes == 0) return (int)hipSuccess;
+    const int64_t n = bytes / 16;
+    if (b == nullptr)
+        launch_stream<false>(flags, blocks, stream, (const f32x4_t*)a, nullptr, (f32x4_t*)dst, n);
+    else
+        launch_stream<true>(flags, blocks, stream, (const f32x4_t*)a, (const f32x4_t*)b, (f32x4_t*)dst, n);
     return (int)hipGetLastError();
 }
 

@@ -33,9 +33,11 @@ def test_exports_every_declared_symbol():
 
 
 def test_peak_probe_library_loads():
-    """bench.py's MFMA-only probe is built beside the library and exports its
-    two calls; its flop count is the kernel's (4 waves x 4 chains x 32x32x16x2
-    per MFMA, the MFMAs per chain rounded up to a multiple of 8)."""
+    """bench.py's probes are built beside the library and export their calls;
+    the MFMA probe's flop count is the kernel's (4 waves x 4 chains x 32x32x16x2
+    per MFMA, the MFMAs per chain rounded up to a multiple of 8); the streaming
+    probe refuses null or misaligned pointers, sizes that are not a multiple of
+    16 bytes, empty grids and unknown flags."""
     lib = ctypes.CDLL(os.path.join(ROOT, "context_attention_flash_amd", "libraprobe.so"))
     assert hasattr(lib, "ra_probe_mfma")
     lib.ra_probe_mfma_flops.restype = ctypes.c_double
@@ -45,6 +47,15 @@ def test_peak_probe_library_loads():
     lib.ra_probe_mfma.restype = ctypes.c_int
     lib.ra_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     assert lib.ra_probe_mfma(None, 1, 8, None) != 0   # refused before any launch
+    lib.ra_probe_stream.restype = ctypes.c_int
+    lib.ra_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    for a, b, dst, nbytes, blocks, flags in (
+            (None, None, 16, 16, 1, 0), (16, None, None, 16, 1, 0), (16, None, 32, 24, 1, 0),
+            (16, None, 32, 16, 0, 0), (8, None, 32, 16, 1, 0), (16, 40, 32, 16, 1, 0),
+            (16, None, 32, -16, 1, 0), (16, None, 32, 16, 1, 4), (16, None, 32, 16, 1, -1)):
+        assert lib.ra_probe_stream(a, b, dst, nbytes, blocks, flags, None) != 0   # refused, no launch
+    assert lib.ra_probe_stream(16, 48, 32, 0, 1, 3, None) == 0                   # nothing to move
 
 
 def _cu(layout, N, D, rng, n_docs=5):

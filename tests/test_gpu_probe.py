@@ -1,0 +1,41 @@
+"""The measurement probes bench.py uses: the streaming copy and add compute
+exactly what they claim over the bytes they are given (the unrolled passes
+and the tail, every cache policy), so their bandwidths are those of correct
+kernels."""
+import ctypes
+import os
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.gpu
+
+
+def _probe():
+    lib = ctypes.CDLL(os.path.join(ROOT, "context_attention_flash_amd", "libraprobe.so"))
+    lib.ra_probe_stream.restype = ctypes.c_int
+    lib.ra_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    return lib
+
+
+@pytest.mark.parametrize("add", [False, True])
+@pytest.mark.parametrize("flags", [0, 3])
+@pytest.mark.parametrize("chunks, blocks", [(1, 1), (100003, 7), (1 << 22, 2048), (3 * 256 * 8 + 5, 3)])
+def test_stream_is_exact(chunks, blocks, flags, add):
+    import torch
+    lib = _probe()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(chunks + 7 * flags + add)
+    a = torch.randn(chunks * 4, device="cuda", generator=g)
+    b = torch.randn(chunks * 4, device="cuda", generator=g)
+    dst = torch.full((chunks * 4 + 4,), 7.0, device="cuda")   # one guard chunk past the end
+    print("stream", "add" if add else "copy", chunks, "chunks,", blocks, "blocks, flags", flags,
+          flush=True)
+    rc = lib.ra_probe_stream(a.data_ptr(), b.data_ptr() if add else None, dst.data_ptr(), chunks * 16,
+                             blocks, flags, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dst[: chunks * 4], a + b if add else a)
+    assert torch.equal(dst[chunks * 4:], torch.full((4,), 7.0, device="cuda"))
