@@ -220,6 +220,20 @@ def _run_bwd(w, glob, rank, dk=None, dv=None, ds_store=True, ds_kv_heads=None):
     return dq, dk, dv
 
 
+@pytest.mark.parametrize("ds_store", [True, False])
+def test_bwd_is_deterministic(ds_store):
+    """No kernel of the backward uses atomics: two calls on the same inputs
+    give the same bits (dK/dV accumulated into zeroed buffers), for both dQ
+    paths."""
+    w = _small_workload(ca.ZIGZAG, True, 128, D=3, S=600, B=1, seed=11, with_grad=True)
+    glob = synth.draw_global(w)
+    say(f"bwd determinism ds_store={ds_store}")
+    r1 = _run_bwd(w, glob, 1, ds_store=ds_store)
+    r2 = _run_bwd(w, glob, 1, ds_store=ds_store)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("head_dim", [128, 64])
 @pytest.mark.parametrize("causal", [True, False])
