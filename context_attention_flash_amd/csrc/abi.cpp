@@ -10,7 +10,9 @@
 #include <map>
 #include <memory>
 #include <mutex>
+#include <functional>
 #include <numeric>
+#include <queue>
 #include <string>
 #include <tuple>
 #include <vector>
@@ -71,6 +73,10 @@ struct Plan {
     const int32_t* ring_order = nullptr;
     const int32_t* rng_all = nullptr;
     const int32_t* blk = nullptr;
+    // persistent schedule of the one-launch forward (nullptr: one work item per block)
+    const int32_t* pers_off = nullptr;
+    const int32_t* pers_items = nullptr;
+    int32_t pers_blocks = 0;
     void* dbuf = nullptr;
     std::vector<DevStep> steps;
     ~Plan() {
@@ -212,6 +218,63 @@ void build_ds_lists(const std::vector<int32_t>& boff, const std::vector<int32_t>
 
 // Whether the bf16 forward runs as one launch over every ring step: the
 // entries hold the key tile in 20 bits and the step in 11.
+// Persistent schedule of the one-launch forward.  The kernel holds one
+// work-group per CU (8 waves of 256 registers), so a launch of one block per
+// CU keeps every CU busy until its own list ends: no CU waits for the
+// dispatcher between two work items, and no CU idles at the end while others
+// finish long items.  Work item w = (b, q head) * nq + t runs the list of
+// query tile rord[t].  Each XCD (blocks are dealt to the 8 XCDs in turn) keeps
+// the contiguous range of work items it gets without a schedule, so the items
+// of a head still share that XCD's L2; inside the XCD, items go heaviest first
+// to the least loaded of its blocks.  The cost of an item, in tenths of an
+// unmasked key tile: 10 per unmasked tile, 14 per masked one (the masked
+// loop's extra vector work), 120 for the item's prologue and epilogue.
+// Empty output when the items are no more than the blocks.
+void persistent_schedule(int device, int64_t n_bh, const std::vector<int32_t>& off,
+                         const std::vector<int32_t>& mid, const std::vector<int32_t>& order,
+                         std::vector<int32_t>& poff, std::vector<int32_t>& pitems) {
+    poff.clear();
+    pitems.clear();
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
+        return;
+    constexpr int64_t kXcd = 8;
+    const int64_t nq = (int64_t)order.size();
+    const int64_t W = n_bh * nq;
+    const int64_t nblk = cus / kXcd * kXcd;
+    if (nblk < kXcd || W <= nblk) return;
+    const int64_t per_xcd = nblk / kXcd;
+    std::vector<std::vector<int32_t>> lists(nblk);
+    std::vector<std::pair<int64_t, int32_t>> items;
+    for (int64_t x = 0; x < kXcd; ++x) {
+        const int64_t w0 = x * W / kXcd, w1 = (x + 1) * W / kXcd;
+        items.clear();
+        for (int64_t w = w0; w < w1; ++w) {
+            const int32_t qt = order[w % nq];
+            const int64_t cost = 10 * (int64_t)(mid[qt] - off[qt]) +
+                                 14 * (int64_t)(off[qt + 1] - mid[qt]) + 120;
+            items.emplace_back(cost, (int32_t)w);
+        }
+        std::stable_sort(items.begin(), items.end(),
+                         [](const auto& a, const auto& b) { return a.first > b.first; });
+        // least loaded block first; ties to the lower block index
+        using Slot = std::pair<int64_t, int64_t>;   // (load, local block index)
+        std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
+        for (int64_t l = 0; l < per_xcd; ++l) heap.emplace(0, l);
+        for (const auto& [cost, w] : items) {
+            auto [load, l] = heap.top();
+            heap.pop();
+            lists[l * kXcd + x].push_back(w);
+            heap.emplace(load + cost, l);
+        }
+    }
+    poff.assign(nblk + 1, 0);
+    for (int64_t i = 0; i < nblk; ++i) {
+        poff[i + 1] = poff[i] + (int32_t)lists[i].size();
+        pitems.insert(pitems.end(), lists[i].begin(), lists[i].end());
+    }
+}
+
 bool ring_capable(const Geometry& g) {
     return g.dtype == RA_BF16 && g.nb <= RING_MAX_STEPS &&
            (g.Skv + DQ_BK - 1) / DQ_BK <= RING_MAX_KEY_TILES;
@@ -314,7 +377,8 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
     // stay in step through the blocks every query tile sees whole, instead of
     // being offset by the query-tile-dependent part of the diagonal step.
     // The order changes only the rounding of the running sums.
-    size_t i_roff = 0, i_rmid = 0, i_rent = 0, i_rord = 0, i_rng_all = 0, i_blk = 0;
+    size_t i_roff = 0, i_rmid = 0, i_rent = 0, i_rord = 0, i_rng_all = 0, i_blk = 0, i_poff = 0,
+           i_pitems = 0;
     const int64_t n_active = (int64_t)plan->steps.size();
     plan->ring_ok = ring_capable(g) && n_active <= RING_MAX_STEPS;
     if (plan->ring_ok) {
@@ -345,6 +409,13 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
         std::stable_sort(rord.begin(), rord.end(), [&](int32_t x, int32_t y) {
             return roff[x + 1] - roff[x] > roff[y + 1] - roff[y];
         });
+        std::vector<int32_t> poff, pitems;
+        persistent_schedule(device, (int64_t)g.B * g.Hq, roff, rmid, rord, poff, pitems);
+        if (!poff.empty()) {
+            plan->pers_blocks = (int32_t)poff.size() - 1;
+            i_poff = H.add(std::move(poff));
+            i_pitems = H.add(std::move(pitems));
+        }
         i_roff = H.add(std::move(roff));
         i_rmid = H.add(std::move(rmid));
         i_rent = H.add(std::move(rent));
@@ -396,6 +467,10 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
         plan->ring_order = P(i_rord);
         plan->rng_all = P(i_rng_all);
         plan->blk = P(i_blk);
+        if (plan->pers_blocks > 0) {
+            plan->pers_off = P(i_poff);
+            plan->pers_items = P(i_pitems);
+        }
     }
     out = std::move(plan);
     return RA_OK;
@@ -772,6 +847,9 @@ int ring_attn_fwd(const ring_attn_desc* desc, const void* q, const void* k, cons
             a.t_mid = plan->ring_mid;
             a.t_ent = plan->ring_ent;
             a.t_order = plan->ring_order;
+            a.pers_off = plan->pers_off;
+            a.pers_items = plan->pers_items;
+            a.pers_blocks = plan->pers_blocks;
             a.mode = FWD_SOLO;
             return hip_rc(launch_step(a));
         }

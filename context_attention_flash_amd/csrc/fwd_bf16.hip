@@ -80,8 +80,16 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
-    const int work = xcd_work_index(blockIdx.x, gridDim.x);
-    if (work >= p.total_work) return;
+    // The work items of this work-group: one, from the block index; or, with a
+    // persistent schedule (one work-group per CU), the planner's list for this
+    // block, walked in order.
+    const bool persistent = RING && p.pers_off != nullptr;
+    const int it0 = persistent ? as_const(p.pers_off)[blockIdx.x] : 0;
+    const int it1 = persistent ? as_const(p.pers_off)[blockIdx.x + 1] : 1;
+    for (int it = it0; it < it1; ++it) {
+    const int work = persistent ? as_const(p.pers_items)[it] : xcd_work_index(blockIdx.x, gridDim.x);
+    if (work >= p.total_work) break;
+    if (it > it0) __syncthreads();  // the previous item's epilogue is done with the stages
     const int t = work % p.nqt, bh = work / p.nqt;
     const int h = bh % p.Hq, b = bh / p.Hq;
     const int qt = as_const(p.t_order)[t];
@@ -387,7 +395,7 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
                 *ptr = o;
             }
         if (valid && g == 0) p.lse[lse_idx] = L_out;
-        return;
+        continue;
     }
     if (mode == FWD_PARTIAL) {
         if (valid) {
@@ -402,7 +410,7 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
                 }
             if (g == 0) p.lse_part[lse_idx] = Lj;
         }
-        return;
+        continue;
     }
 
     // FWD_LAST / FWD_SOLO: final bf16 output through LDS for coalesced rows.
@@ -432,6 +440,7 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
         if (iqr < p.S)
             *(u32x4_t*)((uint16_t*)p.out + ((int64_t)(b * p.S + iqr) * p.Hq + h) * DH + ch * 8) = val;
     }
+    }  // work items
 }
 
 template __global__ void fwd_step_bf16_kernel<128, false>(FwdArgs);
@@ -440,7 +449,7 @@ template __global__ void fwd_step_bf16_kernel<64, false>(FwdArgs);
 template __global__ void fwd_step_bf16_kernel<64, true>(FwdArgs);
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, hipStream_t s) {
-    const int grid = (a.total_work + 7) / 8 * 8;
+    const int grid = a.ring && a.pers_off ? a.pers_blocks : (a.total_work + 7) / 8 * 8;
     if (grid == 0) return hipSuccess;
     if (head_dim == 128 && a.ring)
         hipLaunchKernelGGL((fwd_step_bf16_kernel<128, true>), dim3(grid), dim3(512), 0, s, a);

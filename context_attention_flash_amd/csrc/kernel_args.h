@@ -56,6 +56,12 @@ struct FwdArgs {
     int32_t mode;
     int32_t total_work;     // B * Hq * nqt
     float scale_log2;       // softmax scale * log2(e)
+    // Persistent schedule (ring launch only; NULL: one work item per block):
+    // block i walks work items pers_items[pers_off[i] .. pers_off[i + 1]),
+    // and the launch has pers_blocks blocks.
+    const int32_t* pers_off;
+    const int32_t* pers_items;
+    int32_t pers_blocks;
 };
 
 struct BwdArgs {

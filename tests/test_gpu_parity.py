@@ -449,6 +449,23 @@ def test_gqa_large_groups(Hq, Hkv, layout):
             _check_bwd(w, glob, rank, dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
 
 
+@pytest.mark.parametrize("layout,B,head_dim,S", [(ca.ZIGZAG, 2, 64, 1250), (ca.LLAMA3, 1, 128, 2300),
+                                                 (ca.BASIC, 2, 128, 1100)])
+def test_fwd_persistent_schedule(layout, B, head_dim, S):
+    """More work items (batch x q heads x 256-row query tiles) than CUs: the
+    one-launch forward runs one work-group per CU, each walking the planner's
+    list of items (lists of unequal length, ragged last tile), and must give
+    the oracle's result on every row."""
+    w = _small_workload(layout, True, head_dim, D=2, S=S, B=B, Hq=32, Hkv=8, seed=S + layout)
+    n_items = w.batch * w.heads_q * -(-S // 256)
+    assert n_items > torch.cuda.get_device_properties(0).multi_processor_count
+    glob = synth.draw_global(w)
+    for rank in range(w.world):
+        say(f"persistent forward layout={layout} B={w.batch} d={head_dim} S={S} rank={rank}")
+        _, _, _, out, lse = _run_fwd(w, glob, rank)
+        _check_fwd(w, glob, rank, out, lse)
+
+
 def test_hip_graph_capture_and_replay():
     """After a first eager call (which builds the plan), the forward and the
     backward enqueue only kernels: they can be captured into a HIP graph.  The
