@@ -53,6 +53,7 @@ _DP = ctypes.POINTER(RingAttnDesc)
 _SIGS = {
     "ring_attn_workspace_bytes": (ctypes.c_int64, [_DP, ctypes.c_int]),
     "ring_attn_bwd_ds_bytes": (ctypes.c_int64, [_DP, _P]),
+    "ring_attn_fwd_split_bytes": (ctypes.c_int64, [_DP]),
     "ring_attn_fwd": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "ring_attn_bwd": (ctypes.c_int, [_DP, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                      ctypes.c_size_t, _P]),
@@ -143,6 +144,15 @@ def ring_attn_workspace_bytes(desc: RingAttnDesc, is_bwd: bool) -> int:
     n = lib().ring_attn_workspace_bytes(ctypes.byref(desc), int(is_bwd))
     if n < 0:
         raise RingAttnError(int(n), "ring_attn_workspace_bytes")
+    return int(n)
+
+
+def ring_attn_fwd_split_bytes(desc: RingAttnDesc) -> int:
+    """Extra forward workspace that lets long query-tile lists be split
+    across CUs (0 when the descriptor's path never splits)."""
+    n = lib().ring_attn_fwd_split_bytes(ctypes.byref(desc))
+    if n < 0:
+        raise RingAttnError(int(n), "ring_attn_fwd_split_bytes")
     return int(n)
 
 
@@ -246,11 +256,14 @@ def _elem_dtype(desc):
 
 def alloc_workspace(desc: RingAttnDesc, is_bwd: bool, device="cuda", cu_seqlens=None,
                     ds_store: bool = True):
-    """Workspace for the forward or the backward; with ``ds_store`` the
-    backward one includes the dS tile store, whole or (beyond DS_STORE_LIMIT)
-    for as many kv heads at a time as fit the limit."""
+    """Workspace for the forward or the backward.  The forward one includes
+    the part buffer that lets long query-tile lists be split across CUs; with
+    ``ds_store`` the backward one includes the dS tile store, whole or (beyond
+    DS_STORE_LIMIT) for as many kv heads at a time as fit the limit."""
     torch = _torch()
     n = ring_attn_workspace_bytes(desc, is_bwd)
+    if not is_bwd:
+        n += ring_attn_fwd_split_bytes(desc)
     if is_bwd and ds_store:
         full = ring_attn_bwd_ds_bytes(desc, cu_seqlens)
         per_kv_head = -(-full // desc.heads_kv)
@@ -272,12 +285,12 @@ def ring_attn_fwd(desc: RingAttnDesc, q, k, v, cu_seqlens=None, out=None, lse=No
         out = torch.empty(sh["q"], dtype=dt, device=q.device)
     if lse is None:
         lse = torch.empty(sh["lse"], dtype=torch.float32, device=q.device)
+    args = [_expect(q, sh["q"], dt, "q"), _expect(k, sh["kv"], dt, "k"), _expect(v, sh["kv"], dt, "v"),
+            _expect(out, sh["q"], dt, "out"), _expect(lse, sh["lse"], torch.float32, "lse")]
     if workspace is None:
         workspace = alloc_workspace(desc, False, q.device)
-    args = [_expect(q, sh["q"], dt, "q"), _expect(k, sh["kv"], dt, "k"), _expect(v, sh["kv"], dt, "v")]
     keep, cu = _cu_arg(cu_seqlens)
-    rc = lib().ring_attn_fwd(ctypes.byref(desc), *args, cu, _expect(out, sh["q"], dt, "out"),
-                             _expect(lse, sh["lse"], torch.float32, "lse"),
+    rc = lib().ring_attn_fwd(ctypes.byref(desc), *args[:3], cu, *args[3:],
                              ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                              _stream_ptr(stream))
     _check(rc, "ring_attn_fwd")

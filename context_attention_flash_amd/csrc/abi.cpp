@@ -73,10 +73,17 @@ struct Plan {
     const int32_t* ring_order = nullptr;
     const int32_t* rng_all = nullptr;
     const int32_t* blk = nullptr;
-    // persistent schedule of the one-launch forward (nullptr: one work item per block)
+    // persistent schedules of the one-launch forward (nullptr: one work item
+    // per block): whole lists, and (when a list is split) with parts
     const int32_t* pers_off = nullptr;
     const int32_t* pers_items = nullptr;
     int32_t pers_blocks = 0;
+    const int32_t* split_off = nullptr;
+    const int32_t* split_items = nullptr;
+    const int32_t* split_merge = nullptr;
+    int32_t split_lists = 0;      // lists that are split (part-merge work-groups)
+    int32_t split_slots = 0;      // part slots (parts of all split lists)
+    int64_t split_bytes = 0;      // part buffer the split schedule needs (0: none)
     void* dbuf = nullptr;
     std::vector<DevStep> steps;
     ~Plan() {
@@ -223,56 +230,139 @@ void build_ds_lists(const std::vector<int32_t>& boff, const std::vector<int32_t>
 // CU keeps every CU busy until its own list ends: no CU waits for the
 // dispatcher between two work items, and no CU idles at the end while others
 // finish long items.  Work item w = (b, q head) * nq + t runs the list of
-// query tile rord[t].  Each XCD (blocks are dealt to the 8 XCDs in turn) keeps
-// the contiguous range of work items it gets without a schedule, so the items
-// of a head still share that XCD's L2; inside the XCD, items go heaviest first
-// to the least loaded of its blocks.  The cost of an item, in tenths of an
-// unmasked key tile: 10 per unmasked tile, 14 per masked one (the masked
-// loop's extra vector work), 120 for the item's prologue and epilogue.
-// Empty output when the items are no more than the blocks.
-void persistent_schedule(int device, int64_t n_bh, const std::vector<int32_t>& off,
-                         const std::vector<int32_t>& mid, const std::vector<int32_t>& order,
-                         std::vector<int32_t>& poff, std::vector<int32_t>& pitems) {
-    poff.clear();
-    pitems.clear();
+// query tile order[t].  Each XCD (blocks are dealt to the 8 XCDs in turn)
+// keeps the contiguous range of work items it gets without a schedule, so the
+// items of a head still share that XCD's L2; inside the XCD, items go
+// heaviest first to the least loaded of its blocks.  The cost of a list, in
+// tenths of an unmasked key tile: 10 per unmasked tile, 14 per masked one,
+// 120 for a work item's prologue and epilogue (measured: 3024 and 4411 cycles
+// per tile, 13.2k per item).
+//
+// With `split`, a list that costs more than a third of its XCD's mean block
+// load is cut into parts of about equal cost (at most 8, at most one per
+// entry); each part runs as an item of its own and writes its normalised
+// partial to a part slot, and the part-merge kernel folds the parts.  Whole
+// items alone cannot balance the blocks when an item is a large fraction of a
+// block's load (few items per CU of very different lengths).  The parts never
+// outnumber the blocks (the threshold is raised until they fit), which bounds
+// the part buffer.
+struct PersSchedule {
+    std::vector<int32_t> off;     // [blocks + 1]
+    std::vector<int32_t> items;   // 4 per item: work, first entry, end entry, part slot (-1)
+    std::vector<int32_t> merge;   // 3 per split list: work, first slot, parts
+    int32_t slots = 0;
+    int64_t makespan = 0;         // largest block load (cost units)
+};
+
+int64_t persistent_blocks(int device) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
-        return;
-    constexpr int64_t kXcd = 8;
+        return 0;
+    return cus / 8 * 8;
+}
+
+void persistent_schedule(int device, int64_t n_bh, const std::vector<int32_t>& off,
+                         const std::vector<int32_t>& mid, const std::vector<int32_t>& order,
+                         bool split, PersSchedule& out) {
+    out = PersSchedule{};
+    constexpr int64_t kXcd = 8, kMaxParts = 8, kTile = 10, kMasked = 14, kItem = 120;
+    const int64_t nblk = persistent_blocks(device);
     const int64_t nq = (int64_t)order.size();
     const int64_t W = n_bh * nq;
-    const int64_t nblk = cus / kXcd * kXcd;
     if (nblk < kXcd || W <= nblk) return;
     const int64_t per_xcd = nblk / kXcd;
+    auto nfull = [&](int64_t w) { const int32_t q = order[w % nq]; return (int64_t)(mid[q] - off[q]); };
+    auto nall = [&](int64_t w) { const int32_t q = order[w % nq]; return (int64_t)(off[q + 1] - off[q]); };
+    auto cost_of = [&](int64_t w, int64_t a, int64_t b) {   // entries [a, b) of w's list
+        const int64_t f = nfull(w);
+        const int64_t full = std::max<int64_t>(0, std::min(b, f) - a);
+        return kTile * full + kMasked * (b - a - full) + kItem;
+    };
+    // the threshold of each XCD: a third of its mean block load, raised until
+    // the parts fit the part slots
+    std::vector<int64_t> thresh(kXcd, INT64_MAX);
+    auto parts_of = [&](int64_t w, int64_t T) {
+        const int64_t c = cost_of(w, 0, nall(w));
+        if (c <= T || nall(w) < 2) return (int64_t)1;
+        return std::min({(c + T - 1) / T, kMaxParts, nall(w)});
+    };
+    if (split) {
+        int64_t used = 0;
+        for (int64_t x = 0; x < kXcd; ++x) {
+            const int64_t w0 = x * W / kXcd, w1 = (x + 1) * W / kXcd;
+            int64_t total = 0;
+            for (int64_t w = w0; w < w1; ++w) total += cost_of(w, 0, nall(w));
+            thresh[x] = std::max<int64_t>(1, total / per_xcd / 3);
+        }
+        for (;;) {
+            used = 0;
+            for (int64_t x = 0; x < kXcd; ++x)
+                for (int64_t w = x * W / kXcd; w < (x + 1) * W / kXcd; ++w) {
+                    const int64_t k = parts_of(w, thresh[x]);
+                    if (k > 1) used += k;
+                }
+            if (used <= nblk) break;
+            for (auto& t : thresh) t = t + t / 4 + 1;
+        }
+    }
+    struct Piece { int64_t cost; int32_t w, a, b, slot; };
     std::vector<std::vector<int32_t>> lists(nblk);
-    std::vector<std::pair<int64_t, int32_t>> items;
+    std::vector<Piece> pieces;
     for (int64_t x = 0; x < kXcd; ++x) {
         const int64_t w0 = x * W / kXcd, w1 = (x + 1) * W / kXcd;
-        items.clear();
+        pieces.clear();
         for (int64_t w = w0; w < w1; ++w) {
-            const int32_t qt = order[w % nq];
-            const int64_t cost = 10 * (int64_t)(mid[qt] - off[qt]) +
-                                 14 * (int64_t)(off[qt + 1] - mid[qt]) + 120;
-            items.emplace_back(cost, (int32_t)w);
+            const int64_t n = nall(w);
+            const int64_t k = split ? parts_of(w, thresh[x]) : 1;
+            if (k == 1) {
+                pieces.push_back({cost_of(w, 0, n), (int32_t)w, 0, (int32_t)n, -1});
+                continue;
+            }
+            // cut the entries where the running cost passes j/k of the list's
+            const int64_t f = nfull(w);
+            const int64_t tiles = kTile * std::min(f, n) + kMasked * (n - std::min(f, n));
+            out.merge.insert(out.merge.end(), {(int32_t)w, out.slots, (int32_t)k});
+            int64_t a = 0, acc = 0, e = 0;
+            for (int64_t j = 1; j <= k; ++j) {
+                int64_t b = n;
+                if (j < k) {
+                    const int64_t goal = tiles * j / k;
+                    while (e < n && acc < goal) acc += e++ < f ? kTile : kMasked;
+                    b = std::max(e, a + 1);
+                    b = std::min(b, n - (k - j));   // every later part keeps one entry
+                    e = b;
+                    acc = kTile * std::min(b, f) + kMasked * (b - std::min(b, f));
+                }
+                pieces.push_back({cost_of(w, a, b), (int32_t)w, (int32_t)a, (int32_t)b, out.slots++});
+                a = b;
+            }
         }
-        std::stable_sort(items.begin(), items.end(),
-                         [](const auto& a, const auto& b) { return a.first > b.first; });
+        std::stable_sort(pieces.begin(), pieces.end(),
+                         [](const Piece& p, const Piece& q) { return p.cost > q.cost; });
         // least loaded block first; ties to the lower block index
         using Slot = std::pair<int64_t, int64_t>;   // (load, local block index)
         std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
         for (int64_t l = 0; l < per_xcd; ++l) heap.emplace(0, l);
-        for (const auto& [cost, w] : items) {
+        for (const Piece& pc : pieces) {
             auto [load, l] = heap.top();
             heap.pop();
-            lists[l * kXcd + x].push_back(w);
-            heap.emplace(load + cost, l);
+            auto& L = lists[l * kXcd + x];
+            L.insert(L.end(), {pc.w, pc.a, pc.b, pc.slot});
+            heap.emplace(load + pc.cost, l);
+            out.makespan = std::max(out.makespan, load + pc.cost);
         }
     }
-    poff.assign(nblk + 1, 0);
+    out.off.assign(nblk + 1, 0);
     for (int64_t i = 0; i < nblk; ++i) {
-        poff[i + 1] = poff[i] + (int32_t)lists[i].size();
-        pitems.insert(pitems.end(), lists[i].begin(), lists[i].end());
+        out.off[i + 1] = out.off[i] + (int32_t)(lists[i].size() / 4);
+        out.items.insert(out.items.end(), lists[i].begin(), lists[i].end());
     }
+}
+
+// Bytes of the part buffer of a split schedule with `slots` part slots:
+// partial outputs [slots][256 rows][d] fp32, then lse [slots][256 rows].
+int64_t part_bytes(int64_t slots, int64_t d) {
+    return round_up(slots * DQ_BQ * d * 4, 256) + round_up(slots * DQ_BQ * 4, 256);
 }
 
 bool ring_capable(const Geometry& g) {
@@ -378,7 +468,7 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
     // being offset by the query-tile-dependent part of the diagonal step.
     // The order changes only the rounding of the running sums.
     size_t i_roff = 0, i_rmid = 0, i_rent = 0, i_rord = 0, i_rng_all = 0, i_blk = 0, i_poff = 0,
-           i_pitems = 0;
+           i_pitems = 0, i_soff = 0, i_sitems = 0, i_smerge = 0;
     const int64_t n_active = (int64_t)plan->steps.size();
     plan->ring_ok = ring_capable(g) && n_active <= RING_MAX_STEPS;
     if (plan->ring_ok) {
@@ -409,12 +499,23 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
         std::stable_sort(rord.begin(), rord.end(), [&](int32_t x, int32_t y) {
             return roff[x + 1] - roff[x] > roff[y + 1] - roff[y];
         });
-        std::vector<int32_t> poff, pitems;
-        persistent_schedule(device, (int64_t)g.B * g.Hq, roff, rmid, rord, poff, pitems);
-        if (!poff.empty()) {
-            plan->pers_blocks = (int32_t)poff.size() - 1;
-            i_poff = H.add(std::move(poff));
-            i_pitems = H.add(std::move(pitems));
+        PersSchedule plain, cut;
+        persistent_schedule(device, (int64_t)g.B * g.Hq, roff, rmid, rord, false, plain);
+        if (!plain.off.empty()) {
+            plan->pers_blocks = (int32_t)plain.off.size() - 1;
+            i_poff = H.add(std::move(plain.off));
+            i_pitems = H.add(std::move(plain.items));
+            persistent_schedule(device, (int64_t)g.B * g.Hq, roff, rmid, rord, true, cut);
+            // split only where the cut shortens the busiest block by more than
+            // the part merge costs (about 12 us, some 70 cost units)
+            if (cut.slots > 0 && cut.makespan + 70 < plain.makespan * 99 / 100) {
+                plan->split_lists = (int32_t)cut.merge.size() / 3;
+                plan->split_slots = cut.slots;
+                plan->split_bytes = part_bytes(cut.slots, g.d);
+                i_soff = H.add(std::move(cut.off));
+                i_sitems = H.add(std::move(cut.items));
+                i_smerge = H.add(std::move(cut.merge));
+            }
         }
         i_roff = H.add(std::move(roff));
         i_rmid = H.add(std::move(rmid));
@@ -471,6 +572,11 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
             plan->pers_off = P(i_poff);
             plan->pers_items = P(i_pitems);
         }
+        if (plan->split_lists > 0) {
+            plan->split_off = P(i_soff);
+            plan->split_items = P(i_sitems);
+            plan->split_merge = P(i_smerge);
+        }
     }
     out = std::move(plan);
     return RA_OK;
@@ -514,10 +620,10 @@ int get_plan(const Geometry& g, std::shared_ptr<const Plan>* out, bool build, hi
 
 enum KernelClass {
     KC_FWD = 0, KC_MERGE, KC_FINALIZE, KC_BWD_PRE, KC_BWD, KC_BWD_DQ, KC_BWD_DQ_DS, KC_BWD_POST,
-    KC_COUNT
+    KC_FWD_PART_MERGE, KC_COUNT
 };
 const char* kClassNames[KC_COUNT] = {"fwd_step", "lse_merge", "finalize", "bwd_pre",  "bwd_step",
-                                     "bwd_dq",   "bwd_dq_ds", "bwd_post"};
+                                     "bwd_dq",   "bwd_dq_ds", "bwd_post", "fwd_part_merge"};
 
 struct Timing {
     std::mutex mu;
@@ -706,6 +812,17 @@ int64_t ring_attn_bwd_ds_bytes(const ring_attn_desc* desc, const int32_t* cu) {
     }
 }
 
+int64_t ring_attn_fwd_split_bytes(const ring_attn_desc* desc) {
+    if (!desc) return RA_E_NULL;
+    if (desc->head_dim != 64 && desc->head_dim != 128) return RA_E_UNSUPPORTED;
+    if (desc->dtype != RA_BF16 || desc->merge_mode != RA_MERGE_FUSED) return 0;
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return RA_E_HIP;
+    const int64_t nblk = persistent_blocks(device);
+    if (nblk <= 0) return RA_E_HIP;
+    return part_bytes(nblk, desc->head_dim);
+}
+
 int ring_attn_positions(const ring_attn_desc* desc, const int32_t* cu, int32_t rank,
                         int64_t* pos_out) {
     try {
@@ -851,7 +968,29 @@ int ring_attn_fwd(const ring_attn_desc* desc, const void* q, const void* k, cons
             a.pers_items = plan->pers_items;
             a.pers_blocks = plan->pers_blocks;
             a.mode = FWD_SOLO;
-            return hip_rc(launch_step(a));
+            // the split schedule when the workspace holds its part buffer
+            const bool split = plan->split_lists > 0 && workspace != nullptr &&
+                               (int64_t)workspace_bytes >= plan->split_bytes;
+            if (!split) return hip_rc(launch_step(a));
+            a.pers_off = plan->split_off;
+            a.pers_items = plan->split_items;
+            a.part_o = (float*)workspace;
+            a.part_l = (float*)((unsigned char*)workspace +
+                                round_up((int64_t)plan->split_slots * DQ_BQ * g.d * 4, 256));
+            if ((rc = hip_rc(launch_step(a))) != RA_OK) return rc;
+            PartMergeArgs m{};
+            m.items = plan->split_merge;
+            m.t_order = plan->ring_order;
+            m.part_o = a.part_o;
+            m.part_l = a.part_l;
+            m.out = out;
+            m.lse = lse;
+            m.n_items = plan->split_lists;
+            m.nqt = a.nqt;
+            m.S = a.S;
+            m.Hq = a.Hq;
+            m.d = g.d;
+            return hip_rc(timed(KC_FWD_PART_MERGE, s, [&] { return launch_fwd_part_merge(m, s); }));
         }
         if (g.merge_mode != RA_MERGE_SEPARATE) {   // one launch per step, merge in the epilogue
             a.o_run = (float*)workspace;

@@ -87,7 +87,18 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
     const int it0 = persistent ? as_const(p.pers_off)[blockIdx.x] : 0;
     const int it1 = persistent ? as_const(p.pers_off)[blockIdx.x + 1] : 1;
     for (int it = it0; it < it1; ++it) {
-    const int work = persistent ? as_const(p.pers_items)[it] : xcd_work_index(blockIdx.x, gridDim.x);
+    // item: work index, entries [first, end) of the work's list (relative),
+    // and the part slot (-1: the whole list, whose result is final)
+    int work, e_first = 0, e_end = 0x7fffffff, pslot = -1;
+    if (persistent) {
+        const cint_ptr item = as_const(p.pers_items) + 4 * it;
+        work = item[0];
+        e_first = item[1];
+        e_end = item[2];
+        pslot = item[3];
+    } else {
+        work = xcd_work_index(blockIdx.x, gridDim.x);
+    }
     if (work >= p.total_work) break;
     if (it > it0) __syncthreads();  // the previous item's epilogue is done with the stages
     const int t = work % p.nqt, bh = work / p.nqt;
@@ -95,8 +106,10 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
     const int qt = as_const(p.t_order)[t];
     const int hk = (h * p.Hkv) / p.Hq;
     const cint_ptr ents = as_const(p.t_ent);
-    const int e0 = as_const(p.t_off)[qt], e1 = as_const(p.t_off)[qt + 1];
-    const int m_full = as_const(p.t_mid)[qt];   // FULL tiles in [e0, m_full), PARTIAL after
+    const int l0 = as_const(p.t_off)[qt], l1 = as_const(p.t_off)[qt + 1];
+    const int e0 = l0 + e_first, e1 = l0 + min(l1 - l0, e_end);
+    // FULL tiles in [e0, m_full), PARTIAL after
+    const int m_full = min(max(as_const(p.t_mid)[qt], e0), e1);
 
     const int iq = qt * C::BQ + wave * 32 + l32;  // this lane's query row
     const int iqc = min(iq, p.S - 1);
@@ -368,6 +381,22 @@ __global__ __launch_bounds__(512, 1) void fwd_step_bf16_kernel(FwdArgs p) {
     float w_old = 0.f, w_new = inv, L_out = Lj;
     f32x4_t* orun = (f32x4_t*)p.o_run +
                     (((int64_t)b * p.Hq + h) * (p.S_pad / 32) + (qt * (C::BQ / 32) + wave)) * (8 * DH) + lane;
+    if (pslot >= 0) {
+        // a part of a split list: its normalised partial and lse, merged with
+        // the other parts' by the part-merge kernel
+        const int row = wave * 32 + l32;
+        float* orow = p.part_o + ((int64_t)pslot * C::BQ + row) * DH;
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                f32x4_t o = {oacc[dt][4 * rg] * inv, oacc[dt][4 * rg + 1] * inv,
+                             oacc[dt][4 * rg + 2] * inv, oacc[dt][4 * rg + 3] * inv};
+                *(f32x4_t*)(orow + 32 * dt + 8 * rg + 4 * g) = o;
+            }
+        if (g == 0) p.part_l[(int64_t)pslot * C::BQ + row] = Lj;
+        continue;
+    }
     const int mode = p.mode;
     if (mode == FWD_MERGE || mode == FWD_LAST) {
         const float Lr = valid ? p.lse[lse_idx] : -INFINITY;
@@ -447,6 +476,54 @@ template __global__ void fwd_step_bf16_kernel<128, false>(FwdArgs);
 template __global__ void fwd_step_bf16_kernel<128, true>(FwdArgs);
 template __global__ void fwd_step_bf16_kernel<64, false>(FwdArgs);
 template __global__ void fwd_step_bf16_kernel<64, true>(FwdArgs);
+
+// Merge of the parts of split forward lists: one work-group per 32 query
+// rows of a split list; each row's parts are folded with the log-sum-exp merge of
+// "Numerically-Stable Output Fusion" (instagit/nanotron page), generalised to
+// any number of parts: L = M + ln sum_k e^{L_k - M}, O = sum_k e^{L_k - L} O_k,
+// M = max_k L_k; a row that sees no key in any part gets O = 0, L = -inf.
+// The result is rounded to bf16 (RNE) and written with its lse, as the
+// one-launch forward writes an unsplit list.
+constexpr int PART_MERGE_ROWS = 32;   // rows of a split list per work-group
+__global__ __launch_bounds__(256) void fwd_part_merge_kernel(PartMergeArgs p) {
+    const int i = blockIdx.x / (DQ_BQ / PART_MERGE_ROWS);
+    const int r0 = (blockIdx.x % (DQ_BQ / PART_MERGE_ROWS)) * PART_MERGE_ROWS;
+    const int work = p.items[3 * i], slot0 = p.items[3 * i + 1], np = p.items[3 * i + 2];
+    const int t = work % p.nqt, bh = work / p.nqt;
+    const int h = bh % p.Hq, b = bh / p.Hq;
+    const int qt = as_const(p.t_order)[t];
+    const int cpr = p.d / 4;      // 4-float chunks per row
+    const int rpp = 256 / cpr;    // rows per pass of the work-group
+    const int c = (threadIdx.x % cpr) * 4;
+    for (int r = r0 + threadIdx.x / cpr; r < r0 + PART_MERGE_ROWS; r += rpp) {
+        const int iq = qt * DQ_BQ + r;
+        if (iq >= p.S) break;
+        float M = -INFINITY;
+        for (int k = 0; k < np; ++k) M = fmaxf(M, p.part_l[(int64_t)(slot0 + k) * DQ_BQ + r]);
+        f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+        float L = -INFINITY;
+        if (M != -INFINITY) {
+            float sum = 0.f;
+            for (int k = 0; k < np; ++k) sum += expf(p.part_l[(int64_t)(slot0 + k) * DQ_BQ + r] - M);
+            L = M + logf(sum);
+            for (int k = 0; k < np; ++k) {
+                const float wk = expf(p.part_l[(int64_t)(slot0 + k) * DQ_BQ + r] - L);
+                o += wk * *(const f32x4_t*)(p.part_o + ((int64_t)(slot0 + k) * DQ_BQ + r) * p.d + c);
+            }
+        }
+        const u32x2_t w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        *(u32x2_t*)((uint16_t*)p.out + ((int64_t)(b * p.S + iq) * p.Hq + h) * p.d + c) = w;
+        if (c == 0) p.lse[((int64_t)b * p.Hq + h) * p.S + iq] = L;
+    }
+}
+
+hipError_t launch_fwd_part_merge(const PartMergeArgs& a, hipStream_t s) {
+    if (a.n_items == 0) return hipSuccess;
+    if (a.d != 64 && a.d != 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fwd_part_merge_kernel, dim3(a.n_items * (DQ_BQ / PART_MERGE_ROWS)), dim3(256), 0,
+                       s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, hipStream_t s) {
     const int grid = a.ring && a.pers_off ? a.pers_blocks : (a.total_work + 7) / 8 * 8;

@@ -57,11 +57,28 @@ struct FwdArgs {
     int32_t total_work;     // B * Hq * nqt
     float scale_log2;       // softmax scale * log2(e)
     // Persistent schedule (ring launch only; NULL: one work item per block):
-    // block i walks work items pers_items[pers_off[i] .. pers_off[i + 1]),
-    // and the launch has pers_blocks blocks.
+    // block i walks items pers_off[i] .. pers_off[i + 1] - 1 of pers_items,
+    // 4 ints each: work index, first and end entry of the work's list
+    // (relative to its start), part slot (-1: the whole list); the launch has
+    // pers_blocks blocks.  A part writes its normalised partial output and lse
+    // to part_o [slot][256 rows][d] and part_l [slot][256 rows].
     const int32_t* pers_off;
     const int32_t* pers_items;
     int32_t pers_blocks;
+    float* part_o;
+    float* part_l;
+};
+
+// Merge of the parts of split forward lists (fwd_part_merge_kernel): item i
+// is items[3i..3i+2] = work index, first part slot, number of parts.
+struct PartMergeArgs {
+    const int32_t* items;
+    const int32_t* t_order;   // [nqt] query tile of each list position
+    const float* part_o;
+    const float* part_l;
+    void* out;                // [B, S, Hq, d] bf16
+    float* lse;               // [B, Hq, S]
+    int32_t n_items, nqt, S, Hq, d;
 };
 
 struct BwdArgs {
@@ -147,6 +164,7 @@ struct BwdPreArgs {
 // Launchers (defined in the .hip files).  Return hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_fwd_part_merge(const PartMergeArgs& a, hipStream_t s);
 hipError_t launch_lse_merge(float* out, float* lse, const float* out_j, const float* lse_j,
                             int32_t B, int64_t S, int32_t H, int32_t d, hipStream_t s);
 hipError_t launch_finalize(const float* o, void* out, int is_bf16, int64_t n, hipStream_t s);

@@ -210,10 +210,13 @@ void classify(const StepRanges& sr, int64_t S, int64_t Skv, int32_t bq, int32_t 
 
 std::string plan_key(const Geometry& g) {
     // The schedule and tile lists depend on the token geometry; which lists a
-    // plan holds also depends on the input type.
+    // plan holds also depends on the input type; the forward's persistent
+    // schedule on the number of (batch, q head) pairs, its part buffer on the
+    // head dimension.
     std::ostringstream o;
     o << g.N << ',' << g.D << ',' << g.r << ',' << g.causal << ',' << g.layout << ','
-      << g.win_left << ',' << g.win_right << ',' << g.dtype;
+      << g.win_left << ',' << g.win_right << ',' << g.dtype << ',' << g.B << ',' << g.Hq << ','
+      << g.d;
     if (g.varlen) {
         o << '|';
         for (int64_t c : g.cu) o << c << ',';

@@ -193,14 +193,32 @@ int64_t ring_attn_workspace_bytes(const ring_attn_desc* desc, int is_bwd);
  * Returns a negative RA_E_* for an invalid descriptor. */
 int64_t ring_attn_bwd_ds_bytes(const ring_attn_desc* desc, const int32_t* cu_seqlens);
 
+/* Extra forward workspace, in bytes, that lets the one-launch RA_MERGE_FUSED
+ * bf16 forward split long query-tile lists across CUs.  With more work items
+ * (batch x q heads x 256-row query tiles) than CUs, the forward runs one
+ * work-group per CU over a balanced list of items; a list much longer than
+ * the others can be cut into parts run on different CUs, each part's
+ * normalised partial and lse written to the workspace and the parts folded
+ * by the log-sum-exp merge of "Numerically-Stable Output Fusion" (a second,
+ * small kernel).  The parts never outnumber the CUs, so the bound is
+ * (CUs of the current device, rounded down to a multiple of 8) x 256 rows x
+ * (head_dim + 1) x 4 bytes; 0 for other dtypes and merge modes.  A smaller
+ * workspace is accepted: the lists then run whole.  Host only (queries the
+ * current device); negative RA_E_* for an invalid descriptor, RA_E_HIP when
+ * no device can be queried. */
+int64_t ring_attn_fwd_split_bytes(const ring_attn_desc* desc);
+
 /* Forward of the rank share ("Forward Pass Implementation"): for s = 0..D-1
  * the block j = (rank - s) mod D is attended if at least one (query, key) pair
  * of the step is visible (under a causal basic layout exactly the steps with
  * s <= rank), each step's partial is merged into the running result, and the
  * result is written as out (dtype of q) and lse (fp32).  A row with no
  * visible key gets out = 0 and lse = -inf.  Workspace: at least
- * ring_attn_workspace_bytes(desc, 0) bytes of device memory; its contents
- * need not be initialised and are garbage afterwards. */
+ * ring_attn_workspace_bytes(desc, 0) bytes of device memory; with
+ * ring_attn_fwd_split_bytes(desc) bytes beyond that, long query-tile lists
+ * may be split across CUs (the results then differ from an unsplit run only
+ * by the rounding of the merge).  Its contents need not be initialised and
+ * are garbage afterwards. */
 int ring_attn_fwd(const ring_attn_desc* desc, const void* q, const void* k,
                   const void* v, const int32_t* cu_seqlens, void* out, float* lse,
                   void* workspace, size_t workspace_bytes, void* stream);

@@ -147,6 +147,21 @@ def test_tile_kinds_against_brute_force(layout, causal, window):
                             assert blk.any() and not (blk.all() and full_width)
 
 
+def test_fwd_split_bytes_without_device_work():
+    """The split part buffer exists only for the one-launch bf16 forward: other
+    dtypes and merge modes need none, and an unsupported head_dim or a null
+    descriptor is refused, all without touching a device."""
+    lib = ca.lib()
+    d32 = ca.make_desc(1, 4, 2, 128, 64, 4, 1, True, ca.BASIC, dtype="f32")
+    assert lib.ring_attn_fwd_split_bytes(ctypes.byref(d32)) == 0
+    for mode in (ca.RA_MERGE_SEPARATE, ca.RA_MERGE_STEPWISE):
+        d = ca.make_desc(1, 4, 2, 128, 64, 4, 1, True, ca.BASIC, merge_mode=mode)
+        assert lib.ring_attn_fwd_split_bytes(ctypes.byref(d)) == 0
+    bad = ca.make_desc(1, 4, 2, 96, 64, 4, 1, True, ca.BASIC)
+    assert lib.ring_attn_fwd_split_bytes(ctypes.byref(bad)) < 0
+    assert lib.ring_attn_fwd_split_bytes(None) < 0
+
+
 def _rc_fwd(desc, cu=None, ws_bytes=1 << 30, nulls=False):
     """Calls ring_attn_fwd with fake non-null device pointers: validation must
     fail before any of them is touched."""

@@ -456,14 +456,51 @@ def test_fwd_persistent_schedule(layout, B, head_dim, S):
     one-launch forward runs one work-group per CU, each walking the planner's
     list of items (lists of unequal length, ragged last tile), and must give
     the oracle's result on every row."""
-    w = _small_workload(layout, True, head_dim, D=2, S=S, B=B, Hq=32, Hkv=8, seed=S + layout)
-    n_items = w.batch * w.heads_q * -(-S // 256)
-    assert n_items > torch.cuda.get_device_properties(0).multi_processor_count
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    # the same token geometry with two head counts (and head dims): each call
+    # needs the schedule of its own (batch, q head) pairs
+    for Hq, d in ((32, head_dim), (40, 192 - head_dim)):
+        w = _small_workload(layout, True, d, D=2, S=S, B=B, Hq=Hq, Hkv=8, seed=S + layout)
+        assert w.batch * w.heads_q * -(-S // 256) > cus
+        glob = synth.draw_global(w)
+        for rank in range(w.world):
+            say(f"persistent forward layout={layout} B={w.batch} Hq={Hq} d={d} S={S} rank={rank}")
+            _, _, _, out, lse = _run_fwd(w, glob, rank)
+            _check_fwd(w, glob, rank, out, lse)
+
+
+@pytest.mark.parametrize("layout,B,head_dim,S", [(ca.LLAMA3, 1, 128, 2300), (ca.LLAMA3, 1, 64, 2300)])
+def test_fwd_split_lists(layout, B, head_dim, S):
+    """Packed documents of very different lengths give query-tile lists of
+    very different lengths: with the part buffer in the workspace the
+    persistent forward cuts the longest lists into parts on different CUs and
+    merges them (the part-merge kernel runs); without it the lists run whole.
+    Both match the oracle, and differ from each other only by the rounding of
+    the merge."""
+    w = _small_workload(layout, True, head_dim, D=2, S=S, B=B, Hq=32, Hkv=8, seed=3 * S + layout)
     glob = synth.draw_global(w)
-    for rank in range(w.world):
-        say(f"persistent forward layout={layout} B={w.batch} d={head_dim} S={S} rank={rank}")
-        _, _, _, out, lse = _run_fwd(w, glob, rank)
-        _check_fwd(w, glob, rank, out, lse)
+    rank = w.world - 1
+    sh = shard(glob, w, rank)
+    desc = ca.desc_from_workload(w, rank=rank)
+    q, k, v = (to_dev(sh[n], w.dtype) for n in ("q", "k", "v"))
+    split_bytes = ca.ring_attn_fwd_split_bytes(desc)
+    assert split_bytes > 0
+    results = {}
+    for name, nbytes in (("split", ca.ring_attn_workspace_bytes(desc, False) + split_bytes),
+                         ("whole", 16)):
+        say(f"split lists layout={layout} d={head_dim} S={S} workspace={name}")
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        ca.ring_attn_timing_enable(False)
+        ca.ring_attn_timing_enable(True)
+        out, lse = ca.ring_attn_fwd(desc, q, k, v, w.cu_seqlens, workspace=ws)
+        torch.cuda.synchronize()
+        merges, _ = ca.ring_attn_timing_read("fwd_part_merge")
+        ca.ring_attn_timing_enable(False)
+        assert (merges > 0) == (name == "split"), (name, merges)
+        results[name] = (out.float().cpu().numpy(), lse.cpu().numpy())
+        _check_fwd(w, glob, rank, *results[name])
+    assert np.abs(results["split"][0] - results["whole"][0]).max() <= 1e-2
+    assert max_err_lse(results["split"][1], results["whole"][1]) <= 1e-4
 
 
 def test_hip_graph_capture_and_replay():
