@@ -477,24 +477,34 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // work-group can end and release its LDS
     __builtin_amdgcn_s_waitcnt(0);
 
-    // dK_j += scale * dK^T acc, dV_j += dV^T acc (this lane's key, 64 head-dim values)
+    // dK_j += scale * dK^T acc, dV_j += dV^T acc (this lane's key, DH head-dim
+    // values of each).  Every load is issued before the first store: a store
+    // to dK may alias a later load of dV as far as the compiler knows, so
+    // interleaved load-add-store would wait for a memory round trip per pair.
     if (key < p.Skv) {
         float* dkr = p.dk + ((int64_t)b * p.Skv + key) * kv_stride + hk * DH;
         float* dvr = p.dv + ((int64_t)b * p.Skv + key) * kv_stride + hk * DH;
+        f32x4_t xk[C::NDT][4], xv[C::NDT][4];
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 const int d0 = 32 * dt + 8 * rg + 4 * g;
-                f32x4_t x = *(f32x4_t*)(dkr + d0);
-                f32x4_t y = *(f32x4_t*)(dvr + d0);
+                xk[dt][rg] = *(const f32x4_t*)(dkr + d0);
+                xv[dt][rg] = *(const f32x4_t*)(dvr + d0);
+            }
+#pragma unroll
+        for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+                const int d0 = 32 * dt + 8 * rg + 4 * g;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    x[i] += p.scale * dk_acc[dt][4 * rg + i];
-                    y[i] += dv_acc[dt][4 * rg + i];
+                    xk[dt][rg][i] += p.scale * dk_acc[dt][4 * rg + i];
+                    xv[dt][rg][i] += dv_acc[dt][4 * rg + i];
                 }
-                *(f32x4_t*)(dkr + d0) = x;
-                *(f32x4_t*)(dvr + d0) = y;
+                *(f32x4_t*)(dkr + d0) = xk[dt][rg];
+                *(f32x4_t*)(dvr + d0) = xv[dt][rg];
             }
     }
 }
@@ -753,19 +763,29 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     // dq_acc (+)= scale * acc in the accumulator layout: element (dt, r) of
     // query block qb is head-dim index 32*dt + 8*(r/4) + 4*g + r%4 of query
     // row qt*256 + 64*wave + 32*qb + l32.
+    // (one branch on `first` for the whole update, and all loads of a 32-row
+    // block issued before its stores: per element, the branch split the
+    // update into one load-wait-store round trip each)
+    const bool add = !p.first;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         f32x4_t* dst = (f32x4_t*)p.dq_acc +
                        (((int64_t)b * p.Hq + h) * (p.S_pad / 32) + (qt * 8 + wave * 2 + qb)) * (8 * DH) + lane;
+        f32x4_t old[C::NDT][4];
+        if (add) {
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) old[dt][rg] = dst[(dt * 4 + rg) * 64];
+        }
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 f32x4_t o = {acc[qb][dt][4 * rg] * p.scale, acc[qb][dt][4 * rg + 1] * p.scale,
                              acc[qb][dt][4 * rg + 2] * p.scale, acc[qb][dt][4 * rg + 3] * p.scale};
-                f32x4_t* ptr = dst + (dt * 4 + rg) * 64;
-                if (!p.first) o += *ptr;
-                *ptr = o;
+                if (add) o += old[dt][rg];
+                dst[(dt * 4 + rg) * 64] = o;
             }
     }
 }
@@ -961,19 +981,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_ds_bf16_kernel(DqDsArgs p) {
     mfma_ks(c_ops);
 
     // dq_acc (+)= scale * acc, in the layout of the recomputing dQ kernel
+    // (one branch on `first` for the whole update, and all loads of a 32-row
+    // block issued before its stores: per element, the branch split the
+    // update into one load-wait-store round trip each)
+    const bool add = !p.first;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         f32x4_t* dst = (f32x4_t*)p.dq_acc +
                        (((int64_t)b * p.Hq + h) * (p.S_pad / 32) + (qt * 8 + wave * 2 + qb)) * (8 * DH) + lane;
+        f32x4_t old[C::NDT][4];
+        if (add) {
+#pragma unroll
+            for (int dt = 0; dt < C::NDT; ++dt)
+#pragma unroll
+                for (int rg = 0; rg < 4; ++rg) old[dt][rg] = dst[(dt * 4 + rg) * 64];
+        }
 #pragma unroll
         for (int dt = 0; dt < C::NDT; ++dt)
 #pragma unroll
             for (int rg = 0; rg < 4; ++rg) {
                 f32x4_t o = {acc[qb][dt][4 * rg] * p.scale, acc[qb][dt][4 * rg + 1] * p.scale,
                              acc[qb][dt][4 * rg + 2] * p.scale, acc[qb][dt][4 * rg + 3] * p.scale};
-                f32x4_t* ptr = dst + (dt * 4 + rg) * 64;
-                if (!p.first) o += *ptr;
-                *ptr = o;
+                if (add) o += old[dt][rg];
+                dst[(dt * 4 + rg) * 64] = o;
             }
     }
 }
