@@ -213,9 +213,9 @@ def measured_peaks(torch):
     alone (libraprobe.so's MFMA-only kernel, two work-groups of four waves per
     CU, timed after a second of the same load so that the clock has settled)
     and streaming over 1 GiB per operand, bytes read + written: torch's copy
-    kernel, and libraprobe.so's streaming copy (one byte read per byte written)
-    and streaming add (two read per byte written, the LSE merge's ratio), each
-    the best over grid sizes and cache policies."""
+    kernel, and libraprobe.so's streaming copy (one byte read per byte written),
+    streaming add (two read per byte written, the LSE merge's ratio) and
+    read-only fold, each the best over grid sizes and cache policies."""
     import ctypes
     path = os.path.join(ROOT, "context_attention_flash_amd", "libraprobe.so")
     if not os.path.exists(path):
@@ -279,13 +279,35 @@ def measured_peaks(torch):
                 torch.cuda.synchronize()
                 gbs = moved * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
                 best[kind] = max(best[kind], (gbs, blocks, flags))
-    del z
+    probe.ra_probe_stream_read.restype = ctypes.c_int
+    probe.ra_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    sink = torch.empty(32768 * 256, dtype=torch.int32, device="cuda")
+    best["read"] = (0.0, 0, 0)
+    for flags in range(2):
+        for blocks in (256, 512, 1024, 2048, 4096, 8192, 16384, 32768):
+            def run():
+                rc = probe.ra_probe_stream_read(x.data_ptr(), sink.data_ptr(), nbytes, blocks, flags,
+                                                ctypes.c_void_p(stream.cuda_stream))
+                if rc != 0:
+                    raise RuntimeError(f"ra_probe_stream_read failed ({rc})")
+            for _ in range(3):
+                run()
+            ev0.record(stream)
+            for _ in range(reps):
+                run()
+            ev1.record(stream)
+            torch.cuda.synchronize()
+            gbs = nbytes * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+            best["read"] = max(best["read"], (gbs, blocks, flags))
+    del z, sink
     del x, y, out
     torch.cuda.empty_cache()
     return {"mfma_only_bf16_TFLOP/s": mfma_tf, "mfma_only_frac_of_spec": mfma_tf / PEAK_BF16_TFLOPS,
             "copy_GB/s": copy_gbs, "copy_frac_of_spec": copy_gbs / PEAK_HBM_GBS,
             "stream_copy_GB/s": best["copy"][0], "stream_copy_frac_of_spec": best["copy"][0] / PEAK_HBM_GBS,
             "stream_add_GB/s": best["add"][0], "stream_add_frac_of_spec": best["add"][0] / PEAK_HBM_GBS,
+            "stream_read_GB/s": best["read"][0], "stream_read_frac_of_spec": best["read"][0] / PEAK_HBM_GBS,
             "stream_best_config": {k: {"blocks": v[1], "nt_loads": bool(v[2] & 1),
                                        "nt_stores": bool(v[2] & 2)} for k, v in best.items()},
             "spec": {"bf16_TFLOP/s": PEAK_BF16_TFLOPS, "hbm_GB/s": PEAK_HBM_GBS}}

@@ -1,9 +1,9 @@
 // Measurement aids (not part of the attention path): a kernel that does
 // nothing but bf16 MFMAs, to measure what the matrix cores of this GPU deliver
 // when they are the only thing running, under the clocks the chip then holds,
-// and streaming kernels (a copy, and an add that reads two bytes per byte
-// written, as the LSE merge does), to measure what HBM delivers to plain
-// read-and-write kernels.  Built into their own library (libraprobe.so), loaded by bench.py
+// and streaming kernels (a copy, an add that reads two bytes per byte
+// written, as the LSE merge does, and a read-only fold), to measure what HBM
+// delivers to plain streaming kernels.  Built into their own library (libraprobe.so), loaded by bench.py
 // and the tests only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -90,6 +90,35 @@ __global__ __launch_bounds__(256) void stream_kernel(const f32x4_t* __restrict__
     }
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// The xor of a chunk's four words.  The whole vector is bit-cast: this
+// compiler folds a bit-cast of a single vector element (v[k]) as if every
+// element were the first, which turns the xor of four of them into zero.
+__device__ __forceinline__ uint32_t xor4(f32x4_t v) {
+    const u32x4_t w = __builtin_bit_cast(u32x4_t, v);
+    return w.x ^ w.y ^ w.z ^ w.w;
+}
+
+// Read-only streaming: each thread folds its chunks of a[0 .. n) into one
+// word (the xor of their bits, so no load is optimised away) and writes it to
+// out[thread] (4 bytes per thread).
+template <bool NT_LD>
+__global__ __launch_bounds__(256) void stream_read_kernel(const f32x4_t* __restrict__ a,
+                                                          uint32_t* __restrict__ out, int64_t n) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    uint32_t x = 0;
+    for (; i + (STREAM_UNROLL - 1) * stride < n; i += STREAM_UNROLL * stride) {
+        f32x4_t v[STREAM_UNROLL];
+#pragma unroll
+        for (int u = 0; u < STREAM_UNROLL; ++u) v[u] = ld16<NT_LD>(a + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < STREAM_UNROLL; ++u) x ^= xor4(v[u]);
+    }
+    for (; i < n; i += stride) x ^= xor4(ld16<NT_LD>(a + i));
+    out[(int64_t)blockIdx.x * 256 + threadIdx.x] = x;
+}
+
 template <bool ADD>
 void launch_stream(int flags, int blocks, hipStream_t s, const f32x4_t* a, const f32x4_t* b,
                    f32x4_t* d, int64_t n) {
@@ -123,6 +152,24 @@ int ra_probe_mfma(float* out, int32_t blocks, int32_t iters, hipStream_t stream)
 // 16, dst overlapping neither input) with `blocks` work-groups of 256 threads
 // on `stream`.  flags bit 0: non-temporal loads, bit 1: non-temporal stores.
 // Returns a hipError_t value.
+// Read `bytes` bytes of a (16-byte aligned, a multiple of 16) with `blocks`
+// work-groups of 256 threads on `stream`; out receives blocks * 256 uint32.
+// flags bit 0: non-temporal loads.  Returns a hipError_t value.
+int ra_probe_stream_read(const void* a, void* out, int64_t bytes, int32_t blocks, int32_t flags,
+                         hipStream_t stream) {
+    if (a == nullptr || out == nullptr || bytes < 0 || bytes % 16 != 0 || blocks <= 0 || flags < 0 ||
+        flags > 1 || ((uintptr_t)a | (uintptr_t)out) % 16 != 0)
+        return (int)hipErrorInvalidValue;
+    if (bytes == 0) return (int)hipSuccess;
+    if (flags & 1)
+        hipLaunchKernelGGL(stream_read_kernel<true>, dim3(blocks), dim3(256), 0, stream,
+                           (const f32x4_t*)a, (uint32_t*)out, bytes / 16);
+    else
+        hipLaunchKernelGGL(stream_read_kernel<false>, dim3(blocks), dim3(256), 0, stream,
+                           (const f32x4_t*)a, (uint32_t*)out, bytes / 16);
+    return (int)hipGetLastError();
+}
+
 int ra_probe_stream(const void* a, const void* b, void* dst, int64_t bytes, int32_t blocks,
                     int32_t flags, hipStream_t stream) {
     if (a == nullptr || dst == nullptr || bytes < 0 || bytes % 16 != 0 || blocks <= 0 ||

@@ -56,6 +56,15 @@ def test_peak_probe_library_loads():
             (16, None, 32, -16, 1, 0), (16, None, 32, 16, 1, 4), (16, None, 32, 16, 1, -1)):
         assert lib.ra_probe_stream(a, b, dst, nbytes, blocks, flags, None) != 0   # refused, no launch
     assert lib.ra_probe_stream(16, 48, 32, 0, 1, 3, None) == 0                   # nothing to move
+    lib.ra_probe_stream_read.restype = ctypes.c_int
+    lib.ra_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    for a, out, nbytes, blocks, flags in (
+            (None, 16, 16, 1, 0), (16, None, 16, 1, 0), (16, 32, 24, 1, 0), (16, 32, 16, 0, 0),
+            (8, 32, 16, 1, 0), (16, 40, 16, 1, 0), (16, 32, -16, 1, 0), (16, 32, 16, 1, 2),
+            (16, 32, 16, 1, -1)):
+        assert lib.ra_probe_stream_read(a, out, nbytes, blocks, flags, None) != 0  # refused
+    assert lib.ra_probe_stream_read(16, 32, 0, 1, 1, None) == 0                 # nothing to read
 
 
 def _cu(layout, N, D, rng, n_docs=5):
