@@ -469,6 +469,28 @@ def test_fwd_persistent_schedule(layout, B, head_dim, S):
             _check_fwd(w, glob, rank, out, lse)
 
 
+@pytest.mark.parametrize("layout,causal,window,head_dim,S,B,Hq", [
+    (ca.STRIPE, True, (-1, -1), 128, 1100, 2, 32),
+    (ca.VARLEN_ZIGZAG, True, (-1, -1), 64, 1800, 1, 40),
+    (ca.VARLEN_STRIPE, False, (-1, -1), 128, 1200, 1, 64),
+    (ca.BASIC, True, (700, -1), 128, 1100, 2, 32),
+    (ca.VARLEN_RING, False, (300, 200), 64, 1500, 1, 48)])
+def test_fwd_persistent_schedule_layouts(layout, causal, window, head_dim, S, B, Hq):
+    """The persistent forward on the other layouts, without the causal mask
+    and with sliding windows (masked tiles at both ends of a list, steps with
+    no visible pair), more work items than CUs."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    w = _small_workload(layout, causal, head_dim, D=2, S=S, B=B, Hq=Hq, Hkv=8, seed=S + 11 * layout,
+                        window=window)
+    assert w.batch * w.heads_q * -(-S // 256) > cus
+    glob = synth.draw_global(w)
+    for rank in range(w.world):
+        say(f"persistent forward layout={layout} causal={causal} window={window} d={head_dim} "
+            f"S={S} B={w.batch} Hq={Hq} rank={rank}")
+        _, _, _, out, lse = _run_fwd(w, glob, rank)
+        _check_fwd(w, glob, rank, out, lse)
+
+
 @pytest.mark.parametrize("layout,B,head_dim,S", [(ca.LLAMA3, 1, 128, 2300), (ca.LLAMA3, 1, 64, 2300)])
 def test_fwd_split_lists(layout, B, head_dim, S):
     """Packed documents of very different lengths give query-tile lists of
