@@ -223,143 +223,13 @@ void build_ds_lists(const std::vector<int32_t>& boff, const std::vector<int32_t>
     });
 }
 
-// Whether the bf16 forward runs as one launch over every ring step: the
-// entries hold the key tile in 20 bits and the step in 11.
-// Persistent schedule of the one-launch forward.  The kernel holds one
-// work-group per CU (8 waves of 256 registers), so a launch of one block per
-// CU keeps every CU busy until its own list ends: no CU waits for the
-// dispatcher between two work items, and no CU idles at the end while others
-// finish long items.  Work item w = (b, q head) * nq + t runs the list of
-// query tile order[t].  Each XCD (blocks are dealt to the 8 XCDs in turn)
-// keeps the contiguous range of work items it gets without a schedule, so the
-// items of a head still share that XCD's L2; inside the XCD, items go
-// heaviest first to the least loaded of its blocks.  The cost of a list, in
-// tenths of an unmasked key tile: 10 per unmasked tile, 14 per masked one,
-// 120 for a work item's prologue and epilogue (measured: 3024 and 4411 cycles
-// per tile, 13.2k per item).
-//
-// With `split`, a list that costs more than a third of its XCD's mean block
-// load is cut into parts of about equal cost (at most 8, at most one per
-// entry); each part runs as an item of its own and writes its normalised
-// partial to a part slot, and the part-merge kernel folds the parts.  Whole
-// items alone cannot balance the blocks when an item is a large fraction of a
-// block's load (few items per CU of very different lengths).  The parts never
-// outnumber the blocks (the threshold is raised until they fit), which bounds
-// the part buffer.
-struct PersSchedule {
-    std::vector<int32_t> off;     // [blocks + 1]
-    std::vector<int32_t> items;   // 4 per item: work, first entry, end entry, part slot (-1)
-    std::vector<int32_t> merge;   // 3 per split list: work, first slot, parts
-    int32_t slots = 0;
-    int64_t makespan = 0;         // largest block load (cost units)
-};
-
+// Blocks of the persistent forward on `device`: its CU count rounded down to
+// a multiple of 8 (the XCDs); 0 when the count cannot be read.
 int64_t persistent_blocks(int device) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess)
         return 0;
     return cus / 8 * 8;
-}
-
-void persistent_schedule(int device, int64_t n_bh, const std::vector<int32_t>& off,
-                         const std::vector<int32_t>& mid, const std::vector<int32_t>& order,
-                         bool split, PersSchedule& out) {
-    out = PersSchedule{};
-    constexpr int64_t kXcd = 8, kMaxParts = 8, kTile = 10, kMasked = 14, kItem = 120;
-    const int64_t nblk = persistent_blocks(device);
-    const int64_t nq = (int64_t)order.size();
-    const int64_t W = n_bh * nq;
-    if (nblk < kXcd || W <= nblk) return;
-    const int64_t per_xcd = nblk / kXcd;
-    auto nfull = [&](int64_t w) { const int32_t q = order[w % nq]; return (int64_t)(mid[q] - off[q]); };
-    auto nall = [&](int64_t w) { const int32_t q = order[w % nq]; return (int64_t)(off[q + 1] - off[q]); };
-    auto cost_of = [&](int64_t w, int64_t a, int64_t b) {   // entries [a, b) of w's list
-        const int64_t f = nfull(w);
-        const int64_t full = std::max<int64_t>(0, std::min(b, f) - a);
-        return kTile * full + kMasked * (b - a - full) + kItem;
-    };
-    // the threshold of each XCD: a third of its mean block load, raised until
-    // the parts fit the part slots
-    std::vector<int64_t> thresh(kXcd, INT64_MAX);
-    auto parts_of = [&](int64_t w, int64_t T) {
-        const int64_t c = cost_of(w, 0, nall(w));
-        if (c <= T || nall(w) < 2) return (int64_t)1;
-        return std::min({(c + T - 1) / T, kMaxParts, nall(w)});
-    };
-    if (split) {
-        int64_t used = 0;
-        for (int64_t x = 0; x < kXcd; ++x) {
-            const int64_t w0 = x * W / kXcd, w1 = (x + 1) * W / kXcd;
-            int64_t total = 0;
-            for (int64_t w = w0; w < w1; ++w) total += cost_of(w, 0, nall(w));
-            thresh[x] = std::max<int64_t>(1, total / per_xcd / 3);
-        }
-        for (;;) {
-            used = 0;
-            for (int64_t x = 0; x < kXcd; ++x)
-                for (int64_t w = x * W / kXcd; w < (x + 1) * W / kXcd; ++w) {
-                    const int64_t k = parts_of(w, thresh[x]);
-                    if (k > 1) used += k;
-                }
-            if (used <= nblk) break;
-            for (auto& t : thresh) t = t + t / 4 + 1;
-        }
-    }
-    struct Piece { int64_t cost; int32_t w, a, b, slot; };
-    std::vector<std::vector<int32_t>> lists(nblk);
-    std::vector<Piece> pieces;
-    for (int64_t x = 0; x < kXcd; ++x) {
-        const int64_t w0 = x * W / kXcd, w1 = (x + 1) * W / kXcd;
-        pieces.clear();
-        for (int64_t w = w0; w < w1; ++w) {
-            const int64_t n = nall(w);
-            const int64_t k = split ? parts_of(w, thresh[x]) : 1;
-            if (k == 1) {
-                pieces.push_back({cost_of(w, 0, n), (int32_t)w, 0, (int32_t)n, -1});
-                continue;
-            }
-            // cut the entries where the running cost passes j/k of the list's
-            const int64_t f = nfull(w);
-            const int64_t tiles = kTile * std::min(f, n) + kMasked * (n - std::min(f, n));
-            out.merge.insert(out.merge.end(), {(int32_t)w, out.slots, (int32_t)k});
-            int64_t a = 0, acc = 0, e = 0;
-            for (int64_t j = 1; j <= k; ++j) {
-                int64_t b = n;
-                if (j < k) {
-                    const int64_t goal = tiles * j / k;
-                    while (e < n && acc < goal) acc += e++ < f ? kTile : kMasked;
-                    b = std::max(e, a + 1);
-                    b = std::min(b, n - (k - j));   // every later part keeps one entry
-                    e = b;
-                    acc = kTile * std::min(b, f) + kMasked * (b - std::min(b, f));
-                }
-                pieces.push_back({cost_of(w, a, b), (int32_t)w, (int32_t)a, (int32_t)b, out.slots++});
-                a = b;
-            }
-        }
-        // heaviest first, each to the least loaded block (ties to the lower
-        // block index).  (Taking the pieces in their own order instead, as the
-        // hardware would dispatch them, balanced basic_s8192 as well but
-        // doubled the forward's L2 misses; the time did not change.)
-        std::stable_sort(pieces.begin(), pieces.end(),
-                         [](const Piece& p, const Piece& q) { return p.cost > q.cost; });
-        using Slot = std::pair<int64_t, int64_t>;   // (load, local block index)
-        std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
-        for (int64_t l = 0; l < per_xcd; ++l) heap.emplace(0, l);
-        for (const Piece& pc : pieces) {
-            auto [load, l] = heap.top();
-            heap.pop();
-            auto& L = lists[l * kXcd + x];
-            L.insert(L.end(), {pc.w, pc.a, pc.b, pc.slot});
-            heap.emplace(load + pc.cost, l);
-            out.makespan = std::max(out.makespan, load + pc.cost);
-        }
-    }
-    out.off.assign(nblk + 1, 0);
-    for (int64_t i = 0; i < nblk; ++i) {
-        out.off[i + 1] = out.off[i] + (int32_t)(lists[i].size() / 4);
-        out.items.insert(out.items.end(), lists[i].begin(), lists[i].end());
-    }
 }
 
 // Bytes of the part buffer of a split schedule with `slots` part slots:
@@ -368,6 +238,8 @@ int64_t part_bytes(int64_t slots, int64_t d) {
     return round_up(slots * DQ_BQ * d * 4, 256) + round_up(slots * DQ_BQ * 4, 256);
 }
 
+// Whether the bf16 forward runs as one launch over every ring step: the
+// entries hold the key tile in 20 bits and the step in 11.
 bool ring_capable(const Geometry& g) {
     return g.dtype == RA_BF16 && g.nb <= RING_MAX_STEPS &&
            (g.Skv + DQ_BK - 1) / DQ_BK <= RING_MAX_KEY_TILES;
@@ -503,12 +375,12 @@ int build_plan(const Geometry& g, int device, std::unique_ptr<Plan>& out) {
             return roff[x + 1] - roff[x] > roff[y + 1] - roff[y];
         });
         PersSchedule plain, cut;
-        persistent_schedule(device, (int64_t)g.B * g.Hq, roff, rmid, rord, false, plain);
+        persistent_schedule(persistent_blocks(device), (int64_t)g.B * g.Hq, roff, rmid, rord, false, plain);
         if (!plain.off.empty()) {
             plan->pers_blocks = (int32_t)plain.off.size() - 1;
             i_poff = H.add(std::move(plain.off));
             i_pitems = H.add(std::move(plain.items));
-            persistent_schedule(device, (int64_t)g.B * g.Hq, roff, rmid, rord, true, cut);
+            persistent_schedule(persistent_blocks(device), (int64_t)g.B * g.Hq, roff, rmid, rord, true, cut);
             // split only where the cut shortens the busiest block by more than
             // the part merge costs (about 12 us, some 70 cost units)
             if (cut.slots > 0 && cut.makespan + 70 < plain.makespan * 99 / 100) {

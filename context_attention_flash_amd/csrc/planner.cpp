@@ -11,6 +11,8 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <functional>
+#include <queue>
 #include <sstream>
 
 namespace ra {
@@ -205,6 +207,106 @@ void classify(const StepRanges& sr, int64_t S, int64_t Skv, int32_t bq, int32_t 
             else if (run > 0) kind = TILE_PARTIAL;
             kinds[qt * nkt + kt] = kind;
         }
+    }
+}
+
+void persistent_schedule(int64_t nblk, int64_t n_bh, const std::vector<int32_t>& off,
+                         const std::vector<int32_t>& mid, const std::vector<int32_t>& order,
+                         bool split, PersSchedule& out) {
+    out = PersSchedule{};
+    constexpr int64_t kXcd = 8, kMaxParts = 8, kTile = 10, kMasked = 14, kItem = 120;
+    const int64_t nq = (int64_t)order.size();
+    const int64_t W = n_bh * nq;
+    if (nblk < kXcd || W <= nblk) return;
+    const int64_t per_xcd = nblk / kXcd;
+    auto nfull = [&](int64_t w) { const int32_t q = order[w % nq]; return (int64_t)(mid[q] - off[q]); };
+    auto nall = [&](int64_t w) { const int32_t q = order[w % nq]; return (int64_t)(off[q + 1] - off[q]); };
+    auto cost_of = [&](int64_t w, int64_t a, int64_t b) {   // entries [a, b) of w's list
+        const int64_t f = nfull(w);
+        const int64_t full = std::max<int64_t>(0, std::min(b, f) - a);
+        return kTile * full + kMasked * (b - a - full) + kItem;
+    };
+    // the threshold of each XCD: a third of its mean block load, raised until
+    // the parts fit the part slots
+    std::vector<int64_t> thresh(kXcd, INT64_MAX);
+    auto parts_of = [&](int64_t w, int64_t T) {
+        const int64_t c = cost_of(w, 0, nall(w));
+        if (c <= T || nall(w) < 2) return (int64_t)1;
+        return std::min({(c + T - 1) / T, kMaxParts, nall(w)});
+    };
+    if (split) {
+        int64_t used = 0;
+        for (int64_t x = 0; x < kXcd; ++x) {
+            const int64_t w0 = x * W / kXcd, w1 = (x + 1) * W / kXcd;
+            int64_t total = 0;
+            for (int64_t w = w0; w < w1; ++w) total += cost_of(w, 0, nall(w));
+            thresh[x] = std::max<int64_t>(1, total / per_xcd / 3);
+        }
+        for (;;) {
+            used = 0;
+            for (int64_t x = 0; x < kXcd; ++x)
+                for (int64_t w = x * W / kXcd; w < (x + 1) * W / kXcd; ++w) {
+                    const int64_t k = parts_of(w, thresh[x]);
+                    if (k > 1) used += k;
+                }
+            if (used <= nblk) break;
+            for (auto& t : thresh) t = t + t / 4 + 1;
+        }
+    }
+    struct Piece { int64_t cost; int32_t w, a, b, slot; };
+    std::vector<std::vector<int32_t>> lists(nblk);
+    std::vector<Piece> pieces;
+    for (int64_t x = 0; x < kXcd; ++x) {
+        const int64_t w0 = x * W / kXcd, w1 = (x + 1) * W / kXcd;
+        pieces.clear();
+        for (int64_t w = w0; w < w1; ++w) {
+            const int64_t n = nall(w);
+            const int64_t k = split ? parts_of(w, thresh[x]) : 1;
+            if (k == 1) {
+                pieces.push_back({cost_of(w, 0, n), (int32_t)w, 0, (int32_t)n, -1});
+                continue;
+            }
+            // cut the entries where the running cost passes j/k of the list's
+            const int64_t f = nfull(w);
+            const int64_t tiles = kTile * std::min(f, n) + kMasked * (n - std::min(f, n));
+            out.merge.insert(out.merge.end(), {(int32_t)w, out.slots, (int32_t)k});
+            int64_t a = 0, acc = 0, e = 0;
+            for (int64_t j = 1; j <= k; ++j) {
+                int64_t b = n;
+                if (j < k) {
+                    const int64_t goal = tiles * j / k;
+                    while (e < n && acc < goal) acc += e++ < f ? kTile : kMasked;
+                    b = std::max(e, a + 1);
+                    b = std::min(b, n - (k - j));   // every later part keeps one entry
+                    e = b;
+                    acc = kTile * std::min(b, f) + kMasked * (b - std::min(b, f));
+                }
+                pieces.push_back({cost_of(w, a, b), (int32_t)w, (int32_t)a, (int32_t)b, out.slots++});
+                a = b;
+            }
+        }
+        // heaviest first, each to the least loaded block (ties to the lower
+        // block index).  (Taking the pieces in their own order instead, as the
+        // hardware would dispatch them, balanced basic_s8192 as well but
+        // doubled the forward's L2 misses; the time did not change.)
+        std::stable_sort(pieces.begin(), pieces.end(),
+                         [](const Piece& p, const Piece& q) { return p.cost > q.cost; });
+        using Slot = std::pair<int64_t, int64_t>;   // (load, local block index)
+        std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
+        for (int64_t l = 0; l < per_xcd; ++l) heap.emplace(0, l);
+        for (const Piece& pc : pieces) {
+            auto [load, l] = heap.top();
+            heap.pop();
+            auto& L = lists[l * kXcd + x];
+            L.insert(L.end(), {pc.w, pc.a, pc.b, pc.slot});
+            heap.emplace(load + pc.cost, l);
+            out.makespan = std::max(out.makespan, load + pc.cost);
+        }
+    }
+    out.off.assign(nblk + 1, 0);
+    for (int64_t i = 0; i < nblk; ++i) {
+        out.off[i + 1] = out.off[i] + (int32_t)(lists[i].size() / 4);
+        out.items.insert(out.items.end(), lists[i].begin(), lists[i].end());
     }
 }
 
