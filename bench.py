@@ -210,9 +210,10 @@ def merge_rotating(ca, torch, rows=131072, d=128, sets=3, reps=30):
 
 def measured_peaks(torch):
     """What this GPU delivers in isolation, beside the spec peaks: bf16 MFMAs
-    alone (libraprobe.so's MFMA-only kernel, two work-groups of four waves per
-    CU, timed after a second of the same load so that the clock has settled)
-    and streaming over 1 GiB per operand, bytes read + written: torch's copy
+    alone (libraprobe.so's MFMA-only kernels, two work-groups of four waves per
+    CU, timed after a second of the same load so that the clock has settled;
+    on nearly constant operands, and on operands with the bit statistics of
+    N(0,1) data, which draw more power and so hold a lower clock) and streaming over 1 GiB per operand, bytes read + written: torch's copy
     kernel, and libraprobe.so's streaming copy (one byte read per byte written),
     streaming add (two read per byte written, the LSE merge's ratio) and
     read-only fold, each the best over grid sizes and cache policies."""
@@ -225,26 +226,34 @@ def measured_peaks(torch):
     probe.ra_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     probe.ra_probe_mfma_flops.restype = ctypes.c_double
     probe.ra_probe_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    probe.ra_probe_mfma_random.restype = ctypes.c_int
+    probe.ra_probe_mfma_random.argtypes = probe.ra_probe_mfma.argtypes
     blocks, iters = 512, 16384
     out = torch.empty(blocks * 256, device="cuda")
     stream = torch.cuda.current_stream()
-    def launch():
-        rc = probe.ra_probe_mfma(out.data_ptr(), blocks, iters, ctypes.c_void_p(stream.cuda_stream))
-        if rc != 0:
-            raise RuntimeError(f"ra_probe_mfma failed ({rc})")
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < 1.0:
-        launch()
-        torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def mfma_rate(fn):
+        def launch():
+            rc = fn(out.data_ptr(), blocks, iters, ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"MFMA probe failed ({rc})")
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 1.0:   # a second of the same load first
+            launch()
+            torch.cuda.synchronize()
+        reps = 10
+        ev0.record(stream)
+        for _ in range(reps):
+            launch()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all().item()
+        return probe.ra_probe_mfma_flops(blocks, iters) * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e12
+
+    mfma_tf = mfma_rate(probe.ra_probe_mfma)
+    mfma_rand_tf = mfma_rate(probe.ra_probe_mfma_random)
     reps = 10
-    ev0.record(stream)
-    for _ in range(reps):
-        launch()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    mfma_tf = probe.ra_probe_mfma_flops(blocks, iters) * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e12
-    assert torch.isfinite(out).all().item()
     x = torch.empty(1 << 28, device="cuda")   # 1 GiB of fp32
     y = torch.empty_like(x)
     for _ in range(3):
@@ -304,6 +313,8 @@ def measured_peaks(torch):
     del x, y, out
     torch.cuda.empty_cache()
     return {"mfma_only_bf16_TFLOP/s": mfma_tf, "mfma_only_frac_of_spec": mfma_tf / PEAK_BF16_TFLOPS,
+            "mfma_only_bf16_random_operands_TFLOP/s": mfma_rand_tf,
+            "mfma_only_random_operands_frac_of_spec": mfma_rand_tf / PEAK_BF16_TFLOPS,
             "copy_GB/s": copy_gbs, "copy_frac_of_spec": copy_gbs / PEAK_HBM_GBS,
             "stream_copy_GB/s": best["copy"][0], "stream_copy_frac_of_spec": best["copy"][0] / PEAK_HBM_GBS,
             "stream_add_GB/s": best["add"][0], "stream_add_frac_of_spec": best["add"][0] / PEAK_HBM_GBS,

@@ -1,10 +1,11 @@
-// Measurement aids (not part of the attention path): a kernel that does
-// nothing but bf16 MFMAs, to measure what the matrix cores of this GPU deliver
-// when they are the only thing running, under the clocks the chip then holds,
-// and streaming kernels (a copy, an add that reads two bytes per byte
+// Measurement aids (not part of the attention path): kernels that do nothing
+// but bf16 MFMAs (on nearly constant operands, and on operands with the bit
+// statistics of N(0,1) data), to measure what the matrix cores of this GPU
+// deliver when they are the only thing running, under the clocks the chip then
+// holds; and streaming kernels (a copy, an add that reads two bytes per byte
 // written, as the LSE merge does, and a read-only fold), to measure what HBM
-// delivers to plain streaming kernels.  Built into their own library (libraprobe.so), loaded by bench.py
-// and the tests only.
+// delivers to plain streaming kernels.  Built into their own library
+// (libraprobe.so), loaded by bench.py and the tests only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -46,6 +47,48 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(float* out, int iters) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s += acc[c][r];
     out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// The same MFMA chains on operands with the bit statistics of N(0,1) bf16
+// data (random sign, exponents for magnitudes 1/8 .. 4, random mantissas), 8
+// operand sets per lane, each MFMA of a chain taking the next set, so that the
+// matrix cores switch about as many bits as on attention inputs.  Their power
+// depends on that switching: under the board's power limit the chip holds a
+// lower clock on such data than on the nearly constant operands above.
+__global__ __launch_bounds__(256) void mfma_peak_random_kernel(float* out, int iters) {
+    uint32_t x = (blockIdx.x * 256u + threadIdx.x) * 2654435761u + 0x9e3779b9u;
+    auto bf16_rand = [&]() {
+        x ^= x << 13;
+        x ^= x >> 17;
+        x ^= x << 5;
+        const uint32_t sign = x & 0x8000u, mant = x & 0x7fu, ex = 124u + (x >> 16) % 5u;
+        return (short)(sign | (ex << 7) | mant);
+    };
+    bf16x8_t a[8], b[8];
+#pragma unroll
+    for (int sidx = 0; sidx < 8; ++sidx)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            a[sidx][i] = bf16_rand();
+            b[sidx][i] = bf16_rand();
+        }
+    f32x16_t acc[CHAINS];
+#pragma unroll
+    for (int c = 0; c < CHAINS; ++c) acc[c] = (f32x16_t){};
+    for (int it = 0; it < iters; it += 8) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int c = 0; c < CHAINS; ++c)
+                acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(k + c) & 7], b[(k + 3 * c + 1) & 7],
+                                                                 acc[c], 0, 0, 0);
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < CHAINS; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum += acc[c][r];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
 }
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -147,11 +190,14 @@ int ra_probe_mfma(float* out, int32_t blocks, int32_t iters, hipStream_t stream)
     return (int)hipGetLastError();
 }
 
-// dst = a (b == NULL) or dst = a + b as floats (b != NULL), over `bytes`
-// bytes of device memory (every pointer 16-byte aligned, bytes a multiple of
-// 16, dst overlapping neither input) with `blocks` work-groups of 256 threads
-// on `stream`.  flags bit 0: non-temporal loads, bit 1: non-temporal stores.
-// Returns a hipError_t value.
+// As ra_probe_mfma (same flops, ra_probe_mfma_flops), on operands with the
+// bit statistics of N(0,1) bf16 data that change from one MFMA to the next.
+int ra_probe_mfma_random(float* out, int32_t blocks, int32_t iters, hipStream_t stream) {
+    if (out == nullptr || blocks <= 0 || iters <= 0) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(mfma_peak_random_kernel, dim3(blocks), dim3(256), 0, stream, out, iters);
+    return (int)hipGetLastError();
+}
+
 // Read `bytes` bytes of a (16-byte aligned, a multiple of 16) with `blocks`
 // work-groups of 256 threads on `stream`; out receives blocks * 256 uint32.
 // flags bit 0: non-temporal loads.  Returns a hipError_t value.
@@ -170,6 +216,11 @@ int ra_probe_stream_read(const void* a, void* out, int64_t bytes, int32_t blocks
     return (int)hipGetLastError();
 }
 
+// dst = a (b == NULL) or dst = a + b as floats (b != NULL), over `bytes`
+// bytes of device memory (every pointer 16-byte aligned, bytes a multiple of
+// 16, dst overlapping neither input) with `blocks` work-groups of 256 threads
+// on `stream`.  flags bit 0: non-temporal loads, bit 1: non-temporal stores.
+// Returns a hipError_t value.
 int ra_probe_stream(const void* a, const void* b, void* dst, int64_t bytes, int32_t blocks,
                     int32_t flags, hipStream_t stream) {
     if (a == nullptr || dst == nullptr || bytes < 0 || bytes % 16 != 0 || blocks <= 0 ||

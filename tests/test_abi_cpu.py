@@ -47,6 +47,10 @@ def test_peak_probe_library_loads():
     lib.ra_probe_mfma.restype = ctypes.c_int
     lib.ra_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     assert lib.ra_probe_mfma(None, 1, 8, None) != 0   # refused before any launch
+    lib.ra_probe_mfma_random.restype = ctypes.c_int
+    lib.ra_probe_mfma_random.argtypes = lib.ra_probe_mfma.argtypes
+    for out, blocks, iters in ((None, 1, 8), (16, 0, 8), (16, 1, 0)):
+        assert lib.ra_probe_mfma_random(out, blocks, iters, None) != 0
     lib.ra_probe_stream.restype = ctypes.c_int
     lib.ra_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]

@@ -1,7 +1,8 @@
 """The measurement probes bench.py uses: the streaming copy, add and
 read-only fold compute exactly what they claim over the bytes they are given
 (the unrolled passes and the tail, every cache policy), so their bandwidths
-are those of correct kernels."""
+are those of correct kernels; the MFMA-only kernels run and write finite
+sums."""
 import ctypes
 import os
 
@@ -65,3 +66,22 @@ def test_stream_read_visits_every_word_once(chunks, blocks, flags):
     want = np.bitwise_xor.reduce(a.cpu().numpy().view(np.uint32))
     assert got == want
     assert int(out[-1]) == 12345
+
+
+@pytest.mark.parametrize("random_operands", [False, True])
+def test_mfma_probes_run_and_give_finite_sums(random_operands):
+    """The MFMA-only kernels the bench times: every lane writes a finite,
+    non-zero sum of its accumulators (a launch that did no MFMA would leave
+    the sentinel)."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "context_attention_flash_amd", "libraprobe.so"))
+    fn = lib.ra_probe_mfma_random if random_operands else lib.ra_probe_mfma
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    blocks = 16
+    out = torch.full((blocks * 256,), float("nan"), device="cuda")
+    print("mfma probe, random operands" if random_operands else "mfma probe", flush=True)
+    assert fn(out.data_ptr(), blocks, 64, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    assert (out != 0).any().item()
