@@ -468,6 +468,8 @@ def main():
                     help="time the forward alone (drop the backward of the workload)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the MFMA-only and copy-bandwidth measurements")
+    ap.add_argument("--peaks-only", action="store_true",
+                    help="only run the MFMA-only and copy-bandwidth measurements")
     ap.add_argument("--sustain", choices=("fwd", "bwd", "step"),
                     help="only run that pass of the workload back to back for --seconds "
                          "(a steady load for reading power and clocks from outside)")
@@ -487,7 +489,8 @@ def main():
     if args.sustain:
         w = w.replace(with_grad=args.sustain != "fwd")
     pool = None
-    if not (args.no_cpu_baseline or args.calibrate_copy or args.merge_only or args.sustain):
+    if not (args.no_cpu_baseline or args.calibrate_copy or args.merge_only or args.sustain
+            or args.peaks_only):
         pool, workers = start_host_pool(w)   # before any GPU call
 
     import torch
@@ -499,6 +502,10 @@ def main():
     if args.merge_only:
         torch.cuda.set_device(0)
         print(json.dumps({"merge": merge_bandwidth(ca, torch)}), flush=True)
+        return
+    if args.peaks_only:
+        torch.cuda.set_device(0)
+        print(json.dumps({"measured_peaks": measured_peaks(torch)}), flush=True)
         return
 
     torch.cuda.set_device(0)
