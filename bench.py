@@ -20,6 +20,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -208,51 +209,73 @@ def merge_rotating(ca, torch, rows=131072, d=128, sets=3, reps=30):
             "avg_ms": ms / n, "GB/s": gbs, "frac_hbm_peak": gbs / PEAK_HBM_GBS}
 
 
-def measured_peaks(torch):
-    """What this GPU delivers in isolation, beside the spec peaks: bf16 MFMAs
-    alone (libraprobe.so's MFMA-only kernels, two work-groups of four waves per
-    CU, timed after a second of the same load so that the clock has settled;
-    on nearly constant operands, and on operands with the bit statistics of
-    N(0,1) data, which draw more power and so hold a lower clock) and streaming over 1 GiB per operand, bytes read + written: torch's copy
-    kernel, and libraprobe.so's streaming copy (one byte read per byte written),
-    streaming add (two read per byte written, the LSE merge's ratio) and
-    read-only fold, each the best over grid sizes and cache policies."""
-    import ctypes
-    path = os.path.join(ROOT, "context_attention_flash_amd", "libraprobe.so")
-    if not os.path.exists(path):
-        raise RuntimeError(f"{path} is missing: build it with python -c 'import __graft_entry__ as g; g.build()'")
-    probe = ctypes.CDLL(path)
-    probe.ra_probe_mfma.restype = ctypes.c_int
-    probe.ra_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
-    probe.ra_probe_mfma_flops.restype = ctypes.c_double
-    probe.ra_probe_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
-    probe.ra_probe_mfma_random.restype = ctypes.c_int
-    probe.ra_probe_mfma_random.argtypes = probe.ra_probe_mfma.argtypes
-    blocks, iters = 512, 16384
-    out = torch.empty(blocks * 256, device="cuda")
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+class MfmaProbe:
+    """libraprobe.so's MFMA-only kernels (two work-groups of four waves per
+    CU, 4.4 bf16 TFLOP per launch), on nearly constant operands or (random)
+    on operands with the bit statistics of N(0,1) data."""
 
-    def mfma_rate(fn):
-        def launch():
-            rc = fn(out.data_ptr(), blocks, iters, ctypes.c_void_p(stream.cuda_stream))
+    def __init__(self, torch, random_operands):
+        import ctypes
+        path = os.path.join(ROOT, "context_attention_flash_amd", "libraprobe.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with python -c 'import __graft_entry__ as g; g.build()'")
+        probe = ctypes.CDLL(path)
+        probe.ra_probe_mfma_flops.restype = ctypes.c_double
+        probe.ra_probe_mfma_flops.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        self.fn = probe.ra_probe_mfma_random if random_operands else probe.ra_probe_mfma
+        self.fn.restype = ctypes.c_int
+        self.fn.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+        self.torch, self.ctypes = torch, ctypes
+        self.blocks, self.iters = 512, 16384
+        self.flops = probe.ra_probe_mfma_flops(self.blocks, self.iters)
+        self.out = torch.empty(self.blocks * 256, device="cuda")
+        self.stream = torch.cuda.current_stream()
+
+    def launch(self, n=1):
+        for _ in range(n):
+            rc = self.fn(self.out.data_ptr(), self.blocks, self.iters,
+                         self.ctypes.c_void_p(self.stream.cuda_stream))
             if rc != 0:
                 raise RuntimeError(f"MFMA probe failed ({rc})")
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < 1.0:   # a second of the same load first
-            launch()
-            torch.cuda.synchronize()
-        reps = 10
-        ev0.record(stream)
-        for _ in range(reps):
-            launch()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        assert torch.isfinite(out).all().item()
-        return probe.ra_probe_mfma_flops(blocks, iters) * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e12
 
-    mfma_tf = mfma_rate(probe.ra_probe_mfma)
-    mfma_rand_tf = mfma_rate(probe.ra_probe_mfma_random)
+    def timed(self, n):
+        ev0, ev1 = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
+        ev0.record(self.stream)
+        self.launch(n)
+        ev1.record(self.stream)
+        self.torch.cuda.synchronize()
+        assert self.torch.isfinite(self.out).all().item()
+        return self.flops * n / (ev0.elapsed_time(ev1) * 1e-3) / 1e12
+
+    def sustained(self, seconds=2.0):
+        """Launches queued back to back for `seconds`, the rate of the last
+        half: the steady state under the power limit, as the attention kernels
+        run in the timed steps (a 10-launch burst measures the same)."""
+        rates, t0 = [], time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            rates.append(self.timed(25))
+        return statistics.mean(rates[len(rates) // 2:])
+
+
+def measured_peaks(torch):
+    """What this GPU delivers in isolation, beside the spec peaks: bf16 MFMAs
+    alone (MfmaProbe), on nearly constant operands and on operands with the
+    bit statistics of N(0,1) data (which draw more power and so hold a lower
+    clock), queued back to back for two seconds as the attention kernels run
+    in the timed steps; and streaming over 1 GiB per
+    operand, bytes read + written: torch's copy kernel, and libraprobe.so's
+    streaming copy (one byte read per byte written), streaming add (two read
+    per byte written, the LSE merge's ratio) and read-only fold, each the best
+    over grid sizes and cache policies."""
+    import ctypes
+    path = os.path.join(ROOT, "context_attention_flash_amd", "libraprobe.so")
+    probe = ctypes.CDLL(path)
+    mfma = {}
+    for random_operands in (False, True):
+        pr = MfmaProbe(torch, random_operands)
+        mfma[random_operands] = pr.sustained()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 10
     x = torch.empty(1 << 28, device="cuda")   # 1 GiB of fp32
     y = torch.empty_like(x)
@@ -310,11 +333,11 @@ def measured_peaks(torch):
             gbs = nbytes * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
             best["read"] = max(best["read"], (gbs, blocks, flags))
     del z, sink
-    del x, y, out
+    del x, y
     torch.cuda.empty_cache()
-    return {"mfma_only_bf16_TFLOP/s": mfma_tf, "mfma_only_frac_of_spec": mfma_tf / PEAK_BF16_TFLOPS,
-            "mfma_only_bf16_random_operands_TFLOP/s": mfma_rand_tf,
-            "mfma_only_random_operands_frac_of_spec": mfma_rand_tf / PEAK_BF16_TFLOPS,
+    return {"mfma_only_bf16_TFLOP/s": mfma[False], "mfma_only_frac_of_spec": mfma[False] / PEAK_BF16_TFLOPS,
+            "mfma_only_bf16_random_operands_TFLOP/s": mfma[True],
+            "mfma_only_random_operands_frac_of_spec": mfma[True] / PEAK_BF16_TFLOPS,
             "copy_GB/s": copy_gbs, "copy_frac_of_spec": copy_gbs / PEAK_HBM_GBS,
             "stream_copy_GB/s": best["copy"][0], "stream_copy_frac_of_spec": best["copy"][0] / PEAK_HBM_GBS,
             "stream_add_GB/s": best["add"][0], "stream_add_frac_of_spec": best["add"][0] / PEAK_HBM_GBS,
@@ -470,9 +493,10 @@ def main():
                     help="skip the MFMA-only and copy-bandwidth measurements")
     ap.add_argument("--peaks-only", action="store_true",
                     help="only run the MFMA-only and copy-bandwidth measurements")
-    ap.add_argument("--sustain", choices=("fwd", "bwd", "step"),
-                    help="only run that pass of the workload back to back for --seconds "
-                         "(a steady load for reading power and clocks from outside)")
+    ap.add_argument("--sustain", choices=("fwd", "bwd", "step", "mfma", "mfma_random"),
+                    help="only run that pass of the workload (or the MFMA-only kernel, on "
+                         "nearly constant or on N(0,1)-like operands) back to back for "
+                         "--seconds (a steady load for reading power and clocks from outside)")
     ap.add_argument("--seconds", type=float, default=20.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -486,7 +510,7 @@ def main():
         w = w.replace(with_grad=True)
     if args.fwd_only:
         w = w.replace(with_grad=False)
-    if args.sustain:
+    if args.sustain in ("fwd", "bwd", "step"):
         w = w.replace(with_grad=args.sustain != "fwd")
     pool = None
     if not (args.no_cpu_baseline or args.calibrate_copy or args.merge_only or args.sustain
@@ -502,6 +526,17 @@ def main():
     if args.merge_only:
         torch.cuda.set_device(0)
         print(json.dumps({"merge": merge_bandwidth(ca, torch)}), flush=True)
+        return
+    if args.sustain in ("mfma", "mfma_random"):
+        torch.cuda.set_device(0)
+        pr = MfmaProbe(torch, args.sustain == "mfma_random")
+        log(f"sustain {args.sustain} for {args.seconds} s")
+        rates, t0 = [], time.perf_counter()
+        while time.perf_counter() - t0 < args.seconds:
+            rates.append(pr.timed(25))
+        print(json.dumps({"sustain": args.sustain, "launches": 25 * len(rates),
+                          "TFLOP/s": statistics.mean(rates[len(rates) // 2:]),
+                          "seconds": time.perf_counter() - t0}), flush=True)
         return
     if args.peaks_only:
         torch.cuda.set_device(0)
