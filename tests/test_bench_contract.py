@@ -56,3 +56,27 @@ def test_bench_prints_one_complete_json_line():
     assert cpu["value"] > 0 and isinstance(cpu["unit"], str)
     assert isinstance(cpu["cores"], int) and cpu["cores"] >= 1
     assert isinstance(cpu["sample"], str) and cpu["sample"]
+
+
+@pytest.mark.gpu
+def test_bench_peaks_only_reports_every_measured_peak():
+    """bench.py --peaks-only: the MFMA-only rates (nearly constant and
+    data-like operands) and the streaming bandwidths, each positive and below
+    the spec peak it is compared with, and the fractions consistent."""
+    cmd = [sys.executable, BENCH, "--peaks-only"]
+    print("bench:", " ".join(cmd[1:]), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, r.stdout
+    p = json.loads(lines[0])["measured_peaks"]
+    spec = p["spec"]
+    for rate, frac in (("mfma_only_bf16_TFLOP/s", "mfma_only_frac_of_spec"),
+                       ("mfma_only_bf16_random_operands_TFLOP/s", "mfma_only_random_operands_frac_of_spec")):
+        assert 0 < p[rate] < spec["bf16_TFLOP/s"], (rate, p[rate])
+        assert p[frac] == pytest.approx(p[rate] / spec["bf16_TFLOP/s"], rel=1e-9)
+    for kind in ("copy", "stream_copy", "stream_add", "stream_read"):
+        gbs = p[f"{kind}_GB/s"]
+        assert 0 < gbs < spec["hbm_GB/s"], (kind, gbs)
+        assert p[f"{kind}_frac_of_spec"] == pytest.approx(gbs / spec["hbm_GB/s"], rel=1e-9)
+    assert set(p["stream_best_config"]) == {"copy", "add", "read"}
