@@ -44,9 +44,12 @@ def _run_fwd(w, glob, rank, merge_mode=ca.RA_MERGE_FUSED):
     return sh, desc, (q, k, v), out.float().cpu().numpy(), lse.cpu().numpy()
 
 
-def _check_fwd(w, glob, rank, out, lse):
-    ref_out, ref_lse = oracle.rank_share_forward(glob["q"], glob["k"], glob["v"], w.layout, w.world,
-                                                 rank, w.causal, w.cu_seqlens, window=w.window)
+def _check_fwd(w, glob, rank, out, lse, ref=None):
+    """out and lse against the oracle's rank share (`ref`: the oracle's
+    (out, lse) when the caller has it already)."""
+    ref_out, ref_lse = ref if ref is not None else oracle.rank_share_forward(
+        glob["q"], glob["k"], glob["v"], w.layout, w.world, rank, w.causal, w.cu_seqlens,
+        window=w.window)
     t = tol(w.dtype)
     e_out = float(np.abs(out - ref_out).max())
     e_lse = max_err_lse(lse, ref_lse)
@@ -499,14 +502,34 @@ def test_fwd_split_lists(layout, B, head_dim, S):
     merges them (the part-merge kernel runs); without it the lists run whole.
     Both match the oracle, and differ from each other only by the rounding of
     the merge."""
-    w = _small_workload(layout, True, head_dim, D=2, S=S, B=B, Hq=32, Hkv=8, seed=3 * S + layout)
+    _split_against_whole(_small_workload(layout, True, head_dim, D=2, S=S, B=B, Hq=32, Hkv=8,
+                                         seed=3 * S + layout))
+
+
+def test_fwd_split_lists_across_ring_steps():
+    """A varlen ring share whose lists hold the key tiles of four ring steps:
+    eight short documents and a long one give lists of very different
+    lengths (the planner's cost model cuts this share, checked below through
+    the part-merge launches), and the cuts of the long lists fall inside and
+    between ring steps (each part walks entries of several steps, with their
+    blocks and key intervals)."""
+    cu = (0, 344, 688, 1032, 1376, 1720, 2064, 2408, 2768, 9216)
+    w = synth.Workload("split-varlen-ring", 1, 32, 8, 128, 9216, 4, 0, True, ca.VARLEN_RING, "bf16",
+                       seed=77, cu_seqlens=cu)
+    _split_against_whole(w)
+
+
+def _split_against_whole(w):
     glob = synth.draw_global(w)
     rank = w.world - 1
+    layout, head_dim, S = w.layout, w.head_dim, w.shard
     sh = shard(glob, w, rank)
     desc = ca.desc_from_workload(w, rank=rank)
     q, k, v = (to_dev(sh[n], w.dtype) for n in ("q", "k", "v"))
     split_bytes = ca.ring_attn_fwd_split_bytes(desc)
     assert split_bytes > 0
+    ref = oracle.rank_share_forward(glob["q"], glob["k"], glob["v"], w.layout, w.world, rank, w.causal,
+                                    w.cu_seqlens, window=w.window)
     results = {}
     for name, nbytes in (("split", ca.ring_attn_workspace_bytes(desc, False) + split_bytes),
                          ("whole", 16)):
@@ -520,7 +543,7 @@ def test_fwd_split_lists(layout, B, head_dim, S):
         ca.ring_attn_timing_enable(False)
         assert (merges > 0) == (name == "split"), (name, merges)
         results[name] = (out.float().cpu().numpy(), lse.cpu().numpy())
-        _check_fwd(w, glob, rank, *results[name])
+        _check_fwd(w, glob, rank, *results[name], ref=ref)
     assert np.abs(results["split"][0] - results["whole"][0]).max() <= 1e-2
     assert max_err_lse(results["split"][1], results["whole"][1]) <= 1e-4
 
