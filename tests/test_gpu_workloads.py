@@ -1,8 +1,9 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py
 times (fused merge), on outputs the oracle can afford to compute: sampled query
-rows x heads for the forward and dq, and the complete dK/dV of one KV head for
-the backward (the oracle sums that head's contributions over every query row of
-the rank, chunk by chunk)."""
+rows x heads for the forward and dq; the complete dK/dV of one KV head for the
+backward (the oracle sums that head's contributions over every query row of
+the rank, chunk by chunk); and the complete dK/dV of every KV head when dout
+is zero outside sampled rows."""
 import numpy as np
 import pytest
 
@@ -166,3 +167,39 @@ def test_workload_backward_full_size(name):
         got_dv = dv[..., hk, :].cpu().numpy()
         assert np.abs(got_dk - rdk).max() <= 5e-2 * np.abs(rdk).max()
         assert np.abs(got_dv - rdv).max() <= 5e-2 * np.abs(rdv).max()
+
+
+@pytest.mark.parametrize("name", ["zigzag", "llama3", "basic_s8192"])
+def test_workload_backward_dkdv_from_sampled_rows(name):
+    """The complete dK/dV of every kv head at the zigzag, llama3 and
+    basic_s8192 sizes.
+    dK and dV are linear in dout, and a row whose dout is zero adds nothing to
+    them (its dP and Delta are zero, so its dS = P (dP - Delta) is too): with
+    dout zero except on sampled rows, every element of the GPU's dK/dV (all
+    blocks, keys and kv heads, every q head of each group) must equal the
+    oracle's sums over those rows alone."""
+    w = synth.WORKLOADS[name].replace(with_grad=True)
+    say(f"workload bwd dk/dv from sampled rows {name}")
+    g, desc, cu, pos_q, dev = _inputs(w)
+    S = w.shard
+    extra = (S // 2 - 1, S // 2, S // 2 + 1) if w.layout == ca.ZIGZAG else ()
+    if cu is not None:
+        extra = tuple(int(c - pos_q[0]) + o for c in cu for o in (-1, 0, 1))
+    rows = _sample_rows(S, np.random.default_rng(11), extra)
+    dout_local = np.zeros_like(g["dout"][:, pos_q])
+    dout_local[:, rows] = g["dout"][:, pos_q][:, rows]
+    dout = to_dev(dout_local, w.dtype)
+    ws = ca.alloc_workspace(desc, True, cu_seqlens=cu)
+    out, lse = ca.ring_attn_fwd(desc, dev["q"], dev["k"], dev["v"], cu)
+    _, dk, dv = ca.ring_attn_bwd(desc, dout, dev["q"], dev["k"], dev["v"], out, lse, cu, workspace=ws)
+    torch.cuda.synchronize()
+    # (the drawn inputs hold bf16 values exactly: both sides see the same dout)
+    _, rdk, rdv = oracle.rank_share_backward(g["q"], g["k"], g["v"], dout_local, w.layout, w.world,
+                                             w.rank, w.causal, cu, rows=rows,
+                                             heads=list(range(w.heads_q)))
+    got_dk, got_dv = dk.cpu().numpy(), dv.cpu().numpy()
+    assert got_dk.shape == rdk.shape and got_dv.shape == rdv.shape
+    assert np.abs(got_dk - rdk).max() <= 5e-2 * np.abs(rdk).max(), np.abs(got_dk - rdk).max()
+    assert np.abs(got_dv - rdv).max() <= 5e-2 * np.abs(rdv).max(), np.abs(got_dv - rdv).max()
+    # the rows' contributions reach keys of every kv head
+    assert np.abs(rdv).reshape(-1, w.heads_kv, w.head_dim).max(axis=(0, 2)).min() > 0
