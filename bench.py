@@ -249,8 +249,9 @@ class MfmaProbe:
 
     def sustained(self, seconds=2.0):
         """Launches queued back to back for `seconds`, the rate of the last
-        half: the steady state under the power limit, as the attention kernels
-        run in the timed steps (a 10-launch burst measures the same)."""
+        half: the steady state at the clock the chip holds under this load, as
+        the attention kernels run in the timed steps (a 10-launch burst
+        measures the same)."""
         rates, t0 = [], time.perf_counter()
         while time.perf_counter() - t0 < seconds:
             rates.append(self.timed(25))
@@ -260,13 +261,13 @@ class MfmaProbe:
 def measured_peaks(torch):
     """What this GPU delivers in isolation, beside the spec peaks: bf16 MFMAs
     alone (MfmaProbe), on nearly constant operands and on operands with the
-    bit statistics of N(0,1) data (which draw more power and so hold a lower
-    clock), queued back to back for two seconds as the attention kernels run
-    in the timed steps; and streaming over 1 GiB per
-    operand, bytes read + written: torch's copy kernel, and libraprobe.so's
-    streaming copy (one byte read per byte written), streaming add (two read
-    per byte written, the LSE merge's ratio) and read-only fold, each the best
-    over grid sizes and cache policies."""
+    bit statistics of N(0,1) data (on which the chip holds a lower clock),
+    queued back to back for two seconds as the attention kernels run in the
+    timed steps; and streaming over 1 GiB per operand, bytes read + written:
+    torch's copy kernel, and libraprobe.so's streaming copy (one byte read per
+    byte written), streaming add (two read per byte written, the LSE merge's
+    ratio) and read-only fold, each the best over grid sizes and cache
+    policies."""
     import ctypes
     path = os.path.join(ROOT, "context_attention_flash_amd", "libraprobe.so")
     probe = ctypes.CDLL(path)

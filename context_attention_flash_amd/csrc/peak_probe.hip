@@ -52,9 +52,9 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(float* out, int iters) {
 // The same MFMA chains on operands with the bit statistics of N(0,1) bf16
 // data (random sign, exponents for magnitudes 1/8 .. 4, random mantissas), 8
 // operand sets per lane, each MFMA of a chain taking the next set, so that the
-// matrix cores switch about as many bits as on attention inputs.  Their power
-// depends on that switching: under the board's power limit the chip holds a
-// lower clock on such data than on the nearly constant operands above.
+// matrix cores switch about as many bits as on attention inputs.  The chip
+// holds a lower clock on such data than on the nearly constant operands
+// above, for the same instructions.
 __global__ __launch_bounds__(256) void mfma_peak_random_kernel(float* out, int iters) {
     uint32_t x = (blockIdx.x * 256u + threadIdx.x) * 2654435761u + 0x9e3779b9u;
     auto bf16_rand = [&]() {
